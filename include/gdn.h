@@ -1,0 +1,177 @@
+/*
+ * gdn.h -- C ABI of the gated-delta-rule forward library for MI355X (gfx950).
+ *
+ * Four operations make the hot path of a Gated DeltaNet / Gated DeltaProduct
+ * mixer: the short causal convolution, the gate preparation, the chunked
+ * prefill forward and the one-token recurrent decode. Sources (web pages,
+ * cited by title and section):
+ *   [ZZ]  "ZzCompute", PyTorch Helion Hackathon gallery entry, items 1-4.
+ *   [GDP] Megatron-Core API docs, "core.ssm.ops.gdp.decode_prepare".
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers (HIP global memory) unless stated.
+ *    `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Strides are in elements of the tensor's own dtype.
+ *  - Ownership: the caller owns every buffer. The library never allocates or
+ *    frees memory; intermediates go to the caller's workspace.
+ *  - Asynchrony: every call only enqueues kernels on `stream`; it performs no
+ *    host synchronisation and no device-to-host read, so it may be captured
+ *    in a HIP graph.
+ *  - Errors: every call returns a gdn_status. All argument validation happens
+ *    before the first HIP call, so a rejected call has no effect. A kernel
+ *    launch failure is reported as GDN_ELAUNCH (from hipGetLastError).
+ *    NaN/Inf inputs propagate; they are not trapped.
+ *  - Determinism: no atomics; every output element has exactly one writer, so
+ *    repeated calls on the same inputs give bitwise identical results.
+ *  - Alignment: every device base pointer must be 16-byte aligned, and every
+ *    row stride a multiple of 16 bytes, else GDN_EUNSUPPORTED.
+ *  - bf16 results are rounded to nearest-even from fp32 accumulators.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,        /* null required pointer, bad size, bad stride, aliasing */
+    GDN_EUNSUPPORTED = 2,  /* valid but not implemented: head dims, W, alignment, dtype */
+    GDN_EWORKSPACE = 3,    /* workspace smaller than the size query returns */
+    GDN_ELAUNCH = 4        /* a kernel launch failed (no device, bad stream, ...) */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_FP32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype;
+
+/* Static, NUL-terminated name of a status code ("GDN_OK", ...). Never NULL. */
+const char* gdn_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * gdn_conv1d_causal -- [ZZ] item 1 "Causal Conv1d".
+ * Depthwise causal convolution of width W (only W == 4 is implemented; the
+ * width is fixed at compile time so the tap loop unrolls), each channel with
+ * its own past, optionally followed by SiLU z/(1+exp(-z)):
+ *     y[b,t,c] = act( sum_{j<W} w[c,j] * x[b, t-(W-1)+j, c] (+ bias[c]) )
+ * A tap that falls before the start of the token's own sequence reads zero
+ * (masked load; nothing is padded on the host), so nothing leaks across a
+ * batch row or across a packed-sequence boundary.
+ *   x        [B, T, C] in `dtype`, channel dim contiguous; element (b,t,c) at
+ *            x + b*x_stride_b + t*x_stride_t + c.
+ *   w        [C, W] in `dtype`, contiguous (w[c][W-1] multiplies x_t).
+ *   bias     [C] in `dtype`, or NULL for none.
+ *   y        [B, T, C] in `dtype`, same addressing with y strides. y must not
+ *            overlap x (GDN_EINVAL when the base pointers are equal).
+ *   cu_seqlens  int32 [n_seqs + 1] device array of packed-sequence offsets,
+ *            or NULL. With it, B must be 1 and T the packed length; it must be
+ *            non-decreasing with cu[0] = 0 and cu[n_seqs] = T (not checked:
+ *            checking would need a device read).
+ *   silu     0 = identity, 1 = SiLU.
+ *   dtype    GDN_FP32 or GDN_BF16 (fp32 accumulation either way).
+ *   C must be a multiple of 8 (bf16) or 4 (fp32).
+ * ---------------------------------------------------------------------- */
+int gdn_conv1d_causal(const void* x, int64_t x_stride_b, int64_t x_stride_t,
+                      const void* w, const void* bias,
+                      void* y, int64_t y_stride_b, int64_t y_stride_t,
+                      const int32_t* cu_seqlens, int n_seqs,
+                      int B, int T, int C, int W, int silu, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_gate_prepare -- [GDP] module introduction and "softplus" entry.
+ *     beta = sigmoid(b) = 1 / (1 + exp(-b))
+ *     g    = -exp(A_log[h]) * softplus(a + dt_bias[h]),
+ *     softplus(x) = x if x > 20 else log1p(exp(x))
+ * computed in fp32 with IEEE division.
+ *   a, b     [R, H] rows in `in_dtype`; row r at a + r*a_stride_row (the last
+ *            dim contiguous; rows may be a strided view).
+ *   A_log, dt_bias  [H] fp32.
+ *   g, beta  [R, H] fp32, contiguous outputs (alpha = exp(g) is the decay).
+ * ---------------------------------------------------------------------- */
+int gdn_gate_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
+                     const float* A_log, const float* dt_bias, float* g, float* beta,
+                     int R, int H, int in_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_chunk_fwd -- [ZZ] items 2-4: the gated delta rule evaluated in
+ * 64-timestep chunks (WY recompute per chunk, sequential inter-chunk K x V
+ * state scan, per-chunk output). Per sequence and value head, with state
+ * h (K x V, fp32), the result equals the timestep recurrence
+ *     h_t = exp(g_t) h_{t-1} + beta_t k_t (v_t - exp(g_t) h_{t-1}^T k_t)^T
+ *     o_t = scale * h_t^T q_t
+ * (h = S^T for S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T).
+ *   q, k     [B*T, Hk, K] token rows in `dtype`: element (token, head, d) at
+ *            q + token*qk_stride_t + head*K + d (a batch row b starts at token
+ *            b*T, i.e. rows of all batches are evenly strided). Typically
+ *            zero-copy views of the conv1d output (token stride = C).
+ *   v        [B*T, H, V] token rows in `dtype`, token stride v_stride_t.
+ *   g, beta  [B*T, H] fp32 contiguous (the gdn_gate_prepare outputs).
+ *   initial_state  [N, H, K, V] fp32 contiguous, or NULL for zero.
+ *   final_state    [N, H, K, V] fp32 contiguous output, or NULL to skip.
+ *            N = n_seqs with cu_seqlens, else B.
+ *   o        [B*T, H, V] in `dtype`, contiguous output.
+ *   cu_seqlens  int32 [n_seqs + 1] device offsets of packed sequences or
+ *            NULL (same contract as conv1d; B must be 1). The state restarts
+ *            at every sequence start; the last chunk of a sequence may be
+ *            partial.
+ *   H value heads share Hk q/k heads: value head h reads q/k head
+ *            h / (H / Hk) (H % Hk == 0).
+ *   K, V     head dims; each of 64 or 128.
+ *   qk_l2norm  1: q and k are normalised per token and head as
+ *            x / sqrt(sum x^2 + 1e-6) before use; 0: used as given.
+ *   dtype    GDN_BF16 (bf16 MFMA operands, fp32 accumulation and state) or
+ *            GDN_FP32 (fp32 MFMA operands throughout).
+ *   workspace  device scratch of at least gdn_chunk_fwd_workspace_size(...)
+ *            bytes, 256-byte aligned; contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int Hk, int K, int V,
+                                    int n_seqs, int dtype);
+
+int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t,
+                  const void* v, int64_t v_stride_t,
+                  const float* g, const float* beta,
+                  const float* initial_state, float* final_state,
+                  void* o,
+                  const int32_t* cu_seqlens, int n_seqs,
+                  int B, int T, int H, int Hk, int K, int V,
+                  float scale, int qk_l2norm, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_recurrent_decode -- [GDP] "gdp_decode_prepare" fused with the
+ * recurrent update it feeds: one decode token for n requests of a Gated
+ * DeltaProduct layer with M Householder copies.
+ *   x        [n, M*H*P + M*G*N + G*N] in `dtype`: the post-conv row, value |
+ *            key | query, laid out v [M][H][P], k [M][G][N], q [G][N]; row r
+ *            at x + r*x_stride_n.
+ *   ba       [n, M*H + H] in `dtype`: b [M][H] then a [H]; row r at
+ *            ba + r*ba_stride_n (may be a strided view).
+ *   A_log, dt_bias  [H] fp32.
+ *   state    [n, H, N, P] fp32 (K x V orientation: N = key dim rows, P =
+ *            value dim columns), read and updated IN PLACE.
+ *   o        [n, H, P] in `dtype`, contiguous output.
+ * Per request and value head h (q/k group h / (H/G), H % G == 0), the M
+ * copies run as an M-step sequence: copy 0 carries the decay
+ * exp(-exp(A_log)*softplus(a+dt_bias)), later copies none; every copy m
+ * writes with beta_m = sigmoid(b_m) and key k_m; only the last copy carries
+ * the query, and o is that copy's output scale * h^T q.
+ *   P, N     64 or 128.  M in 1..4.
+ *   qk_l2norm  as for gdn_chunk_fwd.
+ * ---------------------------------------------------------------------- */
+int gdn_recurrent_decode(const void* x, int64_t x_stride_n,
+                         const void* ba, int64_t ba_stride_n,
+                         const float* A_log, const float* dt_bias,
+                         float* state, void* o,
+                         int n, int M, int H, int G, int P, int N,
+                         float scale, int qk_l2norm, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,276 @@
+"""MI355X-native gated-delta-rule forward: Python binding of libgdn.so.
+
+The functions below carry the names of the C entry points in include/gdn.h and
+only marshal arguments: tensor -> device pointer, strides, dtype code, the
+current HIP stream. Every step of the computation runs in the library's HIP
+kernels; there is no fallback. Importing this package fails if libgdn.so has
+not been built (``python -m linear_attention_ssm_amd.build``), and every call
+fails on tensors that are not on a GPU.
+
+PyTorch is used for device memory (allocating outputs and workspaces) and for
+the current stream only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
+    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_recurrent_decode", "prefill_chain",
+    "split_qkv",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_FP32, GDN_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: GDN_FP32, torch.bfloat16: GDN_BF16}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m linear_attention_ssm_amd.build` "
+        "(the HIP library is the only implementation; there is no fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_lib.gdn_status_string.argtypes = [_i32]
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_conv1d_causal.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _i32,
+                                   _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+_lib.gdn_conv1d_causal.restype = _i32
+_lib.gdn_gate_prepare.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.gdn_gate_prepare.restype = _i32
+_lib.gdn_chunk_fwd_workspace_size.argtypes = [_i32] * 8
+_lib.gdn_chunk_fwd_workspace_size.restype = _sz
+_lib.gdn_chunk_fwd.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
+                               + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
+_lib.gdn_chunk_fwd.restype = _i32
+_lib.gdn_recurrent_decode.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
+                                      + [_i32] * 6 + [_f32, _i32, _i32, _vp])
+_lib.gdn_recurrent_decode.restype = _i32
+
+
+class GdnError(RuntimeError):
+    """A non-zero gdn_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_string(status)}")
+
+
+def gdn_status_string(status: int) -> str:
+    return _lib.gdn_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise GdnError(rc, where)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on the GPU")
+    return t.data_ptr()
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _code(dt: torch.dtype) -> int:
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt} (float32 or bfloat16)")
+    return _DTYPE_CODE[dt]
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# --------------------------------------------------------------------- conv1d
+
+def gdn_conv1d_causal(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+                      bias: torch.Tensor | None = None, cu_seqlens: torch.Tensor | None = None,
+                      silu: bool = True) -> torch.Tensor:
+    """Depthwise causal conv1d (W = 4) with optional SiLU. x: [B, T, C] with
+    the channel dim contiguous; w: [C, 4]; cu_seqlens: int32 [N+1] for packed
+    sequences (B == 1). Returns y [B, T, C] (allocated if not given)."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [B, T, C] with a contiguous channel dim")
+    B, T, C = x.shape
+    if y is None:
+        y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
+    if w.dim() != 2 or not w.is_contiguous() or w.dtype != x.dtype or y.dtype != x.dtype:
+        raise ValueError("w must be a contiguous [C, W] tensor of x's dtype; y of x's dtype")
+    if bias is not None and (bias.dtype != x.dtype or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [C] tensor of x's dtype")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rc = _lib.gdn_conv1d_causal(_dev(x, "x"), x.stride(0), x.stride(1), _dev(w, "w"),
+                                _opt(bias, "bias"), _dev(y, "y"), y.stride(0), y.stride(1),
+                                _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, C, w.shape[1],
+                                int(bool(silu)), _code(x.dtype), _stream(x.device))
+    _check(rc, "gdn_conv1d_causal")
+    return y
+
+
+# ---------------------------------------------------------------------- gates
+
+def gdn_gate_prepare(a: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor,
+                     dt_bias: torch.Tensor, g: torch.Tensor | None = None,
+                     beta: torch.Tensor | None = None):
+    """beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias). a, b: [..., H]
+    (rows may be strided, the head dim contiguous). Returns fp32 (g, beta) of
+    a's shape."""
+    if a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("a and b must have the same shape and dtype")
+    H = a.shape[-1]
+    a2 = a.reshape(-1, H) if a.dim() != 2 else a
+    b2 = b.reshape(-1, H) if b.dim() != 2 else b
+    if a2.stride(-1) != 1 or b2.stride(-1) != 1:
+        raise ValueError("the head dim of a and b must be contiguous")
+    R = a2.shape[0]
+    if g is None:
+        g = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    if beta is None:
+        beta = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    for t, n in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != R * H:
+            raise ValueError(f"{n} must be a contiguous fp32 tensor with {R * H} elements")
+    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != H:
+            raise ValueError(f"{n} must be a contiguous fp32 [H] tensor")
+    rc = _lib.gdn_gate_prepare(_dev(a2, "a"), a2.stride(0), _dev(b2, "b"), b2.stride(0),
+                               _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"), _dev(g, "g"),
+                               _dev(beta, "beta"), R, H, _code(a.dtype), _stream(a.device))
+    _check(rc, "gdn_gate_prepare")
+    return g, beta
+
+
+# ----------------------------------------------------------------- chunk fwd
+
+def gdn_chunk_fwd_workspace_size(B: int, T: int, H: int, Hk: int, K: int, V: int,
+                                 n_seqs: int, dtype: torch.dtype) -> int:
+    return int(_lib.gdn_chunk_fwd_workspace_size(B, T, H, Hk, K, V, n_seqs, _code(dtype)))
+
+
+def _token_rows(t: torch.Tensor, name: str, heads: int, d: int):
+    """[B, T, heads, d] with contiguous (heads, d) and batch stride T * token stride."""
+    if t.dim() != 4 or t.shape[2] != heads or t.shape[3] != d:
+        raise ValueError(f"{name} must be [B, T, {heads}, {d}]")
+    B, T = t.shape[:2]
+    st = t.stride(1)
+    if t.stride(3) != 1 or t.stride(2) != d or (B > 1 and T > 0 and t.stride(0) != T * st):
+        raise ValueError(f"{name}: heads and head dim must be contiguous and batches evenly strided")
+    return st
+
+
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, initial_state: torch.Tensor | None = None,
+                  output_final_state: bool = True, cu_seqlens: torch.Tensor | None = None,
+                  scale: float = 1.0, qk_l2norm: bool = True,
+                  workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                  final_state: torch.Tensor | None = None):
+    """Chunked gated delta rule. q, k: [B, T, Hk, K]; v: [B, T, H, V] (token
+    rows may be strided views of the conv output); g, beta: fp32 [B, T, H];
+    initial_state: fp32 [N, H, K, V] or None. Returns (o [B, T, H, V],
+    final_state [N, H, K, V] or None)."""
+    B, T, Hk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    st_qk = _token_rows(q, "q", Hk, K)
+    if _token_rows(k, "k", Hk, K) != st_qk or k.shape != q.shape:
+        raise ValueError("q and k must share shape and strides")
+    st_v = _token_rows(v, "v", H, V)
+    if v.shape[:2] != (B, T) or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must agree in batch, length and dtype")
+    for t, n in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (B, T, H):
+            raise ValueError(f"{n} must be a contiguous fp32 [B, T, H] tensor")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    N = n_seqs if cu_seqlens is not None else B
+    if initial_state is not None and (initial_state.dtype != torch.float32 or
+                                      not initial_state.is_contiguous() or
+                                      initial_state.shape != (N, H, K, V)):
+        raise ValueError(f"initial_state must be a contiguous fp32 [{N}, {H}, {K}, {V}] tensor")
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    ws_bytes = gdn_chunk_fwd_workspace_size(B, T, H, Hk, K, V, n_seqs, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    rc = _lib.gdn_chunk_fwd(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(v, "v"), st_v, _dev(g, "g"),
+                            _dev(beta, "beta"), _opt(initial_state, "initial_state"),
+                            _opt(final_state, "final_state"), _dev(o, "o"),
+                            _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
+                            float(scale), int(bool(qk_l2norm)), _code(q.dtype),
+                            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                            _stream(q.device))
+    _check(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+# -------------------------------------------------------------------- decode
+
+def gdn_recurrent_decode(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
+                         dt_bias: torch.Tensor, state: torch.Tensor, M: int, H: int, G: int,
+                         P: int, N: int, o: torch.Tensor | None = None, scale: float = 1.0,
+                         qk_l2norm: bool = True) -> torch.Tensor:
+    """One decode token for n requests. x: [n, M*H*P + M*G*N + G*N] (v | k | q);
+    ba: [n, M*H + H] (b | a), rows may be strided; state: fp32 [n, H, N, P],
+    updated in place. Returns o [n, H, P] in x's dtype."""
+    if x.dim() == 3:
+        x = x.reshape(x.shape[0], x.shape[-1])
+    if ba.dim() == 3:
+        ba = ba.reshape(ba.shape[0], ba.shape[-1])
+    n = x.shape[0]
+    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[0] != n or ba.dtype != x.dtype:
+        raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
+    if state.dtype != torch.float32 or not state.is_contiguous() or state.shape != (n, H, N, P):
+        raise ValueError(f"state must be a contiguous fp32 [{n}, {H}, {N}, {P}] tensor")
+    if o is None:
+        o = torch.empty((n, H, P), dtype=x.dtype, device=x.device)
+    rc = _lib.gdn_recurrent_decode(_dev(x, "x"), x.stride(0), _dev(ba, "ba"), ba.stride(0),
+                                   _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
+                                   _dev(state, "state"), _dev(o, "o"), n, M, H, G, P, N,
+                                   float(scale), int(bool(qk_l2norm)), _code(x.dtype),
+                                   _stream(x.device))
+    _check(rc, "gdn_recurrent_decode")
+    return o
+
+
+# ------------------------------------------------------------ prefill chain
+
+def split_qkv(y: torch.Tensor, Hk: int, K: int, H: int, V: int):
+    """Zero-copy q, k, v views of the conv output y [B, T, 2*Hk*K + H*V]
+    (channel order q | k | v)."""
+    B, T, C = y.shape
+    if C != 2 * Hk * K + H * V:
+        raise ValueError("channel count does not match q | k | v")
+    q = y[:, :, :Hk * K].unflatten(2, (Hk, K))
+    k = y[:, :, Hk * K:2 * Hk * K].unflatten(2, (Hk, K))
+    v = y[:, :, 2 * Hk * K:].unflatten(2, (H, V))
+    return q, k, v
+
+
+def prefill_chain(x, w, a, b, A_log, dt_bias, *, Hk, K, H, V, initial_state=None,
+                  cu_seqlens=None, scale=1.0, qk_l2norm=True, bufs: dict | None = None):
+    """conv1d + SiLU -> q|k|v views -> gates -> chunked forward. Returns
+    (o, final_state). `bufs` may hold preallocated 'y', 'g', 'beta', 'o',
+    'final_state' and 'workspace' tensors."""
+    bufs = {} if bufs is None else bufs
+    y = gdn_conv1d_causal(x, w, y=bufs.get("y"), cu_seqlens=cu_seqlens, silu=True)
+    q, k, v = split_qkv(y, Hk, K, H, V)
+    g, beta = gdn_gate_prepare(a, b, A_log, dt_bias, g=bufs.get("g"), beta=bufs.get("beta"))
+    return gdn_chunk_fwd(q, k, v, g, beta, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                         scale=scale, qk_l2norm=qk_l2norm, workspace=bufs.get("workspace"),
+                         o=bufs.get("o"), final_state=bufs.get("final_state"))

@@ -1,0 +1,142 @@
+// conv1d.hip -- depthwise causal convolution (W = 4) with optional SiLU.
+//
+// "ZzCompute" (PyTorch Helion Hackathon gallery), item 1 "Causal Conv1d":
+// each channel is convolved with its own past; the width is a compile-time
+// constant so the tap loop unrolls; out-of-range taps are masked to zero
+// instead of padding on the host; the operation is memory bound.
+//
+// Design for CDNA4: the op streams [B, T, C] once in and once out, so it is
+// bound by HBM. A thread owns one 16-byte group of channels (8 bf16 or 4
+// fp32) for a run of RUN consecutive tokens: it issues all RUN row loads up
+// front (RUN x 16 B in flight per lane), keeps the last W-1 inputs in
+// registers as a sliding window, and writes each output row with one 16-byte
+// store. A wave covers 64 adjacent channel groups (1 KiB of one token row),
+// so every access is a fully coalesced 1 KiB segment. Taps before the start
+// of a token's sequence read zero; with packed sequences the run tracks the
+// next boundary and clears its window there.
+#include "gdn_common.hpp"
+
+namespace gdn {
+
+constexpr int kConvW = 4;
+constexpr int kConvRun = 16;       // tokens per thread
+constexpr int kConvThreads = 256;
+
+template <typename T, int RUN>
+__global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
+    const T* __restrict__ x, int64_t xsb, int64_t xst,
+    const T* __restrict__ w, const T* __restrict__ bias,
+    T* __restrict__ y, int64_t ysb, int64_t yst,
+    const int32_t* __restrict__ cu, int n_seqs,
+    int T_len, int C, int runs_per_row, int silu)
+{
+    typedef V16<T> V;
+    constexpr int VN = V::n;
+    const int ncg = C / VN;
+    const int cg = blockIdx.y * kConvThreads + threadIdx.x;
+    if (cg >= ncg) return;
+    const int b = blockIdx.x / runs_per_row;
+    const int t0 = (blockIdx.x % runs_per_row) * RUN;
+    const int c0 = cg * VN;
+
+    // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e]
+    float wt[kConvW][VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e)
+#pragma unroll
+        for (int j = 0; j < kConvW; ++j) wt[j][e] = to_f32(w[(int64_t)(c0 + e) * kConvW + j]);
+    float bs[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) bs[e] = bias ? to_f32(bias[c0 + e]) : 0.f;
+
+    const T* xb = x + (int64_t)b * xsb + c0;
+    T* yb = y + (int64_t)b * ysb + c0;
+
+    // sequence bounds of the first token of the run
+    int seq_start = 0, seq_end = T_len, si = 0;
+    if (cu) {
+        si = find_seq(cu, n_seqs, t0 < T_len ? t0 : T_len - 1);
+        seq_start = cu[si];
+        seq_end = cu[si + 1];
+    }
+
+    // issue every load of the run (window + RUN rows) before using any
+    typename V::type raw[kConvW - 1 + RUN];
+#pragma unroll
+    for (int i = 0; i < kConvW - 1 + RUN; ++i) {
+        int t = t0 - (kConvW - 1) + i;
+        if (t >= 0 && t < T_len)
+            raw[i] = *reinterpret_cast<const typename V::type*>(xb + (int64_t)t * xst);
+        else
+            raw[i] = typename V::type{};
+    }
+
+    float win[kConvW - 1][VN];   // x[t-3], x[t-2], x[t-1]
+#pragma unroll
+    for (int i = 0; i < kConvW - 1; ++i) {
+        int t = t0 - (kConvW - 1) + i;
+        typename V::ftype f = V::to_float(raw[i]);
+        bool live = (t >= seq_start);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) win[i][e] = live ? f[e] : 0.f;
+    }
+
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        const int t = t0 + i;
+        if (t >= T_len) break;
+        if (cu && t >= seq_end) {
+            // crossed into a later sequence: its taps start from zero
+            while (t >= seq_end) { ++si; seq_start = cu[si]; seq_end = cu[si + 1]; }
+#pragma unroll
+            for (int a = 0; a < kConvW - 1; ++a)
+#pragma unroll
+                for (int e = 0; e < VN; ++e)
+                    win[a][e] = (t - (kConvW - 1) + a >= seq_start) ? win[a][e] : 0.f;
+        }
+        typename V::ftype xf = V::to_float(raw[kConvW - 1 + i]);
+        typename V::ftype out;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+            float acc = bs[e];
+            acc = fmaf(wt[0][e], win[0][e], acc);
+            acc = fmaf(wt[1][e], win[1][e], acc);
+            acc = fmaf(wt[2][e], win[2][e], acc);
+            acc = fmaf(wt[3][e], xf[e], acc);
+            out[e] = silu ? acc / (1.f + __expf(-acc)) : acc;
+            win[0][e] = win[1][e];
+            win[1][e] = win[2][e];
+            win[2][e] = xf[e];
+        }
+        *reinterpret_cast<typename V::type*>(yb + (int64_t)t * yst) = V::from_float(out);
+    }
+}
+
+template <typename T>
+hipError_t launch_conv1d_t(const void* x, int64_t xsb, int64_t xst, const void* w,
+                           const void* bias, void* y, int64_t ysb, int64_t yst,
+                           const int32_t* cu, int n_seqs, int B, int T_len, int C, int silu,
+                           hipStream_t stream)
+{
+    const int ncg = C / V16<T>::n;
+    const int runs = (T_len + kConvRun - 1) / kConvRun;
+    dim3 grid(runs * B, (ncg + kConvThreads - 1) / kConvThreads);
+    hipLaunchKernelGGL((conv1d_causal_kernel<T, kConvRun>), grid, dim3(kConvThreads), 0, stream,
+                       (const T*)x, xsb, xst, (const T*)w, (const T*)bias, (T*)y, ysb, yst,
+                       cu, n_seqs, T_len, C, runs, silu);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w,
+                         const void* bias, void* y, int64_t ysb, int64_t yst,
+                         const int32_t* cu, int n_seqs, int B, int T_len, int C, int silu,
+                         bool bf16_io, hipStream_t stream)
+{
+    if (bf16_io)
+        return launch_conv1d_t<bf16>(x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C,
+                                     silu, stream);
+    return launch_conv1d_t<float>(x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C,
+                                  silu, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,183 @@
+// decode.hip -- one decode token of a Gated DeltaProduct layer, fused:
+// split + gate + L2 norm + M Householder sub-steps + readout, state in place.
+//
+// Megatron-Core API docs, "core.ssm.ops.gdp.decode_prepare": the module
+// introduction describes the preparation (split value/key/query, expand q/k
+// groups to heads, interleave the Householder copies with the query on the
+// last copy and the decay on the first, gate ba into beta and g); the
+// "gdp_decode_prepare" Returns list says the recurrent kernel then runs an
+// M-length sequence per request. The preparation is launch-bound on its own,
+// which is why it is fused here rather than written out.
+//
+// Design for CDNA4: the op streams the fp32 state (64 KiB per request and
+// head at N = P = 128) once in and once out, so it is HBM bound. One
+// 256-thread workgroup owns one (request, head) state: thread (rg, cg) holds
+// columns 4cg..4cg+3 of rows rg, rg+RG, rg+2RG, ... in registers, loaded with
+// 16-byte loads (a wave reads whole 512-byte rows: coalesced). Each sub-step
+// needs h^T k (a reduction over rows): per-thread partial sums, then one LDS
+// exchange across the RG row groups (double-buffered, one barrier per
+// sub-step). The state never leaves registers between the M sub-steps, so it
+// is read once and written once per token.
+#include "gdn_common.hpp"
+
+namespace gdn {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeMaxM = 4;
+
+__device__ __forceinline__ float dec_softplus(float x) {
+    return x > 20.f ? x : log1pf(expf(x));
+}
+
+template <typename T, int NK, int PV>
+__global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
+    const T* __restrict__ x, int64_t xs, const T* __restrict__ ba, int64_t bas,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    float* __restrict__ state, T* __restrict__ o,
+    int M, int H, int G, float scale, int l2norm)
+{
+    constexpr int CG = PV / 4;               // column groups of 4
+    constexpr int RG = kDecodeThreads / CG;  // row groups
+    constexpr int RPT = NK / RG;             // rows per thread
+    static_assert(RPT * RG == NK && CG * RG == kDecodeThreads, "tile shape");
+
+    __shared__ float kv[kDecodeMaxM][NK];
+    __shared__ float qv[NK];
+    __shared__ float vv[kDecodeMaxM][PV];
+    __shared__ __align__(16) float red[2][RG][PV];
+    __shared__ float beta_s[kDecodeMaxM];
+    __shared__ float alpha_s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int r = blockIdx.x / H;
+    const int h = blockIdx.x - r * H;
+    const int grp = h / (H / G);
+    const T* xr = x + (int64_t)r * xs;
+    const T* br = ba + (int64_t)r * bas;
+    const int64_t k_base = (int64_t)M * H * PV;
+    const int64_t q_base = k_base + (int64_t)M * G * NK;
+
+    // --- split: this head's value slices, its group's keys and query
+    for (int e = tid; e < M * PV; e += kDecodeThreads) {
+        int m = e / PV, p = e - m * PV;
+        vv[m][p] = to_f32(xr[((int64_t)m * H + h) * PV + p]);
+    }
+    for (int e = tid; e < M * NK; e += kDecodeThreads) {
+        int m = e / NK, i = e - m * NK;
+        kv[m][i] = to_f32(xr[k_base + ((int64_t)m * G + grp) * NK + i]);
+    }
+    for (int i = tid; i < NK; i += kDecodeThreads) qv[i] = to_f32(xr[q_base + (int64_t)grp * NK + i]);
+    // --- gates: beta per copy, the decay on copy 0 only
+    if (tid < M) beta_s[tid] = 1.f / (1.f + expf(-to_f32(br[(int64_t)tid * H + h])));
+    if (tid == kWave) {
+        float a = to_f32(br[(int64_t)M * H + h]);
+        alpha_s = expf(-expf(A_log[h]) * dec_softplus(a + dt_bias[h]));
+    }
+
+    // --- issue the state loads early: they are the bulk of the traffic
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    float* st = state + ((int64_t)r * H + h) * NK * PV;
+    f32x4 S[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        S[j] = *reinterpret_cast<const f32x4*>(st + (int64_t)(rg + RG * j) * PV + 4 * cg);
+    __syncthreads();
+
+    // --- L2 normalisation of k_0..k_{M-1} and q, one wave per vector
+    if (l2norm) {
+        for (int vec = wave; vec <= M; vec += kDecodeThreads / kWave) {
+            float* z = (vec < M) ? kv[vec] : qv;
+            float ss = 0.f;
+            for (int i = lane; i < NK; i += kWave) ss += z[i] * z[i];
+            ss = wave_sum(ss);
+            float inv = 1.f / sqrtf(ss + 1e-6f);
+            for (int i = lane; i < NK; i += kWave) z[i] *= inv;
+        }
+        __syncthreads();
+    }
+
+    const float alpha = alpha_s;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) S[j] *= alpha;
+
+    // --- M sub-steps: u = beta (v - h^T k); h += k u^T
+    for (int m = 0; m < M; ++m) {
+        f32x4 part = zero4();
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) part += S[j] * kv[m][rg + RG * j];
+        *reinterpret_cast<f32x4*>(&red[m & 1][rg][4 * cg]) = part;
+        __syncthreads();
+        f32x4 hk = zero4();
+#pragma unroll
+        for (int a = 0; a < RG; ++a) hk += *reinterpret_cast<const f32x4*>(&red[m & 1][a][4 * cg]);
+        const f32x4 vm = *reinterpret_cast<const f32x4*>(&vv[m][4 * cg]);
+        const f32x4 u = beta_s[m] * (vm - hk);
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) S[j] += kv[m][rg + RG * j] * u;
+    }
+
+    // --- readout of the last copy: o = scale * h^T q
+    {
+        f32x4 part = zero4();
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) part += S[j] * qv[rg + RG * j];
+        *reinterpret_cast<f32x4*>(&red[M & 1][rg][4 * cg]) = part;
+        __syncthreads();
+        if (rg == 0) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int a = 0; a < RG; ++a) acc += *reinterpret_cast<const f32x4*>(&red[M & 1][a][4 * cg]);
+            T* orow = o + ((int64_t)r * H + h) * PV + 4 * cg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) orow[e] = from_f32<T>(scale * acc[e]);
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        *reinterpret_cast<f32x4*>(st + (int64_t)(rg + RG * j) * PV + 4 * cg) = S[j];
+}
+
+template <typename T, int NK, int PV>
+static void launch_decode_nkpv(const void* x, int64_t xs, const void* ba, int64_t bas,
+                               const float* A_log, const float* dt_bias, float* state, void* o,
+                               int n, int M, int H, int G, float scale, int l2norm,
+                               hipStream_t stream)
+{
+    hipLaunchKernelGGL((gdp_decode_kernel<T, NK, PV>), dim3((unsigned)((int64_t)n * H)),
+                       dim3(kDecodeThreads), 0, stream, (const T*)x, xs, (const T*)ba, bas,
+                       A_log, dt_bias, state, (T*)o, M, H, G, scale, l2norm);
+}
+
+template <typename T>
+static void launch_decode_t(const void* x, int64_t xs, const void* ba, int64_t bas,
+                            const float* A_log, const float* dt_bias, float* state, void* o,
+                            int n, int M, int H, int G, int P, int N, float scale, int l2norm,
+                            hipStream_t stream)
+{
+    if (N == 128 && P == 128)
+        launch_decode_nkpv<T, 128, 128>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, scale, l2norm, stream);
+    else if (N == 128 && P == 64)
+        launch_decode_nkpv<T, 128, 64>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, scale, l2norm, stream);
+    else if (N == 64 && P == 128)
+        launch_decode_nkpv<T, 64, 128>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, scale, l2norm, stream);
+    else
+        launch_decode_nkpv<T, 64, 64>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, scale, l2norm, stream);
+}
+
+hipError_t launch_recurrent_decode(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                   const float* A_log, const float* dt_bias, float* state,
+                                   void* o, int n, int M, int H, int G, int P, int N, float scale,
+                                   int l2norm, bool bf16_io, hipStream_t stream)
+{
+    if (bf16_io)
+        launch_decode_t<bf16>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, P, N, scale, l2norm, stream);
+    else
+        launch_decode_t<float>(x, xs, ba, bas, A_log, dt_bias, state, o, n, M, H, G, P, N, scale, l2norm, stream);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,158 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: argument validation,
+// dtype / shape dispatch, workspace carving and launches on the caller's
+// stream. Validation finishes before the first HIP call, so a rejected call
+// has no side effect and the checks can be exercised without a GPU.
+#include <climits>
+#include <cstdint>
+
+#include "../../include/gdn.h"
+#include "gdn_common.hpp"
+
+namespace gdn {
+hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w, const void* bias,
+                         void* y, int64_t ysb, int64_t yst, const int32_t* cu, int n_seqs, int B,
+                         int T_len, int C, int silu, bool bf16_io, hipStream_t stream);
+hipError_t launch_gate_prepare(const void* a, int64_t asr, const void* b, int64_t bsr,
+                               const float* A_log, const float* dt_bias, float* g, float* beta,
+                               int R, int H, bool bf16_in, hipStream_t stream);
+size_t chunk_workspace_bytes(int B, int T_len, int H, int n_seqs, bool packed, bool bf16);
+hipError_t launch_chunk_fwd(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
+                            const float* g, const float* beta, const float* S0, float* Sf,
+                            void* o, const int32_t* cu, int n_seqs, int B, int T_len, int H,
+                            int Hk, int K, int V, float scale, int l2norm, bool bf16, void* ws,
+                            hipStream_t stream);
+hipError_t launch_recurrent_decode(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                   const float* A_log, const float* dt_bias, float* state,
+                                   void* o, int n, int M, int H, int G, int P, int N, float scale,
+                                   int l2norm, bool bf16_io, hipStream_t stream);
+}  // namespace gdn
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_dtype(int d) { return d == GDN_FP32 || d == GDN_BF16; }
+inline int elem_size(int d) { return d == GDN_BF16 ? 2 : 4; }
+inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
+// a row stride in elements that keeps every row 16-byte aligned
+inline bool stride16(int64_t s, int dtype) { return (s * elem_size(dtype)) % 16 == 0; }
+
+inline int status_from(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+    case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: unsupported size, dtype or alignment";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace too small";
+    case GDN_ELAUNCH: return "GDN_ELAUNCH: kernel launch failed";
+    default: return "GDN_UNKNOWN_STATUS";
+    }
+}
+
+int gdn_conv1d_causal(const void* x, int64_t x_stride_b, int64_t x_stride_t, const void* w,
+                      const void* bias, void* y, int64_t y_stride_b, int64_t y_stride_t,
+                      const int32_t* cu_seqlens, int n_seqs, int B, int T, int C, int W, int silu,
+                      int dtype, void* stream)
+{
+    if (B < 1 || T < 0 || C < 1) return GDN_EINVAL;
+    if (!w || (T > 0 && (!x || !y))) return GDN_EINVAL;   // no tokens: x, y may be NULL
+    if (silu != 0 && silu != 1) return GDN_EINVAL;
+    if (T > 0 && x == y) return GDN_EINVAL;
+    if (cu_seqlens && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
+    if (x_stride_t < C || y_stride_t < C) return GDN_EINVAL;
+    if (B > 1 && (x_stride_b < (int64_t)T * x_stride_t || y_stride_b < (int64_t)T * y_stride_t))
+        return GDN_EINVAL;
+    if (!valid_dtype(dtype) || W != 4) return GDN_EUNSUPPORTED;
+    const int vn = 16 / elem_size(dtype);
+    if (C % vn != 0) return GDN_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(y) || !stride16(x_stride_t, dtype) ||
+        !stride16(y_stride_t, dtype) || (B > 1 && (!stride16(x_stride_b, dtype) || !stride16(y_stride_b, dtype))))
+        return GDN_EUNSUPPORTED;
+    if (T == 0) return GDN_OK;
+    if ((C / vn + 255) / 256 > 65535 || (int64_t)((T + 15) / 16) * B > INT_MAX) return GDN_EUNSUPPORTED;
+    return status_from(gdn::launch_conv1d(x, x_stride_b, x_stride_t, w, bias, y, y_stride_b,
+                                          y_stride_t, cu_seqlens, n_seqs, B, T, C, silu,
+                                          dtype == GDN_BF16, (hipStream_t)stream));
+}
+
+int gdn_gate_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
+                     const float* A_log, const float* dt_bias, float* g, float* beta, int R, int H,
+                     int in_dtype, void* stream)
+{
+    if (!a || !b || !A_log || !dt_bias || !g || !beta) return GDN_EINVAL;
+    if (R < 0 || H < 1) return GDN_EINVAL;
+    if (a_stride_row < H || b_stride_row < H) return GDN_EINVAL;
+    if ((const void*)g == (const void*)beta) return GDN_EINVAL;
+    if (!valid_dtype(in_dtype)) return GDN_EUNSUPPORTED;
+    if ((int64_t)R * H > (int64_t)INT_MAX * 256) return GDN_EUNSUPPORTED;
+    if (R == 0) return GDN_OK;
+    return status_from(gdn::launch_gate_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias,
+                                                g, beta, R, H, in_dtype == GDN_BF16,
+                                                (hipStream_t)stream));
+}
+
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int Hk, int K, int V, int n_seqs, int dtype)
+{
+    (void)Hk; (void)K; (void)V;
+    if (B < 1 || T < 0 || H < 1 || n_seqs < 0) return 0;
+    const bool packed = n_seqs > 0;
+    return gdn::chunk_workspace_bytes(B, T, H, packed ? n_seqs : 0, packed, dtype == GDN_BF16);
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t, const void* v,
+                  int64_t v_stride_t, const float* g, const float* beta,
+                  const float* initial_state, float* final_state, void* o,
+                  const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K, int V,
+                  float scale, int qk_l2norm, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream)
+{
+    if (B < 1 || T < 0 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_EINVAL;
+    const bool has_tokens = T > 0;   // with no tokens the token tensors may be NULL
+    if (!workspace || (has_tokens && (!q || !k || !v || !g || !beta || !o))) return GDN_EINVAL;
+    if (qk_l2norm != 0 && qk_l2norm != 1) return GDN_EINVAL;
+    if (cu_seqlens && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
+    if ((int64_t)B * T > INT_MAX) return GDN_EINVAL;
+    if (!valid_dtype(dtype) || !head_dim_ok(K) || !head_dim_ok(V)) return GDN_EUNSUPPORTED;
+    if (qk_stride_t < (int64_t)Hk * K || v_stride_t < (int64_t)H * V) return GDN_EINVAL;
+    if (has_tokens && (o == q || o == k || o == v)) return GDN_EINVAL;
+    if (final_state && (const void*)final_state == (const void*)o) return GDN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !stride16(qk_stride_t, dtype) || !stride16(v_stride_t, dtype) ||
+        (initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return GDN_EUNSUPPORTED;
+    const int ns = cu_seqlens ? n_seqs : 0;
+    const size_t need = gdn::chunk_workspace_bytes(B, T, H, ns, cu_seqlens != nullptr, dtype == GDN_BF16);
+    if (workspace_bytes < need) return GDN_EWORKSPACE;
+    return status_from(gdn::launch_chunk_fwd(q, k, qk_stride_t, v, v_stride_t, g, beta,
+                                             initial_state, final_state, o, cu_seqlens, n_seqs, B,
+                                             T, H, Hk, K, V, scale, qk_l2norm, dtype == GDN_BF16,
+                                             workspace, (hipStream_t)stream));
+}
+
+int gdn_recurrent_decode(const void* x, int64_t x_stride_n, const void* ba, int64_t ba_stride_n,
+                         const float* A_log, const float* dt_bias, float* state, void* o, int n,
+                         int M, int H, int G, int P, int N, float scale, int qk_l2norm, int dtype,
+                         void* stream)
+{
+    if (!x || !ba || !A_log || !dt_bias || !state || !o) return GDN_EINVAL;
+    if (n < 0 || M < 1 || H < 1 || G < 1 || H % G != 0) return GDN_EINVAL;
+    if (qk_l2norm != 0 && qk_l2norm != 1) return GDN_EINVAL;
+    if ((const void*)o == (const void*)state) return GDN_EINVAL;
+    if (!valid_dtype(dtype) || !head_dim_ok(P) || !head_dim_ok(N) || M > 4) return GDN_EUNSUPPORTED;
+    const int64_t row = (int64_t)M * H * P + (int64_t)M * G * N + (int64_t)G * N;
+    if (x_stride_n < row || ba_stride_n < (int64_t)M * H + H) return GDN_EINVAL;
+    if (!aligned16(state)) return GDN_EUNSUPPORTED;
+    if ((int64_t)n * H > INT_MAX) return GDN_EUNSUPPORTED;
+    if (n == 0) return GDN_OK;
+    return status_from(gdn::launch_recurrent_decode(x, x_stride_n, ba, ba_stride_n, A_log, dt_bias,
+                                                    state, o, n, M, H, G, P, N, scale, qk_l2norm,
+                                                    dtype == GDN_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

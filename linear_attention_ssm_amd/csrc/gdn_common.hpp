@@ -1,0 +1,130 @@
+// gdn_common.hpp -- device helpers for the gfx950 (CDNA4) kernels.
+//
+// Element types, 16-byte vector access, wave64 reductions, and the MFMA
+// fragment conventions used by the chunk kernels.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_bf16 for bf16 operands and
+// v_mfma_f32_16x16x4f32, eight times, for fp32 operands), for lane l with
+// grp = l >> 4 and col = l & 15:
+//   * accumulator D (16 x 16 fp32): lane holds D[4*grp + e][col], e = 0..3;
+//   * A operand (16 rows x 32 contraction): lane supplies row `col`;
+//   * B operand (32 contraction x 16 cols): lane supplies column `col`.
+// Inside one 32-wide contraction block a lane's eight operand slots stand for
+// the contraction indices  4*grp + {0,1,2,3}  and  16 + 4*grp + {0,1,2,3}.
+// The product only needs A and B to agree on that assignment, and with it a
+// pair of accumulator tiles covering contraction rows [0,16) and [16,32) IS a
+// B operand: no LDS round trip is needed to feed a result (the state h, the
+// corrected values U) into the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;      // timesteps per chunk ([ZZ] item 2: 64-timestep chunks)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// 16 bytes of elements: 8 x bf16 or 4 x fp32.
+template <typename T> struct V16;
+template <> struct V16<bf16> {
+    static constexpr int n = 8;
+    typedef bf16x8 type;
+    typedef f32x8 ftype;
+    static __device__ __forceinline__ ftype to_float(type v) { return __builtin_convertvector(v, f32x8); }
+    static __device__ __forceinline__ type from_float(ftype v) { return __builtin_convertvector(v, bf16x8); }
+};
+template <> struct V16<float> {
+    static constexpr int n = 4;
+    typedef f32x4 type;
+    typedef f32x4 ftype;
+    static __device__ __forceinline__ ftype to_float(type v) { return v; }
+    static __device__ __forceinline__ type from_float(ftype v) { return v; }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = width / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    typedef bf16x8 Frag;
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Operand fragment of a row-major LDS matrix: row `row`, contraction block
+    // starting at column c0; slots as described at the top of this file.
+    static __device__ __forceinline__ Frag lds_frag(const bf16* m, int ld, int row, int c0, int grp) {
+        const bf16* p = m + row * ld + c0 + 4 * grp;
+        bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+        bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // B operand from two accumulator tiles covering contraction rows [0,16), [16,32).
+    static __device__ __forceinline__ Frag acc_frag(f32x4 lo, f32x4 hi) {
+        f32x8 f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_convertvector(f, bf16x8);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef f32x8 Frag;
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ Frag lds_frag(const float* m, int ld, int row, int c0, int grp) {
+        const float* p = m + row * ld + c0 + 4 * grp;
+        f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+        f32x4 hi = *reinterpret_cast<const f32x4*>(p + 16);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ Frag acc_frag(f32x4 lo, f32x4 hi) {
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Index of the packed sequence containing token t: the largest i with
+// cu[i] <= t (binary search over cu[0..n]); requires cu[0] <= t < cu[n].
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n, int t) {
+    int lo = 0, hi = n;  // invariant: cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace gdn

@@ -1,0 +1,205 @@
+"""The C-ABI boundary, without a GPU: the library loads, exports every entry
+point that include/gdn.h declares, and rejects bad arguments with the
+documented status codes (validation runs before any HIP call, so these calls
+never touch a device; the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "linear_attention_ssm_amd", "libgdn.so")
+
+OK, EINVAL, EUNSUP, EWS, ELAUNCH = 0, 1, 2, 3, 4
+FP32, BF16 = 0, 1
+P = 0x10000          # fake, 16-byte aligned "device" addresses (never dereferenced)
+P2 = 0x20000
+P3 = 0x30000
+P4 = 0x40000
+P5 = 0x50000
+P6 = 0x60000
+WS = 0x100000        # 256-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built (run `python -m linear_attention_ssm_amd.build`)")
+    L = ctypes.CDLL(LIB)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.gdn_status_string.argtypes = [i32]
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_conv1d_causal.argtypes = [vp, i64, i64, vp, vp, vp, i64, i64, vp, i32] + [i32] * 6 + [vp]
+    L.gdn_gate_prepare.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i32, i32, i32, vp]
+    L.gdn_chunk_fwd_workspace_size.argtypes = [i32] * 8
+    L.gdn_chunk_fwd_workspace_size.restype = sz
+    L.gdn_chunk_fwd.argtypes = ([vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6
+                                + [f32, i32, i32, vp, sz, vp])
+    L.gdn_recurrent_decode.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp] + [i32] * 6 + [f32, i32, i32, vp]
+    return L
+
+
+def test_header_declares_the_four_operations():
+    fns = declared_functions()
+    for name in ("gdn_conv1d_causal", "gdn_gate_prepare", "gdn_chunk_fwd",
+                 "gdn_chunk_fwd_workspace_size", "gdn_recurrent_decode", "gdn_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gdn_[a-z0-9_]+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    for code, name in [(OK, b"GDN_OK"), (EINVAL, b"GDN_EINVAL"), (EUNSUP, b"GDN_EUNSUPPORTED"),
+                       (EWS, b"GDN_EWORKSPACE"), (ELAUNCH, b"GDN_ELAUNCH")]:
+        assert lib.gdn_status_string(code).startswith(name)
+    assert lib.gdn_status_string(99) is not None
+
+
+def conv(lib, **kw):
+    a = dict(x=P, xsb=4096 * 6144, xst=6144, w=P2, bias=None, y=P3, ysb=4096 * 6144, yst=6144,
+             cu=None, n_seqs=0, B=4, T=4096, C=6144, W=4, silu=1, dtype=BF16, stream=None)
+    a.update(kw)
+    return lib.gdn_conv1d_causal(a["x"], a["xsb"], a["xst"], a["w"], a["bias"], a["y"], a["ysb"],
+                                 a["yst"], a["cu"], a["n_seqs"], a["B"], a["T"], a["C"], a["W"],
+                                 a["silu"], a["dtype"], a["stream"])
+
+
+def test_conv_validation(lib):
+    assert conv(lib, x=None) == EINVAL
+    assert conv(lib, w=None) == EINVAL
+    assert conv(lib, y=None) == EINVAL
+    assert conv(lib, y=P) == EINVAL                     # aliasing
+    assert conv(lib, B=0) == EINVAL
+    assert conv(lib, T=-1) == EINVAL
+    assert conv(lib, C=0) == EINVAL
+    assert conv(lib, silu=2) == EINVAL
+    assert conv(lib, xst=100) == EINVAL                 # rows overlap
+    assert conv(lib, cu=P4, n_seqs=3) == EINVAL         # packed needs B == 1
+    assert conv(lib, cu=P4, n_seqs=0, B=1) == EINVAL
+    assert conv(lib, W=3) == EUNSUP
+    assert conv(lib, dtype=7) == EUNSUP
+    assert conv(lib, C=6140, xst=6144, yst=6144) == EUNSUP   # C not a multiple of 8 bf16
+    assert conv(lib, x=P + 2) == EUNSUP                 # misaligned base
+    assert conv(lib, xst=6148, xsb=4096 * 6148) == EUNSUP    # row stride not 16-byte aligned
+    assert conv(lib, T=0) == OK                         # empty input: nothing to launch
+
+
+def gate(lib, **kw):
+    a = dict(a=P, asr=16, b=P2, bsr=16, A_log=P3, dt=P4, g=P5, beta=P6, R=10, H=16, dtype=BF16)
+    a.update(kw)
+    return lib.gdn_gate_prepare(a["a"], a["asr"], a["b"], a["bsr"], a["A_log"], a["dt"], a["g"],
+                                a["beta"], a["R"], a["H"], a["dtype"], None)
+
+
+def test_gate_validation(lib):
+    for key in ("a", "b", "A_log", "dt", "g", "beta"):
+        assert gate(lib, **{key: None}) == EINVAL
+    assert gate(lib, H=0) == EINVAL
+    assert gate(lib, R=-1) == EINVAL
+    assert gate(lib, asr=8) == EINVAL
+    assert gate(lib, beta=P5) == EINVAL                 # g and beta alias
+    assert gate(lib, dtype=5) == EUNSUP
+    assert gate(lib, R=0) == OK
+
+
+def chunk(lib, **kw):
+    a = dict(q=P, k=P + 4096, qks=6144, v=P + 8192, vs=6144, g=P2, beta=P3, S0=None, Sf=P4, o=P5,
+             cu=None, n=0, B=4, T=4096, H=16, Hk=16, K=128, V=128, scale=1.0, l2=1, dtype=BF16,
+             ws=WS, wsb=1 << 40)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["qks"], a["v"], a["vs"], a["g"], a["beta"], a["S0"],
+                             a["Sf"], a["o"], a["cu"], a["n"], a["B"], a["T"], a["H"], a["Hk"], a["K"],
+                             a["V"], a["scale"], a["l2"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_chunk_validation(lib):
+    for key in ("q", "k", "v", "g", "beta", "o", "ws"):
+        assert chunk(lib, **{key: None}) == EINVAL
+    assert chunk(lib, H=16, Hk=3) == EINVAL             # H % Hk
+    assert chunk(lib, B=0) == EINVAL
+    assert chunk(lib, l2=3) == EINVAL
+    assert chunk(lib, cu=P6, n=4) == EINVAL             # packed needs B == 1
+    assert chunk(lib, qks=100) == EINVAL                # q/k rows shorter than Hk*K
+    assert chunk(lib, vs=100) == EINVAL
+    assert chunk(lib, o=P) == EINVAL                    # o aliases q
+    assert chunk(lib, Sf=P5) == EINVAL                  # final state aliases o
+    assert chunk(lib, K=96) == EUNSUP
+    assert chunk(lib, V=256) == EUNSUP
+    assert chunk(lib, dtype=3) == EUNSUP
+    assert chunk(lib, q=P + 2) == EUNSUP
+    assert chunk(lib, ws=WS + 16) == EUNSUP             # workspace must be 256-byte aligned
+    assert chunk(lib, qks=6148) == EUNSUP
+    need = lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    assert chunk(lib, wsb=need - 1) == EWS
+
+
+def test_chunk_workspace_size(lib):
+    # dense: offsets (256 B) + G (4 B x tiles x H x 64) + T (2 B x tiles x H x 64 x 64)
+    tiles, H = 4 * 64, 16
+    need = lib.gdn_chunk_fwd_workspace_size(4, 4096, H, H, 128, 128, 0, BF16)
+    assert need == 256 + 4 * tiles * H * 64 + 2 * tiles * H * 64 * 64
+    fp32 = lib.gdn_chunk_fwd_workspace_size(4, 4096, H, H, 128, 128, 0, FP32)
+    assert fp32 > need
+    # packed: an upper bound on the chunk count, sum(ceil(len/64)) <= (T + 63 n) / 64
+    packed = lib.gdn_chunk_fwd_workspace_size(1, 1000, 4, 4, 64, 64, 10, BF16)
+    tiles_ub = (1000 + 63 * 10) // 64
+    assert packed >= 4 * tiles_ub * 4 * 64 + 2 * tiles_ub * 4 * 64 * 64
+    assert lib.gdn_chunk_fwd_workspace_size(0, 10, 4, 4, 64, 64, 0, BF16) == 0
+
+
+def decode(lib, **kw):
+    M, H, G, Pd, N = 2, 32, 16, 128, 128
+    a = dict(x=P, xs=M * H * Pd + M * G * N + G * N, ba=P2, bas=M * H + H, A_log=P3, dt=P4,
+             state=P5, o=P6, n=256, M=M, H=H, G=G, P=Pd, N=N, scale=1.0, l2=1, dtype=BF16)
+    a.update(kw)
+    return lib.gdn_recurrent_decode(a["x"], a["xs"], a["ba"], a["bas"], a["A_log"], a["dt"],
+                                    a["state"], a["o"], a["n"], a["M"], a["H"], a["G"], a["P"],
+                                    a["N"], a["scale"], a["l2"], a["dtype"], None)
+
+
+def test_decode_validation(lib):
+    for key in ("x", "ba", "A_log", "dt", "state", "o"):
+        assert decode(lib, **{key: None}) == EINVAL
+    assert decode(lib, G=5) == EINVAL                   # H % G
+    assert decode(lib, M=0) == EINVAL
+    assert decode(lib, n=-1) == EINVAL
+    assert decode(lib, xs=100) == EINVAL
+    assert decode(lib, bas=10) == EINVAL
+    assert decode(lib, o=P5) == EINVAL                  # o aliases state
+    assert decode(lib, M=5, xs=10 ** 6, bas=1000) == EUNSUP
+    assert decode(lib, P=96) == EUNSUP
+    assert decode(lib, state=P5 + 4) == EUNSUP
+    assert decode(lib, n=0) == OK
+
+
+def test_binding_fails_loudly_on_cpu_tensors():
+    import torch
+    import linear_attention_ssm_amd as gdn
+    x = torch.zeros(1, 4, 8, dtype=torch.bfloat16)
+    w = torch.zeros(8, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.gdn_conv1d_causal(x, w, y=torch.zeros_like(x))
+
+
+def test_product_path_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "linear_attention_ssm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
