@@ -6,44 +6,76 @@
 // "the sequential bottleneck") and a per-chunk output mixing the inter-chunk
 // state query with intra-chunk causal attention (item 3). The equations it
 // cites by number are not printed; the ones used here follow from the
-// timestep recurrence (per chunk r = 1..L, entering state h, G_r = inclusive
-// cumsum of g inside the chunk, gamma_r = exp(G_r), Gamma_rs = exp(G_r - G_s)
-// for s <= r else 0):
-//     A  = strict_lower(diag(beta) (K K^T o Gamma)),  T = (I + A)^-1 diag(beta)
-//     U  = T (V - diag(gamma) K h)
-//     O  = scale * (diag(gamma) Q h + (Q K^T o Gamma) U)
-//     h' = gamma_L h + (diag(gamma_L / gamma) K)^T U
+// timestep recurrence. Per chunk (rows r = 1..L, entering state h (K x V),
+// G_r = inclusive cumsum of g inside the chunk, gamma_r = exp(G_r),
+// Gamma_rs = exp(G_r - G_s) for s <= r else 0, k^ / q^ = L2-normalised rows):
+//     A  = strict_lower(diag(beta) (K^ K^T o Gamma)),  T = (I + A)^-1 diag(beta)
+//     U  = T (V - diag(gamma) K^ h)
+//     O  = scale (diag(gamma) Q^ h + (Q^ K^T o Gamma) U)
+//     h' = gamma_L h + (diag(gamma_L / gamma) K^)^T U
+// With the row norms n_r of k and m_r of q kept as per-row factors, the MFMA
+// operands of the state products are the RAW q/k rows:
+//     U  = T (V - a o (K h)),   a_r = gamma_r / n_r
+//     O  = b o (Q h) + P U,     b_r = scale gamma_r / m_r,
+//                               P = scale (Q K^T o Gamma) / (m_r n_s)
+//     h' = gamma_L h + K^T (c o U),  c_r = gamma_L / (gamma_r n_r)
 //
 // Split for CDNA4 (two kernels on one stream):
-//   chunk_prep  one workgroup per (chunk, q/k head), all chunks in parallel:
-//               L2-normalise K, K K^T on MFMA, per value head of the group the
-//               cumsum G, A, and the 64 x 64 unit-lower-triangular inverse
-//               (16 x 16 diagonal blocks by forward substitution, off-diagonal
-//               blocks by block substitution on fp32 MFMA), then T = N diag(beta)
-//               and G go to the workspace.
+//   chunk_prep  one workgroup per (chunk, q/k head), every chunk in parallel:
+//               row norms, K K^T and Q K^T on MFMA (shared by the value heads
+//               of a GQA group), then per value head the cumsum, A, the
+//               64 x 64 unit-lower-triangular inverse (16 x 16 diagonal blocks
+//               by forward substitution, off-diagonal blocks by block
+//               substitution on fp32 MFMA), T, P and the factors a, b, c,
+//               gamma_L. T and P are written as ready MFMA A-operand
+//               fragments (only the 6 non-zero 16 x 32 blocks of each).
 //   chunk_scan  one workgroup per (sequence, value head, 16*NW value columns),
 //               sequential over the sequence's chunks. Each wave owns 16 value
-//               columns of the fp32 state, kept in MFMA accumulators for the
+//               columns of the fp32 state, held in MFMA accumulators for the
 //               whole sequence; accumulator tiles feed the next product
 //               directly as B operands (see gdn_common.hpp), so the chain
-//               h -> K h -> U = T(V - gamma K h) -> h' never leaves registers.
-//               Q K^T o Gamma (the intra-chunk attention) is formed per chunk
-//               on MFMA and shared through LDS.
-// The state is never written per chunk: only the final state (if asked for).
+//               h -> K h -> U -> h' never leaves registers. The raw K and Q
+//               tiles and the chunk's record are copied global -> LDS with
+//               direct-to-LDS loads one chunk ahead (double buffer), K^T
+//               operands are read from the row-major K tile with the gfx950
+//               transposing LDS read, and nothing but the outputs and the
+//               final state is written.
 #include "gdn_common.hpp"
 
 namespace gdn {
 
 constexpr int kPrepThreads = 256;
 constexpr int kLowerTiles = 10;     // 16 x 16 tiles on or below the diagonal of a 64 x 64 matrix
+constexpr int kTriFrags = 6;        // non-zero 16 x 32 A-operand blocks of a lower-triangular 64 x 64
 
 // Lower tile t (0..9) in row order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
 __device__ __forceinline__ int tri_row(int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); }
 __device__ __forceinline__ int tri_col(int t) { const int r = tri_row(t); return t - r * (r + 1) / 2; }
+// A-operand block (row tile rt, 32-wide contraction block kb) of a lower-triangular matrix:
+// (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+__device__ __forceinline__ int tri_frag(int rt, int kb) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + kb; }
+__device__ __forceinline__ int tri_frag_rt(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }
+__device__ __forceinline__ int tri_frag_kb(int f) { return f < 2 ? 0 : (f - 2) % 2; }
 
-// LDS row padding (elements) of the staged tiles.
+// Contraction index of operand slot j of lane group grp (see gdn_common.hpp).
+__device__ __forceinline__ int slot_k(int grp, int j) { return j < 4 ? 4 * grp + j : 12 + 4 * grp + j; }
+
+// LDS row padding (elements) of the prep kernel's staged tiles.
 template <typename T> struct Pad { static constexpr int row = 8; };
 template <> struct Pad<float> { static constexpr int row = 4; };
+
+// Per (chunk, value head) record written by chunk_prep and read by chunk_scan:
+//   T fragments [6][64 lanes], P fragments [6][64 lanes], factors float [4][64]
+//   (a, b, c per row; row 3 holds gamma_L).
+template <typename T> struct Rec {
+    typedef typename Mma<T>::Frag Frag;
+    static constexpr int frag_bytes = (int)sizeof(Frag);                  // 16 (bf16) / 32 (fp32)
+    static constexpr int tfrag = 0;
+    static constexpr int pfrag = kTriFrags * kWave * frag_bytes;
+    static constexpr int fac = 2 * kTriFrags * kWave * frag_bytes;
+    static constexpr int bytes = fac + 4 * kChunk * 4;
+    static_assert(bytes % 1024 == 0, "records are copied in 1 KiB pieces");
+};
 
 // ------------------------------------------------------------ chunk plan
 
@@ -78,7 +110,6 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t* __restri
 struct ChunkLoc {
     int tok0;   // first token row of the chunk
     int L;      // valid rows (1..64)
-    int seq;    // sequence index
 };
 
 // tile -> (sequence, chunk). Dense: tile = seq * nck + c. Packed: offsets
@@ -90,7 +121,6 @@ __device__ __forceinline__ bool locate_tile(int tile, const int32_t* __restrict_
     if (!cu) {
         const int nck = (T_len + kChunk - 1) / kChunk;
         const int seq = tile / nck, c = tile - seq * nck;
-        loc.seq = seq;
         loc.tok0 = seq * T_len + c * kChunk;
         loc.L = min(kChunk, T_len - c * kChunk);
         return true;
@@ -101,49 +131,9 @@ __device__ __forceinline__ bool locate_tile(int tile, const int32_t* __restrict_
         int mid = (lo + hi) >> 1;
         if (offsets[mid] <= tile) lo = mid; else hi = mid;
     }
-    const int c = tile - offsets[lo];
-    loc.seq = lo;
-    loc.tok0 = cu[lo] + c * kChunk;
+    loc.tok0 = cu[lo] + (tile - offsets[lo]) * kChunk;
     loc.L = min(kChunk, cu[lo + 1] - loc.tok0);
     return true;
-}
-
-// Stage a 64 x KD tile of token rows (rows >= L zero) into a row-major LDS
-// tile with row stride `ld`, L2-normalising each row when asked. Optionally
-// also writes the transpose (KD x 64, row stride ldt).
-template <typename T, int KD, int NT>
-__device__ __forceinline__ void stage_rows(const T* __restrict__ src, int64_t stride, int L,
-                                           int l2norm, T* dst, int ld, T* dstT, int ldt)
-{
-    typedef V16<T> V;
-    constexpr int VN = V::n;
-    constexpr int SEGS = KD / VN;          // 16-byte segments per row
-    constexpr int RPP = NT / SEGS;         // rows per pass
-    static_assert(SEGS <= kWave && NT % SEGS == 0 && kChunk % RPP == 0, "staging shape");
-    const int tid = threadIdx.x;
-    const int seg = tid % SEGS;
-#pragma unroll
-    for (int p = 0; p < kChunk / RPP; ++p) {
-        const int row = p * RPP + tid / SEGS;
-        typename V::type raw{};
-        if (row < L) raw = *reinterpret_cast<const typename V::type*>(src + row * stride + seg * VN);
-        typename V::ftype f = V::to_float(raw);
-        if (l2norm) {
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < VN; ++e) ss += f[e] * f[e];
-            ss = group_sum<SEGS>(ss);
-            const float inv = 1.f / sqrtf(ss + 1e-6f);
-#pragma unroll
-            for (int e = 0; e < VN; ++e) f[e] *= inv;
-        }
-        typename V::type out = V::from_float(f);
-        *reinterpret_cast<typename V::type*>(dst + row * ld + seg * VN) = out;
-        if (dstT) {
-#pragma unroll
-            for (int e = 0; e < VN; ++e) dstT[(seg * VN + e) * ldt + row] = out[e];
-        }
-    }
 }
 
 // ------------------------------------------------------------ chunk_prep
@@ -152,22 +142,70 @@ template <typename T, int KD>
 struct PrepSmem {
     static constexpr int ldk = KD + Pad<T>::row;
     static constexpr int lda = kChunk + 4;
-    T k[kChunk * ldk];
+    static constexpr int ldp = kChunk + Pad<T>::row;
+    T k[kChunk * ldk];         // raw k rows (rows >= L zero)
+    T q[kChunk * ldk];         // raw q rows
     float a[kChunk * lda];     // A, strictly lower
     float n[kChunk * lda];     // N = (I + A)^-1, lower
+    T p[kChunk * ldp];         // P
     float G[kChunk];
     float beta[kChunk];
+    float rk[kChunk];          // 1 / |k_r| (1 without normalisation)
+    float rq[kChunk];
+};
+
+// A 64 x KD tile of token rows, loaded by NT threads in 16-byte segments (thread
+// tid owns segment tid % SEGS of rows tid / SEGS + p * RPP). All loads are
+// issued before any is used; rows >= L read row L-1 and are zeroed on store.
+template <typename T, int KD, int NT>
+struct RowTile {
+    typedef V16<T> V;
+    static constexpr int VN = V::n;
+    static constexpr int SEGS = KD / VN;
+    static constexpr int RPP = NT / SEGS;
+    static constexpr int NP = kChunk / RPP;
+    static_assert(SEGS <= kWave && NT % SEGS == 0 && kChunk % RPP == 0, "staging shape");
+    typename V::type raw[NP];
+
+    __device__ __forceinline__ void load(const T* __restrict__ src, int64_t stride, int L) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = p * RPP + tid / SEGS;
+            raw[p] = *reinterpret_cast<const typename V::type*>(src + min(row, L - 1) * stride +
+                                                                (tid % SEGS) * VN);
+        }
+    }
+    // Store into a padded row-major LDS tile and record each row's inverse L2 norm.
+    __device__ __forceinline__ void store(int L, int l2norm, T* dst, int ld, float* rnorm) const {
+        const int tid = threadIdx.x;
+        const int seg = tid % SEGS;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = p * RPP + tid / SEGS;
+            typename V::type r = raw[p];
+            if (row >= L) r = typename V::type{};
+            typename V::ftype f = V::to_float(r);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) ss += f[e] * f[e];
+            ss = group_sum<SEGS>(ss);
+            if (seg == 0) rnorm[row] = l2norm ? 1.f / sqrtf(ss + 1e-6f) : 1.f;
+            *reinterpret_cast<typename V::type*>(dst + row * ld + seg * VN) = r;
+        }
+    }
 };
 
 template <typename T, int KD>
 __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
-    const T* __restrict__ kp, int64_t qk_stride, const float* __restrict__ g,
-    const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ offsets, int n_seqs, int T_len, int H, int Hk, int l2norm,
-    float* __restrict__ ws_G, T* __restrict__ ws_T)
+    const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets, int n_seqs, int T_len,
+    int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec)
 {
     typedef Mma<T> MT;
     typedef PrepSmem<T, KD> SM;
+    typedef Rec<T> RC;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -175,6 +213,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int hk = blockIdx.y;
     ChunkLoc loc;
     if (!locate_tile(tile, cu, offsets, n_seqs, T_len, loc)) return;
+    const int L = loc.L;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -182,37 +221,40 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const int grp = lane >> 4;
     const int col = lane & 15;
 
-    stage_rows<T, KD, kPrepThreads>(kp + (int64_t)loc.tok0 * qk_stride + hk * KD, qk_stride,
-                                    loc.L, l2norm, sm.k, SM::ldk, (T*)nullptr, 0);
+    const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + hk * KD;
+    {
+        RowTile<T, KD, kPrepThreads> kt, qt;
+        kt.load(kp + rowoff, qk_stride, L);
+        qt.load(qp + rowoff, qk_stride, L);
+        kt.store(L, l2norm, sm.k, SM::ldk, sm.rk);
+        qt.store(L, l2norm, sm.q, SM::ldk, sm.rq);
+    }
     __syncthreads();
 
-    // K K^T: the 10 lower 16 x 16 tiles, dealt round-robin to the 4 waves.
-    f32x4 S[3];
+    // raw K K^T (tiles 0..9) and Q K^T (tiles 10..19), lower 16 x 16 tiles, 5 per wave
+    f32x4 S[5];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        S[j] = zero4();
+    for (int j = 0; j < 5; ++j) {
         const int t = wave + 4 * j;
-        if (t < kLowerTiles) {
+        const int tt = t < kLowerTiles ? t : t - kLowerTiles;
+        const T* am = t < kLowerTiles ? sm.k : sm.q;
+        S[j] = zero4();
 #pragma unroll
-            for (int kb = 0; kb < KD / 32; ++kb) {
-                auto a = MT::lds_frag(sm.k, SM::ldk, 16 * tri_row(t) + col, 32 * kb, grp);
-                auto b = MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(t) + col, 32 * kb, grp);
-                S[j] = MT::mma(a, b, S[j]);
-            }
-        }
+        for (int kb = 0; kb < KD / 32; ++kb)
+            S[j] = MT::mma(MT::lds_frag(am, SM::ldk, 16 * tri_row(tt) + col, 32 * kb, grp),
+                           MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(tt) + col, 32 * kb, grp), S[j]);
     }
 
     const int per = H / Hk;
     for (int hv = 0; hv < per; ++hv) {
         const int h = hk * per + hv;
-        const int64_t wsidx = (int64_t)tile * H + h;
+        unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
         if (wave == 0) {
             // G = inclusive cumsum of g over the chunk (rows >= L carry g = 0)
-            float gv = 0.f, bv = 0.f;
-            if (lane < loc.L) {
-                gv = g[(int64_t)(loc.tok0 + lane) * H + h];
-                bv = beta[(int64_t)(loc.tok0 + lane) * H + h];
-            }
+            const int lr = min(lane, L - 1);
+            float gv = g[(int64_t)(loc.tok0 + lr) * H + h];
+            float bv = beta[(int64_t)(loc.tok0 + lr) * H + h];
+            if (lane >= L) { gv = 0.f; bv = 0.f; }
 #pragma unroll
             for (int d = 1; d < kWave; d <<= 1) {
                 float up = __shfl_up(gv, d, kWave);
@@ -220,23 +262,35 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             }
             sm.G[lane] = gv;
             sm.beta[lane] = bv;
-            ws_G[wsidx * kChunk + lane] = gv;
+            const float GL = __shfl(gv, kWave - 1, kWave);
+            const bool live = lane < L;
+            const float gam = __expf(gv);
+            float* fac = reinterpret_cast<float*>(rec + RC::fac);
+            fac[0 * kChunk + lane] = live ? gam * sm.rk[lane] : 0.f;
+            fac[1 * kChunk + lane] = live ? scale * gam * sm.rq[lane] : 0.f;
+            fac[2 * kChunk + lane] = live ? __expf(GL - gv) * sm.rk[lane] : 0.f;
+            fac[3 * kChunk + lane] = __expf(GL);
         }
         __syncthreads();
 
-        // A[r][s] = beta_r exp(G_r - G_s) (k_r . k_s) for s < r
+        // A (normalised keys, strictly lower) and P (scaled, lower incl. diagonal)
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < 5; ++j) {
             const int t = wave + 4 * j;
-            if (t < kLowerTiles) {
-                const int s = 16 * tri_col(t) + col;
-                const float Gs = sm.G[s];
+            const bool isA = t < kLowerTiles;
+            const int tt = isA ? t : t - kLowerTiles;
+            const int s = 16 * tri_col(tt) + col;
+            const float Gs = sm.G[s];
+            const float rks = sm.rk[s];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * tri_row(t) + 4 * grp + e;
-                    float a = 0.f;
-                    if (s < r) a = sm.beta[r] * __expf(sm.G[r] - Gs) * S[j][e];
-                    sm.a[r * SM::lda + s] = a;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tri_row(tt) + 4 * grp + e;
+                const float decay = __expf(fminf(sm.G[r] - Gs, 0.f));
+                if (isA) {
+                    sm.a[r * SM::lda + s] = (s < r) ? sm.beta[r] * decay * sm.rk[r] * rks * S[j][e] : 0.f;
+                } else {
+                    sm.p[r * SM::ldp + s] =
+                        from_f32<T>((s <= r) ? scale * decay * sm.rq[r] * rks * S[j][e] : 0.f);
                 }
             }
         }
@@ -285,22 +339,27 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             __syncthreads();
         }
 
-        // T = N diag(beta), zero above the diagonal; 64 x 64 row-major.
-        {
-            const int r = tid >> 2;
-            const int s0 = (tid & 3) * 16;
-            T* dst = ws_T + wsidx * (kChunk * kChunk) + r * kChunk + s0;
-            typedef V16<T> V;
+        // T = N diag(beta) and P as A-operand fragments: 12 fragments, 3 per wave
 #pragma unroll
-            for (int v = 0; v < 16 / V::n; ++v) {
-                typename V::ftype f;
+        for (int j = 0; j < 3; ++j) {
+            const int f = wave + 4 * j;
+            const bool isT = f < kTriFrags;
+            const int ff = isT ? f : f - kTriFrags;
+            const int r = 16 * tri_frag_rt(ff) + col;
+            const int kb = tri_frag_kb(ff);
+            f32x8 v;
 #pragma unroll
-                for (int e = 0; e < V::n; ++e) {
-                    const int s = s0 + v * V::n + e;
-                    f[e] = (s <= r) ? sm.n[r * SM::lda + s] * sm.beta[s] : 0.f;
-                }
-                *reinterpret_cast<typename V::type*>(dst + v * V::n) = V::from_float(f);
+            for (int jj = 0; jj < 8; ++jj) {
+                const int c = 32 * kb + slot_k(grp, jj);
+                float x = 0.f;
+                if (c <= r) x = isT ? sm.n[r * SM::lda + c] * sm.beta[c] : to_f32(sm.p[r * SM::ldp + c]);
+                v[jj] = x;
             }
+            typename MT::Frag fr;
+            if constexpr (sizeof(typename MT::Frag) == 16) fr = __builtin_convertvector(v, bf16x8);
+            else fr = v;
+            *reinterpret_cast<typename MT::Frag*>(rec + (isT ? RC::tfrag : RC::pfrag) +
+                                                  (ff * kWave + lane) * RC::frag_bytes) = fr;
         }
         __syncthreads();
     }
@@ -308,36 +367,135 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 
 // ------------------------------------------------------------ chunk_scan
 
+// LDS staging of one chunk for the scan: raw K and Q tiles (row-major, 16-byte
+// segments XOR-swizzled by row so that fragment reads spread over the banks)
+// and the chunk's record, all written by direct-to-LDS loads in 1 KiB pieces.
 template <typename T, int KD>
-struct ScanSmem {
-    static constexpr int ldk = KD + Pad<T>::row;       // K, Q tiles [64][ldk]
-    static constexpr int ldt = kChunk + Pad<T>::row;   // K^T [KD][ldt]; T, P [64][ldt]
-    T k[kChunk * ldk];
-    T q[kChunk * ldk];
-    T kt[KD * ldt];
-    T tm[kChunk * ldt];
-    T p[kChunk * ldt];
-    float G[kChunk];
+struct ScanBuf {
+    static constexpr int RB = KD * (int)sizeof(T);   // bytes per row
+    static constexpr int SPR = RB / 16;              // 16-byte segments per row
+    static constexpr int RPI = 1024 / RB;            // rows per 1 KiB piece
+    static constexpr int tile_pieces = kChunk * RB / 1024;
+    static constexpr int rec_pieces = Rec<T>::bytes / 1024;
+    static constexpr int pieces = 2 * tile_pieces + rec_pieces;
+    unsigned char k[kChunk * RB];
+    unsigned char q[kChunk * RB];
+    unsigned char rec[Rec<T>::bytes];
 };
 
+template <typename T, int KD>
+__device__ __forceinline__ int swz(int row, int seg) {
+    return row * ScanBuf<T, KD>::RB + ((seg ^ (row % ScanBuf<T, KD>::SPR)) << 4);
+}
+
+// A-operand fragment of a swizzled tile: row r, contraction block kb.
+template <typename T, int KD>
+__device__ __forceinline__ typename Mma<T>::Frag tile_frag(const unsigned char* tile, int r, int kb, int grp)
+{
+    constexpr int VN = 16 / (int)sizeof(T);
+    const int e0 = 32 * kb + 4 * grp;
+    const int e1 = e0 + 16;
+    const int o0 = (e0 % VN) * (int)sizeof(T);
+    const int o1 = (e1 % VN) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 lo = *reinterpret_cast<const bf16x4*>(tile + swz<T, KD>(r, e0 / VN) + o0);
+        bf16x4 hi = *reinterpret_cast<const bf16x4*>(tile + swz<T, KD>(r, e1 / VN) + o1);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        f32x4 lo = *reinterpret_cast<const f32x4*>(tile + swz<T, KD>(r, e0 / VN) + o0);
+        f32x4 hi = *reinterpret_cast<const f32x4*>(tile + swz<T, KD>(r, e1 / VN) + o1);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// A-operand fragment of the TRANSPOSE of a swizzled row-major tile (rows of the
+// operand = columns d of the tile, contraction = tile rows t): row tile rt,
+// contraction block kb. bf16 uses the transposing LDS read (ds_read_b64_tr_b16):
+// in each 16-lane group, result slot e of lane m is element m % 4 of the 8 bytes
+// that lane 4e + m / 4 of the group addressed, so lane m addresses tile row
+// 32 kb + 4 grp + m / 4 (+16 for slots 4..7), columns 16 rt + 4 (m % 4) .. +3.
+template <typename T, int KD>
+__device__ __forceinline__ typename Mma<T>::Frag tile_frag_t(const unsigned char* tile, int rt, int kb,
+                                                             int grp, int m)
+{
+    constexpr int VN = 16 / (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        const int t0 = 32 * kb + 4 * grp + (m >> 2);
+        const int d0 = 16 * rt + 4 * (m & 3);
+        const int off = (d0 % VN) * 2;
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4 lds_s4;
+        const unsigned char* p0 = tile + swz<T, KD>(t0, d0 / VN) + off;
+        const unsigned char* p1 = tile + swz<T, KD>(t0 + 16, d0 / VN) + off;
+        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(size_t)(uintptr_t)p0);
+        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(size_t)(uintptr_t)p1);
+        typedef short s8 __attribute__((ext_vector_type(8)));
+        s8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, both);
+    } else {
+        f32x8 v;
+        const int d = 16 * rt + m;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = 32 * kb + slot_k(grp, j);
+            v[j] = *reinterpret_cast<const float*>(tile + swz<T, KD>(t, d / VN) + (d % VN) * 4);
+        }
+        return v;
+    }
+}
+
+// Issue this wave's share of the direct-to-LDS copies of chunk (tok0, L) and
+// its record into buffer `buf` (the 1 KiB pieces are dealt round-robin over
+// the NW waves). Rows >= L read row L-1: the record's factors zero them out.
 template <typename T, int KD, int NW>
+__device__ __forceinline__ void stage_chunk(ScanBuf<T, KD>* buf, const T* __restrict__ kp,
+                                            const T* __restrict__ qp, int64_t qk_stride,
+                                            int hoff, int tok0, int L,
+                                            const unsigned char* __restrict__ rec, int wave, int lane)
+{
+    typedef ScanBuf<T, KD> SB;
+    constexpr int VN = 16 / (int)sizeof(T);
+    typedef __attribute__((address_space(1))) const void* gptr;
+    typedef __attribute__((address_space(3))) void* lptr;
+    for (int piece = wave; piece < SB::pieces; piece += NW) {
+        const void* src;
+        unsigned char* dst;
+        if (piece < 2 * SB::tile_pieces) {
+            const bool isq = piece >= SB::tile_pieces;
+            const int pc = isq ? piece - SB::tile_pieces : piece;
+            const int row = pc * SB::RPI + lane / SB::SPR;
+            const int seg = (lane % SB::SPR) ^ (row % SB::SPR);   // logical segment stored here
+            const int rr = row < L ? row : L - 1;
+            const T* base = isq ? qp : kp;
+            src = base + (int64_t)(tok0 + rr) * qk_stride + hoff + seg * VN;
+            dst = (isq ? buf->q : buf->k) + pc * 1024;
+        } else {
+            const int pc = piece - 2 * SB::tile_pieces;
+            src = rec + pc * 1024 + lane * 16;
+            dst = buf->rec + pc * 1024;
+        }
+        __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(size_t)(uintptr_t)dst, 16, 0, 0);
+    }
+}
+
+template <typename T, int KD, int NW, int NBUF>
 __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const T* __restrict__ vp, int64_t v_stride,
     const float* __restrict__ S0, float* __restrict__ Sfin, T* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
-    const float* __restrict__ ws_G, const T* __restrict__ ws_T,
-    int n_seqs, int T_len, int H, int Hk, int V, int units, int groups, float scale, int l2norm)
+    const unsigned char* __restrict__ ws_rec,
+    int T_len, int H, int Hk, int V, int units, int groups)
 {
     typedef Mma<T> MT;
-    typedef ScanSmem<T, KD> SM;
-    constexpr int NT = NW * kWave;
+    typedef ScanBuf<T, KD> SB;
+    typedef Rec<T> RC;
     constexpr int RT = KD / 16;      // 16-row tiles of the state
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+    extern __shared__ __align__(1024) unsigned char smem_raw[];
+    SB* bufs = reinterpret_cast<SB*>(smem_raw);
 
     // XCD-aware block order: all column groups of one (seq, head) unit get the
-    // same blockIdx % 8, i.e. run on the same XCD and share its L2 for K, Q, T.
+    // same blockIdx % 8, i.e. run on the same XCD and share its L2.
     const int bid = blockIdx.x;
     const int rest = bid >> 3;
     const int cgrp = rest % groups;
@@ -347,13 +505,11 @@ __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
     const int h = u - seq * H;
     const int hk = h / (H / Hk);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
     const int grp = lane >> 4;
     const int col = lane & 15;
-    const int c0 = (cgrp * NW + wave) * 16;     // this wave's value columns c0..c0+15
-    const int vc = c0 + col;
+    const int vc = (cgrp * NW + wave) * 16 + col;   // this lane's value column
 
     int tok_begin, tok_end, tile0;
     if (cu) {
@@ -365,6 +521,7 @@ __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
         tok_end = tok_begin + T_len;
         tile0 = seq * ((T_len + kChunk - 1) / kChunk);
     }
+    const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
 
     // state tile rt holds h[16 rt + 4 grp + e][vc]
     f32x4 hs[RT];
@@ -375,139 +532,129 @@ __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
         for (int e = 0; e < 4; ++e)
             hs[rt][e] = S0 ? S0[sbase + (int64_t)(16 * rt + 4 * grp + e) * V + vc] : 0.f;
 
-    // P's tiles above the diagonal are read by P U as zeros and never written
-    for (int i = tid; i < kChunk * SM::ldt; i += NT) sm.p[i] = from_f32<T>(0.f);
-    __syncthreads();
-
-    const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
-    for (int c = 0; c < nchunks; ++c) {
+    const int hoff = hk * KD;
+    auto rec_of = [&](int c) { return ws_rec + ((int64_t)(tile0 + c) * H + h) * RC::bytes; };
+    // values of this lane's column for chunk c (accumulator layout), raw; rows >= L
+    // are zeroed at use. The loads are unpredicated (row clamped to L-1) so that
+    // all 16 stay in flight together.
+    auto load_v = [&](int c, T (&vr)[4][4]) {
         const int tok0 = tok_begin + c * kChunk;
         const int L = min(kChunk, tok_end - tok0);
-        const int64_t wsidx = (int64_t)(tile0 + c) * H + h;
-
-        // ---- stage K (row-major and transposed), Q, T, G
-        stage_rows<T, KD, NT>(kp + (int64_t)tok0 * qk_stride + hk * KD, qk_stride, L, l2norm,
-                              sm.k, SM::ldk, sm.kt, SM::ldt);
-        stage_rows<T, KD, NT>(qp + (int64_t)tok0 * qk_stride + hk * KD, qk_stride, L, l2norm,
-                              sm.q, SM::ldk, (T*)nullptr, 0);
-        {
-            typedef V16<T> VV;
-            constexpr int SEGS = kChunk / VV::n;
-            const T* src = ws_T + wsidx * (kChunk * kChunk);
-            for (int i = tid; i < kChunk * SEGS; i += NT) {
-                const int r = i / SEGS, sg = i - r * SEGS;
-                *reinterpret_cast<typename VV::type*>(sm.tm + r * SM::ldt + sg * VV::n) =
-                    *reinterpret_cast<const typename VV::type*>(src + r * kChunk + sg * VV::n);
-            }
-            for (int i = tid; i < kChunk; i += NT) sm.G[i] = ws_G[wsidx * kChunk + i];
-        }
-        // values of this wave's columns, in accumulator layout (rows >= L zero)
-        float vreg[4][4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * grp + e;
-                vreg[rt][e] = (r < L) ? to_f32(vp[(int64_t)(tok0 + r) * v_stride + h * V + vc]) : 0.f;
+                const int r = min(16 * rt + 4 * grp + e, L - 1);
+                vr[rt][e] = vp[(int64_t)(tok0 + r) * v_stride + h * V + vc];
             }
-        __syncthreads();
+    };
 
-        // ---- h as B operand (contraction over the key dim)
+    T vnext[4][4];
+    if (nchunks > 0) {
+        const int L0 = min(kChunk, tok_end - tok_begin);
+        stage_chunk<T, KD, NW>(&bufs[0], kp, qp, qk_stride, hoff, tok_begin, L0, rec_of(0), wave, lane);
+        load_v(0, vnext);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int tok0 = tok_begin + c * kChunk;
+        const int L = min(kChunk, tok_end - tok0);
+        SB& B = bufs[NBUF == 2 ? (c & 1) : 0];
+        float vcur[4][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vcur[rt][e] = (16 * rt + 4 * grp + e < L) ? to_f32(vnext[rt][e]) : 0.f;
+        if (NBUF == 2 && c + 1 < nchunks) {
+            const int tn = tok0 + kChunk;
+            stage_chunk<T, KD, NW>(&bufs[(c + 1) & 1], kp, qp, qk_stride, hoff, tn,
+                                   min(kChunk, tok_end - tn), rec_of(c + 1), wave, lane);
+            load_v(c + 1, vnext);
+        }
+
+        const float* fac = reinterpret_cast<const float*>(B.rec + RC::fac);
+        const typename MT::Frag* tfr = reinterpret_cast<const typename MT::Frag*>(B.rec + RC::tfrag);
+        const typename MT::Frag* pfr = reinterpret_cast<const typename MT::Frag*>(B.rec + RC::pfrag);
+
+        // h as B operand (contraction over the key dim)
         typename MT::Frag hf[KD / 32];
 #pragma unroll
         for (int kb = 0; kb < KD / 32; ++kb) hf[kb] = MT::acc_frag(hs[2 * kb], hs[2 * kb + 1]);
 
-        // ---- X = K h, Y = Q h
-        f32x4 X[4], Y[4];
+        // X = K h;  V' = V - a o X
+        f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             X[rt] = zero4();
-            Y[rt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < KD / 32; ++kb) {
-                X[rt] = MT::mma(MT::lds_frag(sm.k, SM::ldk, 16 * rt + col, 32 * kb, grp), hf[kb], X[rt]);
-                Y[rt] = MT::mma(MT::lds_frag(sm.q, SM::ldk, 16 * rt + col, 32 * kb, grp), hf[kb], Y[rt]);
-            }
-        }
-
-        // ---- P = (Q K^T) o Gamma (lower incl. diagonal), tiles dealt to waves
-        // (the tiles above the diagonal stay zero from the fill before the loop)
-        for (int t = wave; t < kLowerTiles; t += NW) {
-            f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < KD / 32; ++kb)
-                acc = MT::mma(MT::lds_frag(sm.q, SM::ldk, 16 * tri_row(t) + col, 32 * kb, grp),
-                              MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(t) + col, 32 * kb, grp), acc);
-            const int s = 16 * tri_col(t) + col;
-            const float Gs = sm.G[s];
+                X[rt] = MT::mma(tile_frag<T, KD>(B.k, 16 * rt + col, kb, grp), hf[kb], X[rt]);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(fac + 0 * kChunk + 16 * rt + 4 * grp);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * tri_row(t) + 4 * grp + e;
-                const float pv = (s <= r) ? acc[e] * __expf(sm.G[r] - Gs) : 0.f;
-                sm.p[r * SM::ldt + s] = from_f32<T>(pv);
-            }
+            for (int e = 0; e < 4; ++e) X[rt][e] = vcur[rt][e] - a[e] * X[rt][e];
         }
-
-        // ---- V' = V - gamma o X
-        float gam[4][4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                gam[rt][e] = __expf(sm.G[16 * rt + 4 * grp + e]);
-                X[rt][e] = vreg[rt][e] - gam[rt][e] * X[rt][e];
-            }
-
-        // ---- U = T V'  (T lower triangular: row tile rt needs kb <= rt/2)
+        // U = T V'
         f32x4 U[4];
         {
-            typename MT::Frag vf0 = MT::acc_frag(X[0], X[1]);
-            typename MT::Frag vf1 = MT::acc_frag(X[2], X[3]);
+            const typename MT::Frag vf0 = MT::acc_frag(X[0], X[1]);
+            const typename MT::Frag vf1 = MT::acc_frag(X[2], X[3]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                U[rt] = MT::mma(MT::lds_frag(sm.tm, SM::ldt, 16 * rt + col, 0, grp), vf0, zero4());
-                if (rt >= 2) U[rt] = MT::mma(MT::lds_frag(sm.tm, SM::ldt, 16 * rt + col, 32, grp), vf1, U[rt]);
+                U[rt] = MT::mma(tfr[tri_frag(rt, 0) * kWave + lane], vf0, zero4());
+                if (rt >= 2) U[rt] = MT::mma(tfr[tri_frag(rt, 1) * kWave + lane], vf1, U[rt]);
             }
         }
-        __syncthreads();   // P complete
-
-        // ---- O = scale (gamma o Y + P U)
+        // O = b o (Q h) + P U
         {
-            typename MT::Frag uf0 = MT::acc_frag(U[0], U[1]);
-            typename MT::Frag uf1 = MT::acc_frag(U[2], U[3]);
+            const typename MT::Frag uf0 = MT::acc_frag(U[0], U[1]);
+            const typename MT::Frag uf1 = MT::acc_frag(U[2], U[3]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = MT::mma(MT::lds_frag(sm.p, SM::ldt, 16 * rt + col, 0, grp), uf0, zero4());
-                if (rt >= 2) acc = MT::mma(MT::lds_frag(sm.p, SM::ldt, 16 * rt + col, 32, grp), uf1, acc);
+                f32x4 Y = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KD / 32; ++kb)
+                    Y = MT::mma(tile_frag<T, KD>(B.q, 16 * rt + col, kb, grp), hf[kb], Y);
+                f32x4 acc = MT::mma(pfr[tri_frag(rt, 0) * kWave + lane], uf0, zero4());
+                if (rt >= 2) acc = MT::mma(pfr[tri_frag(rt, 1) * kWave + lane], uf1, acc);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(fac + 1 * kChunk + 16 * rt + 4 * grp);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rt + 4 * grp + e;
-                    if (r < L)
-                        o[((int64_t)(tok0 + r) * H + h) * V + vc] =
-                            from_f32<T>(scale * (gam[rt][e] * Y[rt][e] + acc[e]));
+                    if (r < L) o[((int64_t)(tok0 + r) * H + h) * V + vc] = from_f32<T>(b[e] * Y[e] + acc[e]);
                 }
             }
         }
-
-        // ---- h' = gamma_L h + K^T (diag(gamma_L / gamma) U)
+        // h' = gamma_L h + K^T (c o U)
         {
-            const float GL = sm.G[kChunk - 1];
-            const float gL = __expf(GL);
+            const float gL = fac[3 * kChunk];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) U[rt][e] *= __expf(GL - sm.G[16 * rt + 4 * grp + e]);
-            typename MT::Frag df0 = MT::acc_frag(U[0], U[1]);
-            typename MT::Frag df1 = MT::acc_frag(U[2], U[3]);
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 cf = *reinterpret_cast<const f32x4*>(fac + 2 * kChunk + 16 * rt + 4 * grp);
+                U[rt] *= cf;
+            }
+            const typename MT::Frag df0 = MT::acc_frag(U[0], U[1]);
+            const typename MT::Frag df1 = MT::acc_frag(U[2], U[3]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 f32x4 acc = hs[rt] * gL;
-                acc = MT::mma(MT::lds_frag(sm.kt, SM::ldt, 16 * rt + col, 0, grp), df0, acc);
-                acc = MT::mma(MT::lds_frag(sm.kt, SM::ldt, 16 * rt + col, 32, grp), df1, acc);
+                acc = MT::mma(tile_frag_t<T, KD>(B.k, rt, 0, grp, col), df0, acc);
+                acc = MT::mma(tile_frag_t<T, KD>(B.k, rt, 1, grp, col), df1, acc);
                 hs[rt] = acc;
             }
         }
-        __syncthreads();   // LDS free for the next chunk
+
+        if (NBUF == 1 && c + 1 < nchunks) {
+            __syncthreads();   // every wave is done with the single buffer
+            const int tn = tok0 + kChunk;
+            stage_chunk<T, KD, NW>(&bufs[0], kp, qp, qk_stride, hoff, tn, min(kChunk, tok_end - tn),
+                                   rec_of(c + 1), wave, lane);
+            load_v(c + 1, vnext);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into the next buffer have landed
+        __syncthreads();
     }
 
     if (Sfin) {
@@ -530,11 +677,8 @@ static inline int64_t tiles_upper_bound(int B, int T_len, int n_seqs, bool packe
 
 size_t chunk_workspace_bytes(int B, int T_len, int H, int n_seqs, bool packed, bool use_bf16) {
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
-    const size_t esz = use_bf16 ? 2 : 4;
-    size_t off = align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
-    off += align256(sizeof(float) * (size_t)tiles * H * kChunk);
-    off += align256(esz * (size_t)tiles * H * kChunk * kChunk);
-    return off;
+    const size_t rec = use_bf16 ? Rec<bf16>::bytes : Rec<float>::bytes;
+    return align256(sizeof(int32_t) * (size_t)(n_seqs + 1)) + rec * (size_t)tiles * H;
 }
 
 template <typename K>
@@ -546,20 +690,20 @@ static hipError_t set_smem(K kernel, size_t bytes) {
 template <typename T, int KD, int NW>
 static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
                               const float* S0, float* Sf, void* o, const int32_t* cu,
-                              const int32_t* offsets, const float* wsG, const void* wsT,
-                              int n_seqs, int T_len, int H, int Hk, int V, int N, float scale,
-                              int l2norm, hipStream_t stream)
+                              const int32_t* offsets, const unsigned char* wsrec, int T_len,
+                              int H, int Hk, int V, int N, hipStream_t stream)
 {
     const int units = N * H;
     const int groups = V / (16 * NW);
     const int upad = (units + 7) / 8 * 8;
-    const size_t smem = sizeof(ScanSmem<T, KD>);
-    auto kern = chunk_scan_kernel<T, KD, NW>;
+    constexpr int NBUF = 2 * sizeof(ScanBuf<T, KD>) <= 160 * 1024 ? 2 : 1;
+    const size_t smem = NBUF * sizeof(ScanBuf<T, KD>);
+    auto kern = chunk_scan_kernel<T, KD, NW, NBUF>;
     hipError_t err = set_smem(kern, smem);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3(NW * kWave), smem, stream,
                        (const T*)q, (const T*)k, qks, (const T*)v, vs, S0, Sf, (T*)o, cu, offsets,
-                       wsG, (const T*)wsT, n_seqs, T_len, H, Hk, V, units, groups, scale, l2norm);
+                       wsrec, T_len, H, Hk, V, units, groups);
     return hipGetLastError();
 }
 
@@ -573,12 +717,8 @@ static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, cons
     const bool packed = cu != nullptr;
     const int N = packed ? n_seqs : B;
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
-    char* base = (char*)ws;
-    int32_t* offsets = (int32_t*)base;
-    size_t off = align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
-    float* wsG = (float*)(base + off);
-    off += align256(sizeof(float) * (size_t)tiles * H * kChunk);
-    T* wsT = (T*)(base + off);
+    int32_t* offsets = (int32_t*)ws;
+    unsigned char* wsrec = (unsigned char*)ws + align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
 
     if (packed) {
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, offsets);
@@ -591,22 +731,22 @@ static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, cons
         hipError_t e = set_smem(kern, smem);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles, Hk), dim3(kPrepThreads), smem, stream,
-                           (const T*)k, qks, g, beta, cu, offsets, n_seqs, T_len, H, Hk, l2norm,
-                           wsG, wsT);
+                           (const T*)q, (const T*)k, qks, g, beta, cu, offsets, n_seqs, T_len, H,
+                           Hk, scale, l2norm, wsrec);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // columns per workgroup: enough workgroups to cover the 256 CUs, more
-    // waves per workgroup (shared K/Q/T staging) when there is parallelism to spare
+    // columns per workgroup: enough workgroups to cover the 256 CUs, more waves
+    // per workgroup (shared staging) when there is parallelism to spare
     const int units = N * H;
     const int slabs = V / 16;
     int nw = 1;
     if (units * (slabs / 4) >= 512 && slabs % 4 == 0) nw = 4;
     else if (units * (slabs / 2) >= 256 && slabs % 2 == 0) nw = 2;
     switch (nw) {
-    case 4: return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsG, wsT, n_seqs, T_len, H, Hk, V, N, scale, l2norm, stream);
-    case 2: return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsG, wsT, n_seqs, T_len, H, Hk, V, N, scale, l2norm, stream);
-    default: return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsG, wsT, n_seqs, T_len, H, Hk, V, N, scale, l2norm, stream);
+    case 4: return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+    case 2: return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+    default: return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
     }
 }
 

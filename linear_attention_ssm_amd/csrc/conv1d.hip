@@ -61,14 +61,14 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     }
 
     // issue every load of the run (window + RUN rows) before using any
+    // (unpredicated loads of clamped rows, zeroed after: all stay in flight together)
     typename V::type raw[kConvW - 1 + RUN];
 #pragma unroll
     for (int i = 0; i < kConvW - 1 + RUN; ++i) {
-        int t = t0 - (kConvW - 1) + i;
-        if (t >= 0 && t < T_len)
-            raw[i] = *reinterpret_cast<const typename V::type*>(xb + (int64_t)t * xst);
-        else
-            raw[i] = typename V::type{};
+        const int t = t0 - (kConvW - 1) + i;
+        const int tc = min(max(t, 0), T_len - 1);
+        raw[i] = *reinterpret_cast<const typename V::type*>(xb + (int64_t)tc * xst);
+        if (t < 0 || t >= T_len) raw[i] = typename V::type{};
     }
 
     float win[kConvW - 1][VN];   // x[t-3], x[t-2], x[t-1]
