@@ -368,114 +368,262 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 // ------------------------------------------------------------ chunk_scan
 
 // LDS staging of one chunk for the scan: raw K and Q tiles (row-major, 16-byte
-// segments XOR-swizzled by row so that fragment reads spread over the banks)
-// and the chunk's record, all written by direct-to-LDS loads in 1 KiB pieces.
-template <typename T, int KD>
+// segments XOR-swizzled by row so that fragment reads spread over the banks),
+// the chunk's record, and each wave's 64 x 16 slab of values, all written by
+// direct-to-LDS loads in 1 KiB pieces.
+template <typename T, int KD, int NW>
 struct ScanBuf {
-    static constexpr int RB = KD * (int)sizeof(T);   // bytes per row
-    static constexpr int SPR = RB / 16;              // 16-byte segments per row
-    static constexpr int RPI = 1024 / RB;            // rows per 1 KiB piece
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int VN = 16 / ES;                 // elements per 16-byte segment
+    static constexpr int RB = KD * ES;                 // bytes per K/Q row
+    static constexpr int SPR = RB / 16;                // segments per row
+    static constexpr int RPI = 1024 / RB;              // rows per 1 KiB piece
     static constexpr int tile_pieces = kChunk * RB / 1024;
     static constexpr int rec_pieces = Rec<T>::bytes / 1024;
-    static constexpr int pieces = 2 * tile_pieces + rec_pieces;
+    static constexpr int shared_pieces = 2 * tile_pieces + rec_pieces;   // dealt over the waves
+    static constexpr int VRB = 16 * ES;                // bytes per row of a wave's value slab
+    static constexpr int LPR = VRB / 16;               // lanes per value row
+    static constexpr int v_pieces = kChunk * VRB / 1024;
+    static constexpr int RPV = kChunk / v_pieces;      // value rows per piece
     unsigned char k[kChunk * RB];
     unsigned char q[kChunk * RB];
     unsigned char rec[Rec<T>::bytes];
+    unsigned char v[NW][kChunk * VRB];
 };
 
-template <typename T, int KD>
-__device__ __forceinline__ int swz(int row, int seg) {
-    return row * ScanBuf<T, KD>::RB + ((seg ^ (row % ScanBuf<T, KD>::SPR)) << 4);
-}
-
-// A-operand fragment of a swizzled tile: row r, contraction block kb.
-template <typename T, int KD>
-__device__ __forceinline__ typename Mma<T>::Frag tile_frag(const unsigned char* tile, int r, int kb, int grp)
-{
-    constexpr int VN = 16 / (int)sizeof(T);
-    const int e0 = 32 * kb + 4 * grp;
-    const int e1 = e0 + 16;
-    const int o0 = (e0 % VN) * (int)sizeof(T);
-    const int o1 = (e1 % VN) * (int)sizeof(T);
-    if constexpr (sizeof(T) == 2) {
-        bf16x4 lo = *reinterpret_cast<const bf16x4*>(tile + swz<T, KD>(r, e0 / VN) + o0);
-        bf16x4 hi = *reinterpret_cast<const bf16x4*>(tile + swz<T, KD>(r, e1 / VN) + o1);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-        f32x4 lo = *reinterpret_cast<const f32x4*>(tile + swz<T, KD>(r, e0 / VN) + o0);
-        f32x4 hi = *reinterpret_cast<const f32x4*>(tile + swz<T, KD>(r, e1 / VN) + o1);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-}
-
-// A-operand fragment of the TRANSPOSE of a swizzled row-major tile (rows of the
-// operand = columns d of the tile, contraction = tile rows t): row tile rt,
-// contraction block kb. bf16 uses the transposing LDS read (ds_read_b64_tr_b16):
-// in each 16-lane group, result slot e of lane m is element m % 4 of the 8 bytes
-// that lane 4e + m / 4 of the group addressed, so lane m addresses tile row
-// 32 kb + 4 grp + m / 4 (+16 for slots 4..7), columns 16 rt + 4 (m % 4) .. +3.
-template <typename T, int KD>
-__device__ __forceinline__ typename Mma<T>::Frag tile_frag_t(const unsigned char* tile, int rt, int kb,
-                                                             int grp, int m)
-{
-    constexpr int VN = 16 / (int)sizeof(T);
-    if constexpr (sizeof(T) == 2) {
-        const int t0 = 32 * kb + 4 * grp + (m >> 2);
-        const int d0 = 16 * rt + 4 * (m & 3);
-        const int off = (d0 % VN) * 2;
-        typedef short s4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s4 lds_s4;
-        const unsigned char* p0 = tile + swz<T, KD>(t0, d0 / VN) + off;
-        const unsigned char* p1 = tile + swz<T, KD>(t0 + 16, d0 / VN) + off;
-        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(size_t)(uintptr_t)p0);
-        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(size_t)(uintptr_t)p1);
-        typedef short s8 __attribute__((ext_vector_type(8)));
-        s8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, both);
-    } else {
-        f32x8 v;
-        const int d = 16 * rt + m;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = 32 * kb + slot_k(grp, j);
-            v[j] = *reinterpret_cast<const float*>(tile + swz<T, KD>(t, d / VN) + (d % VN) * 4);
-        }
-        return v;
-    }
-}
-
-// Issue this wave's share of the direct-to-LDS copies of chunk (tok0, L) and
-// its record into buffer `buf` (the 1 KiB pieces are dealt round-robin over
-// the NW waves). Rows >= L read row L-1: the record's factors zero them out.
 template <typename T, int KD, int NW>
-__device__ __forceinline__ void stage_chunk(ScanBuf<T, KD>* buf, const T* __restrict__ kp,
-                                            const T* __restrict__ qp, int64_t qk_stride,
-                                            int hoff, int tok0, int L,
-                                            const unsigned char* __restrict__ rec, int wave, int lane)
+__device__ __forceinline__ int swz(int row, int seg) {
+    typedef ScanBuf<T, KD, NW> SB;
+    return row * SB::RB + ((seg ^ (row % SB::SPR)) << 4);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group,
+// result slot e of lane m is element m % 4 of the 8 bytes addressed by lane
+// 4 e + m / 4 of the group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+template <typename V>
+__device__ __forceinline__ V ld(const unsigned char* p) { return *reinterpret_cast<const V*>(p); }
+
+// Per-lane constants of the scan, computed once per workgroup.
+template <typename T, int KD, int NW>
+struct ScanLane {
+    typedef ScanBuf<T, KD, NW> SB;
+    static constexpr int KB = KD / 32;
+    static constexpr int RT = KD / 16;
+    static constexpr int PPW = (SB::shared_pieces + NW - 1) / NW;
+    static constexpr int RTP = SB::SPR > 16 ? 2 : 1;   // (16 rt + col) % SPR depends on rt only for SPR = 32
+    uint32_t soff[PPW];           // staging source offsets (bytes) of this wave's shared pieces
+    uint32_t voff[SB::v_pieces];  // staging source offsets of this wave's value pieces
+    uint32_t rf[RTP][KB][2];      // K / Q fragment reads (row tile 0 / 1), per block and half
+    uint32_t tf[RT];              // transposed K fragment reads (bf16), per state row tile
+    uint32_t vtr;                 // value slab read in accumulator layout
+    int vrow0;
+};
+
+template <typename T, int KD, int NW>
+struct ScanArgs {
+    const T* qp;
+    const T* kp;
+    int64_t qk_stride;
+    const T* vp;
+    int64_t v_stride;
+    const unsigned char* ws_rec;
+    int tok_begin, tok_end, tile0, H, h, wave, lane;
+};
+
+// Issue this wave's direct-to-LDS copies of chunk c into `nxt`. Rows past the
+// end of a partial chunk re-read row L-1 (their factors are zero).
+template <typename T, int KD, int NW>
+__device__ __forceinline__ void scan_stage(ScanBuf<T, KD, NW>* __restrict__ nxt, int c,
+                                           const ScanLane<T, KD, NW>& ln,
+                                           const ScanArgs<T, KD, NW>& a)
 {
-    typedef ScanBuf<T, KD> SB;
-    constexpr int VN = 16 / (int)sizeof(T);
+    typedef ScanBuf<T, KD, NW> SB;
     typedef __attribute__((address_space(1))) const void* gptr;
     typedef __attribute__((address_space(3))) void* lptr;
-    for (int piece = wave; piece < SB::pieces; piece += NW) {
-        const void* src;
+    constexpr int ES = SB::ES;
+    const int tok0 = a.tok_begin + c * kChunk;
+    const int L = min(kChunk, a.tok_end - tok0);
+    const int lastrow = L - 1;
+    const unsigned char* kb8 = reinterpret_cast<const unsigned char*>(a.kp + (int64_t)tok0 * a.qk_stride);
+    const unsigned char* qb8 = reinterpret_cast<const unsigned char*>(a.qp + (int64_t)tok0 * a.qk_stride);
+    const unsigned char* rb8 = a.ws_rec + ((int64_t)(a.tile0 + c) * a.H + a.h) * Rec<T>::bytes;
+    const unsigned char* vb8 = reinterpret_cast<const unsigned char*>(a.vp + (int64_t)tok0 * a.v_stride);
+#pragma unroll
+    for (int j = 0; j < ScanLane<T, KD, NW>::PPW; ++j) {
+        const int piece = a.wave + j * NW;
+        if (piece >= SB::shared_pieces) break;
+        uint32_t off = ln.soff[j];
+        const unsigned char* base;
         unsigned char* dst;
         if (piece < 2 * SB::tile_pieces) {
             const bool isq = piece >= SB::tile_pieces;
             const int pc = isq ? piece - SB::tile_pieces : piece;
-            const int row = pc * SB::RPI + lane / SB::SPR;
-            const int seg = (lane % SB::SPR) ^ (row % SB::SPR);   // logical segment stored here
-            const int rr = row < L ? row : L - 1;
-            const T* base = isq ? qp : kp;
-            src = base + (int64_t)(tok0 + rr) * qk_stride + hoff + seg * VN;
-            dst = (isq ? buf->q : buf->k) + pc * 1024;
+            if (L < kChunk) {
+                const int row = pc * SB::RPI + a.lane / SB::SPR;
+                off -= (uint32_t)(max(row - lastrow, 0) * a.qk_stride * ES);
+            }
+            base = isq ? qb8 : kb8;
+            dst = (isq ? nxt->q : nxt->k) + pc * 1024;
         } else {
-            const int pc = piece - 2 * SB::tile_pieces;
-            src = rec + pc * 1024 + lane * 16;
-            dst = buf->rec + pc * 1024;
+            base = rb8;
+            dst = nxt->rec + (piece - 2 * SB::tile_pieces) * 1024;
         }
-        __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(size_t)(uintptr_t)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr)(base + off), (lptr)dst, 16, 0, 0);
     }
+#pragma unroll
+    for (int p = 0; p < SB::v_pieces; ++p) {
+        uint32_t off = ln.voff[p];
+        if (L < kChunk) off -= (uint32_t)(max(p * SB::RPV + ln.vrow0 - lastrow, 0) * a.v_stride * ES);
+        __builtin_amdgcn_global_load_lds((gptr)(vb8 + off), (lptr)(nxt->v[a.wave] + p * 1024), 16, 0, 0);
+    }
+}
+
+// One chunk of the scan from the staged buffer `cur`: updates the state tiles
+// hs and leaves the chunk's outputs (accumulator layout) in ov.
+template <typename T, int KD, int NW>
+__device__ __forceinline__ void scan_compute(const ScanBuf<T, KD, NW>* __restrict__ cur,
+                                             const ScanLane<T, KD, NW>& ln, int wave, int grp,
+                                             int col, f32x4 (&hs)[KD / 16], f32x4 (&ov)[4])
+{
+    typedef Mma<T> MT;
+    typedef typename MT::Frag Frag;
+    typedef ScanBuf<T, KD, NW> SB;
+    typedef Rec<T> RC;
+    typedef ScanLane<T, KD, NW> LN;
+    constexpr int ES = SB::ES;
+    constexpr int VN = SB::VN;
+    constexpr int KB = LN::KB;
+    constexpr int RT = LN::RT;
+    constexpr int RTP = LN::RTP;
+    const int lane = 16 * grp + col;
+    const unsigned char* kt = cur->k;
+    const unsigned char* qt = cur->q;
+    const unsigned char* rec = cur->rec;
+    const unsigned char* vs = cur->v[wave];
+
+    // h as B operand (contraction over the key dim)
+    Frag hf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hf[kb] = MT::acc_frag(hs[2 * kb], hs[2 * kb + 1]);
+
+    auto row_frag = [&](const unsigned char* tile, int rt, int kb) -> Frag {
+        const int rtoff = (16 * rt - 16 * (rt % RTP)) * SB::RB;
+        const unsigned char* p0 = tile + ln.rf[rt % RTP][kb][0] + rtoff;
+        const unsigned char* p1 = tile + ln.rf[rt % RTP][kb][1] + rtoff;
+        if constexpr (ES == 2) {
+            const bf16x4 lo = ld<bf16x4>(p0), hi = ld<bf16x4>(p1);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            const f32x4 lo = ld<f32x4>(p0), hi = ld<f32x4>(p1);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto fac4 = [&](int which, int rt) -> f32x4 {
+        return ld<f32x4>(rec + RC::fac + (which * kChunk + 16 * rt + 4 * grp) * 4);
+    };
+    auto rec_frag = [&](int region, int f) -> Frag {
+        return ld<Frag>(rec + region + (f * kWave + lane) * RC::frag_bytes);
+    };
+
+    // values in accumulator layout
+    f32x4 vv[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        if constexpr (ES == 2) {
+            const s16x4 raw = lds_read_tr16(vs + ln.vtr + rt * 16 * SB::VRB);
+            vv[rt] = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vv[rt][e] = ld<float>(vs + (16 * rt + 4 * grp + e) * SB::VRB + col * 4);
+        }
+    }
+
+    // X = K h;  V' = V - a o X
+    f32x4 X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        X[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) X[rt] = MT::mma(row_frag(kt, rt, kb), hf[kb], X[rt]);
+        X[rt] = vv[rt] - fac4(0, rt) * X[rt];
+    }
+    // U = T V'
+    f32x4 U[4];
+    {
+        const Frag vf0 = MT::acc_frag(X[0], X[1]);
+        const Frag vf1 = MT::acc_frag(X[2], X[3]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            U[rt] = MT::mma(rec_frag(RC::tfrag, tri_frag(rt, 0)), vf0, zero4());
+            if (rt >= 2) U[rt] = MT::mma(rec_frag(RC::tfrag, tri_frag(rt, 1)), vf1, U[rt]);
+        }
+    }
+    // O = b o (Q h) + P U
+    {
+        const Frag uf0 = MT::acc_frag(U[0], U[1]);
+        const Frag uf1 = MT::acc_frag(U[2], U[3]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 Y = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Y = MT::mma(row_frag(qt, rt, kb), hf[kb], Y);
+            f32x4 acc = MT::mma(rec_frag(RC::pfrag, tri_frag(rt, 0)), uf0, zero4());
+            if (rt >= 2) acc = MT::mma(rec_frag(RC::pfrag, tri_frag(rt, 1)), uf1, acc);
+            ov[rt] = acc + fac4(1, rt) * Y;
+        }
+    }
+    // h' = gamma_L h + K^T (c o U)
+    {
+        const float gL = ld<float>(rec + RC::fac + 3 * kChunk * 4);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] *= fac4(2, rt);
+        const Frag df0 = MT::acc_frag(U[0], U[1]);
+        const Frag df1 = MT::acc_frag(U[2], U[3]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            Frag k0, k1;
+            if constexpr (ES == 2) {
+                const unsigned char* p = kt + ln.tf[rt];
+                const s16x4 a = lds_read_tr16(p);
+                const s16x4 b = lds_read_tr16(p + 16 * SB::RB);
+                const s16x4 cc = lds_read_tr16(p + 32 * SB::RB);
+                const s16x4 d = lds_read_tr16(p + 48 * SB::RB);
+                k0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+                k1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(cc, d, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                const int dd = 16 * rt + col;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = slot_k(grp, j);
+                    k0[j] = ld<float>(kt + swz<T, KD, NW>(t, dd / VN) + (dd % VN) * 4);
+                    k1[j] = ld<float>(kt + swz<T, KD, NW>(t + 32, dd / VN) + (dd % VN) * 4);
+                }
+            }
+            f32x4 acc = hs[rt] * gL;
+            acc = MT::mma(k0, df0, acc);
+            acc = MT::mma(k1, df1, acc);
+            hs[rt] = acc;
+        }
+    }
+}
+
+// Double-buffered step: the copies of chunk c + 1 into `nxt` are in flight
+// while chunk c is computed from `cur` (the two never alias).
+template <typename T, int KD, int NW>
+__device__ __forceinline__ void scan_step(const ScanBuf<T, KD, NW>* __restrict__ cur,
+                                          ScanBuf<T, KD, NW>* __restrict__ nxt, int c, bool more,
+                                          const ScanLane<T, KD, NW>& ln,
+                                          const ScanArgs<T, KD, NW>& a, int grp, int col,
+                                          f32x4 (&hs)[KD / 16], f32x4 (&ov)[4])
+{
+    if (more) scan_stage<T, KD, NW>(nxt, c + 1, ln, a);
+    scan_compute<T, KD, NW>(cur, ln, a.wave, grp, col, hs, ov);
 }
 
 template <typename T, int KD, int NW, int NBUF>
@@ -487,10 +635,11 @@ __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
     const unsigned char* __restrict__ ws_rec,
     int T_len, int H, int Hk, int V, int units, int groups)
 {
-    typedef Mma<T> MT;
-    typedef ScanBuf<T, KD> SB;
-    typedef Rec<T> RC;
-    constexpr int RT = KD / 16;      // 16-row tiles of the state
+    typedef ScanBuf<T, KD, NW> SB;
+    typedef ScanLane<T, KD, NW> LN;
+    constexpr int ES = SB::ES;
+    constexpr int VN = SB::VN;
+    constexpr int RT = KD / 16;
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     SB* bufs = reinterpret_cast<SB*>(smem_raw);
 
@@ -509,153 +658,110 @@ __global__ __launch_bounds__(NW * kWave) void chunk_scan_kernel(
     const int wave = threadIdx.x / kWave;
     const int grp = lane >> 4;
     const int col = lane & 15;
-    const int vc = (cgrp * NW + wave) * 16 + col;   // this lane's value column
+    const int c0 = (cgrp * NW + wave) * 16;     // this wave's first value column
+    const int vc = c0 + col;                    // this lane's value column
 
-    int tok_begin, tok_end, tile0;
+    ScanArgs<T, KD, NW> a;
+    a.qp = qp; a.kp = kp; a.qk_stride = qk_stride; a.vp = vp; a.v_stride = v_stride;
+    a.ws_rec = ws_rec; a.H = H; a.h = h; a.wave = wave; a.lane = lane;
     if (cu) {
-        tok_begin = cu[seq];
-        tok_end = cu[seq + 1];
-        tile0 = offsets[seq];
+        a.tok_begin = cu[seq];
+        a.tok_end = cu[seq + 1];
+        a.tile0 = offsets[seq];
     } else {
-        tok_begin = seq * T_len;
-        tok_end = tok_begin + T_len;
-        tile0 = seq * ((T_len + kChunk - 1) / kChunk);
+        a.tok_begin = seq * T_len;
+        a.tok_end = a.tok_begin + T_len;
+        a.tile0 = seq * ((T_len + kChunk - 1) / kChunk);
     }
-    const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
+    const int nchunks = (a.tok_end - a.tok_begin + kChunk - 1) / kChunk;
 
-    // state tile rt holds h[16 rt + 4 grp + e][vc]
-    f32x4 hs[RT];
-    const int64_t sbase = ((int64_t)seq * H + h) * KD * V;
+    // ---- per-lane constants ----
+    LN ln;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int j = 0; j < LN::PPW; ++j) {
+        const int piece = wave + j * NW;
+        if (piece < 2 * SB::tile_pieces) {
+            const int pc = piece % SB::tile_pieces;
+            const int row = pc * SB::RPI + lane / SB::SPR;
+            const int seg = (lane % SB::SPR) ^ (row % SB::SPR);
+            ln.soff[j] = (uint32_t)(((int64_t)row * qk_stride + hk * KD + seg * VN) * ES);
+        } else {
+            ln.soff[j] = (uint32_t)((piece - 2 * SB::tile_pieces) * 1024 + lane * 16);
+        }
+    }
+    ln.vrow0 = lane / SB::LPR;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            hs[rt][e] = S0 ? S0[sbase + (int64_t)(16 * rt + 4 * grp + e) * V + vc] : 0.f;
+    for (int p = 0; p < SB::v_pieces; ++p)
+        ln.voff[p] = (uint32_t)(((int64_t)(p * SB::RPV + ln.vrow0) * v_stride + h * V + c0 +
+                                 (lane % SB::LPR) * VN) * ES);
+#pragma unroll
+    for (int r = 0; r < LN::RTP; ++r)
+#pragma unroll
+        for (int kb = 0; kb < LN::KB; ++kb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int e0 = 32 * kb + 16 * hf + 4 * grp;
+                ln.rf[r][kb][hf] = (uint32_t)(swz<T, KD, NW>(16 * r + col, e0 / VN) + (e0 % VN) * ES);
+            }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int t0 = 4 * grp + (col >> 2);
+        const int d0 = 16 * rt + 4 * (col & 3);
+        ln.tf[rt] = (uint32_t)(swz<T, KD, NW>(t0, d0 / VN) + (d0 % VN) * 2);
+    }
+    ln.vtr = (uint32_t)((4 * grp + (col >> 2)) * SB::VRB + (col & 3) * 8);
 
-    const int hoff = hk * KD;
-    auto rec_of = [&](int c) { return ws_rec + ((int64_t)(tile0 + c) * H + h) * RC::bytes; };
-    // values of this lane's column for chunk c (accumulator layout), raw; rows >= L
-    // are zeroed at use. The loads are unpredicated (row clamped to L-1) so that
-    // all 16 stay in flight together.
-    auto load_v = [&](int c, T (&vr)[4][4]) {
-        const int tok0 = tok_begin + c * kChunk;
-        const int L = min(kChunk, tok_end - tok0);
+    const uint32_t ooff = (uint32_t)((4 * grp) * H * V + h * V + vc);   // output lane offset
+    const int64_t HV = (int64_t)H * V;
+    auto store_o = [&](int c, const f32x4 (&ov)[4]) {
+        const int tok0 = a.tok_begin + c * kChunk;
+        const int L = min(kChunk, a.tok_end - tok0);
+        T* ochunk = o + (int64_t)tok0 * HV;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = min(16 * rt + 4 * grp + e, L - 1);
-                vr[rt][e] = vp[(int64_t)(tok0 + r) * v_stride + h * V + vc];
+                T* orow = ochunk + (16 * rt + e) * HV;     // uniform row base
+                if (L == kChunk || 16 * rt + 4 * grp + e < L) orow[ooff] = from_f32<T>(ov[rt][e]);
             }
     };
 
-    T vnext[4][4];
-    if (nchunks > 0) {
-        const int L0 = min(kChunk, tok_end - tok_begin);
-        stage_chunk<T, KD, NW>(&bufs[0], kp, qp, qk_stride, hoff, tok_begin, L0, rec_of(0), wave, lane);
-        load_v(0, vnext);
+    // ---- state: tile rt holds h[16 rt + 4 grp + e][vc] ----
+    f32x4 hs[RT];
+    const int64_t sbase = ((int64_t)seq * H + h) * KD * V;
+    if (S0) {   // (one branch around all loads, so they are issued together)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hs[rt][e] = S0[sbase + (int64_t)(16 * rt + 4 * grp + e) * V + vc];
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) hs[rt] = zero4();
     }
+
+    if (nchunks > 0) scan_stage<T, KD, NW>(&bufs[0], 0, ln, a);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    f32x4 ov[4];
     for (int c = 0; c < nchunks; ++c) {
-        const int tok0 = tok_begin + c * kChunk;
-        const int L = min(kChunk, tok_end - tok0);
-        SB& B = bufs[NBUF == 2 ? (c & 1) : 0];
-        float vcur[4][4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vcur[rt][e] = (16 * rt + 4 * grp + e < L) ? to_f32(vnext[rt][e]) : 0.f;
-        if (NBUF == 2 && c + 1 < nchunks) {
-            const int tn = tok0 + kChunk;
-            stage_chunk<T, KD, NW>(&bufs[(c + 1) & 1], kp, qp, qk_stride, hoff, tn,
-                                   min(kChunk, tok_end - tn), rec_of(c + 1), wave, lane);
-            load_v(c + 1, vnext);
-        }
-
-        const float* fac = reinterpret_cast<const float*>(B.rec + RC::fac);
-        const typename MT::Frag* tfr = reinterpret_cast<const typename MT::Frag*>(B.rec + RC::tfrag);
-        const typename MT::Frag* pfr = reinterpret_cast<const typename MT::Frag*>(B.rec + RC::pfrag);
-
-        // h as B operand (contraction over the key dim)
-        typename MT::Frag hf[KD / 32];
-#pragma unroll
-        for (int kb = 0; kb < KD / 32; ++kb) hf[kb] = MT::acc_frag(hs[2 * kb], hs[2 * kb + 1]);
-
-        // X = K h;  V' = V - a o X
-        f32x4 X[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            X[rt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < KD / 32; ++kb)
-                X[rt] = MT::mma(tile_frag<T, KD>(B.k, 16 * rt + col, kb, grp), hf[kb], X[rt]);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(fac + 0 * kChunk + 16 * rt + 4 * grp);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) X[rt][e] = vcur[rt][e] - a[e] * X[rt][e];
-        }
-        // U = T V'
-        f32x4 U[4];
-        {
-            const typename MT::Frag vf0 = MT::acc_frag(X[0], X[1]);
-            const typename MT::Frag vf1 = MT::acc_frag(X[2], X[3]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                U[rt] = MT::mma(tfr[tri_frag(rt, 0) * kWave + lane], vf0, zero4());
-                if (rt >= 2) U[rt] = MT::mma(tfr[tri_frag(rt, 1) * kWave + lane], vf1, U[rt]);
+        // the previous chunk's outputs go out first: their stores then have the
+        // whole chunk to complete before the wait below
+        if (c > 0) store_o(c - 1, ov);
+        if constexpr (NBUF == 2) {
+            scan_step<T, KD, NW>(&bufs[c & 1], &bufs[(c & 1) ^ 1], c, c + 1 < nchunks, ln, a, grp,
+                                 col, hs, ov);
+        } else {
+            scan_compute<T, KD, NW>(&bufs[0], ln, wave, grp, col, hs, ov);
+            if (c + 1 < nchunks) {
+                __syncthreads();   // every wave is done with the single buffer
+                scan_stage<T, KD, NW>(&bufs[0], c + 1, ln, a);
             }
         }
-        // O = b o (Q h) + P U
-        {
-            const typename MT::Frag uf0 = MT::acc_frag(U[0], U[1]);
-            const typename MT::Frag uf1 = MT::acc_frag(U[2], U[3]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 Y = zero4();
-#pragma unroll
-                for (int kb = 0; kb < KD / 32; ++kb)
-                    Y = MT::mma(tile_frag<T, KD>(B.q, 16 * rt + col, kb, grp), hf[kb], Y);
-                f32x4 acc = MT::mma(pfr[tri_frag(rt, 0) * kWave + lane], uf0, zero4());
-                if (rt >= 2) acc = MT::mma(pfr[tri_frag(rt, 1) * kWave + lane], uf1, acc);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(fac + 1 * kChunk + 16 * rt + 4 * grp);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rt + 4 * grp + e;
-                    if (r < L) o[((int64_t)(tok0 + r) * H + h) * V + vc] = from_f32<T>(b[e] * Y[e] + acc[e]);
-                }
-            }
-        }
-        // h' = gamma_L h + K^T (c o U)
-        {
-            const float gL = fac[3 * kChunk];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const f32x4 cf = *reinterpret_cast<const f32x4*>(fac + 2 * kChunk + 16 * rt + 4 * grp);
-                U[rt] *= cf;
-            }
-            const typename MT::Frag df0 = MT::acc_frag(U[0], U[1]);
-            const typename MT::Frag df1 = MT::acc_frag(U[2], U[3]);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                f32x4 acc = hs[rt] * gL;
-                acc = MT::mma(tile_frag_t<T, KD>(B.k, rt, 0, grp, col), df0, acc);
-                acc = MT::mma(tile_frag_t<T, KD>(B.k, rt, 1, grp, col), df1, acc);
-                hs[rt] = acc;
-            }
-        }
-
-        if (NBUF == 1 && c + 1 < nchunks) {
-            __syncthreads();   // every wave is done with the single buffer
-            const int tn = tok0 + kChunk;
-            stage_chunk<T, KD, NW>(&bufs[0], kp, qp, qk_stride, hoff, tn, min(kChunk, tok_end - tn),
-                                   rec_of(c + 1), wave, lane);
-            load_v(c + 1, vnext);
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into the next buffer have landed
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next chunk have landed
         __syncthreads();
     }
+    if (nchunks > 0) store_o(nchunks - 1, ov);
 
     if (Sfin) {
 #pragma unroll
@@ -696,8 +802,8 @@ static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const v
     const int units = N * H;
     const int groups = V / (16 * NW);
     const int upad = (units + 7) / 8 * 8;
-    constexpr int NBUF = 2 * sizeof(ScanBuf<T, KD>) <= 160 * 1024 ? 2 : 1;
-    const size_t smem = NBUF * sizeof(ScanBuf<T, KD>);
+    constexpr int NBUF = 2 * sizeof(ScanBuf<T, KD, NW>) <= 160 * 1024 ? 2 : 1;
+    const size_t smem = NBUF * sizeof(ScanBuf<T, KD, NW>);
     auto kern = chunk_scan_kernel<T, KD, NW, NBUF>;
     hipError_t err = set_smem(kern, smem);
     if (err != hipSuccess) return err;
@@ -743,11 +849,15 @@ static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, cons
     int nw = 1;
     if (units * (slabs / 4) >= 512 && slabs % 4 == 0) nw = 4;
     else if (units * (slabs / 2) >= 256 && slabs % 2 == 0) nw = 2;
-    switch (nw) {
-    case 4: return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
-    case 2: return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
-    default: return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+    if (nw == 4)
+        return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+    // the fp32 operand path (small parity workloads) runs with 1 or 4 waves per
+    // workgroup only: its 2-wave instance does not get through the gfx950 backend
+    if constexpr (sizeof(T) == 2) {
+        if (nw == 2)
+            return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
     }
+    return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
 }
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
