@@ -3,14 +3,18 @@
 A step is one pass of the prefill hot path over one batch of the bf16 prefill
 workload (B=4, H=16, T=4096, K=V=128): causal conv1d + SiLU over the q|k|v
 channels (C = 6144), gate preparation, and the chunked forward (per-chunk WY
-solve + sequential state scan + outputs + final state). Inputs are resident in
-HBM before timing starts. `value` is tokens/s of the whole step (16,384 tokens
-per step); the chunked forward alone and the one-token Gated DeltaProduct
-decode (n=256 requests, M=2, H=32, G=16, P=N=128, 1000 steps, state in place)
-are reported beside it.
+solve, then the sequential state scan with the outputs and the final state).
+Inputs are resident in HBM before timing starts. `value` is tokens/s of the
+whole step (16,384 tokens per step). The chunked forward alone and the
+one-token Gated DeltaProduct decode (n=256 requests, M=2, H=32, G=16,
+P=N=128, 1000 steps, fp32 state updated in place) are reported beside it.
 
-Per-op durations come from HIP events recorded on the stream the kernels are
-launched on (torch's current stream, which the binding passes to the library).
+Per-kernel durations come from HIP events recorded between the launches on
+the stream the kernels run on (torch's current stream, which the binding
+passes to the library). `roofline` describes the kernel that takes the most
+time per step; `traffic` comes from committed rocprofv3 counter summaries
+(profiles/traffic.json) and is null when absent or when the kernel's source
+has changed since they were taken.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
 """
@@ -29,12 +33,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {
-    "conv1d_causal_kernel": "linear_attention_ssm_amd/csrc/conv1d.hip",
-    "chunk_scan_kernel": "linear_attention_ssm_amd/csrc/chunk.hip",
-    "chunk_prep_kernel": "linear_attention_ssm_amd/csrc/chunk.hip",
-    "gdp_decode_kernel": "linear_attention_ssm_amd/csrc/decode.hip",
+CSRC = "linear_attention_ssm_amd/csrc/"
+KERNELS = {   # bench op -> (kernel symbol stem, source file)
+    "conv1d": ("conv1d_causal_kernel", CSRC + "conv1d.hip"),
+    "gate_prepare": ("gate_prepare_kernel", CSRC + "gate.hip"),
+    "chunk_prepare": ("chunk_prep_kernel", CSRC + "chunk.hip"),
+    "chunk_scan": ("chunk_scan_kernel", CSRC + "chunk.hip"),
+    "decode": ("gdp_decode_kernel", CSRC + "decode.hip"),
 }
+REC_BYTES_BF16 = 2 * 6 * 64 * 16 + 4 * 64 * 4   # per (chunk, value head) workspace record
 
 
 def parse():
@@ -53,19 +60,33 @@ def parse():
     return p.parse_args()
 
 
-# algorithmic traffic / work of the prefill workload (one step)
 def prefill_accounting(B, T, H, Hk, K, V):
+    """Algorithmic HBM bytes (and MFMA flops) per launch of each prefill kernel:
+    every input read once, every output written once."""
     C = 2 * Hk * K + H * V
     tok = B * T
-    conv_bytes = 2 * tok * C * 2 + C * 4 * 2                    # x in + y out (bf16) + w
-    gate_bytes = 2 * tok * H * 2 + 2 * tok * H * 4              # a, b in (bf16); g, beta out (fp32)
-    chunk_bytes = (2 * tok * Hk * K * 2 + tok * H * V * 2       # q, k, v in (bf16)
-                   + 2 * tok * H * 4                            # g, beta in (fp32)
-                   + tok * H * V * 2                            # o out (bf16)
-                   + B * H * K * V * 4)                         # final state out (fp32)
+    chunks = B * ((T + 63) // 64)
+    qk = 2 * tok * Hk * K * 2
+    v = tok * H * V * 2
+    o = tok * H * V * 2
+    gb = 2 * tok * H * 4
+    state = B * H * K * V * 4
+    rec = chunks * H * REC_BYTES_BF16
     d, Cc = K, 64
-    flops_tri = tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3)
-    return dict(conv=conv_bytes, gate=gate_bytes, chunk=chunk_bytes, chunk_flops=flops_tri)
+    return {
+        "conv1d": {"bytes": 2 * tok * C * 2 + C * 4 * 2},
+        "gate_prepare": {"bytes": 2 * tok * H * 2 + gb},
+        "chunk_prepare": {"bytes": qk + gb + rec,
+                          # lower-triangular K K^T and Q K^T tiles plus the 64x64 solve
+                          "flops": chunks * (Hk * 2 * 10 * 16 * 16 * K * 2 + H * 64 ** 3 / 3)},
+        "chunk_scan": {"bytes": qk + v + rec + o + state,
+                       # K h, Q h, K^T U (dense) + T V', P U (lower-triangular), per chunk and head
+                       "flops": chunks * H * (3 * 64 * K * V * 2 + 2 * 0.5 * 64 * 64 * V * 2)},
+        # the whole chunked forward, single-pass: q, k, v, g, beta in; o, final state out;
+        # flops per token and head 6 d^2 + 5 C d + 2/3 C^2 (triangular count)
+        "chunk_fwd": {"bytes": qk + v + gb + o + state,
+                      "flops": tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3)},
+    }
 
 
 def decode_accounting(n, M, H, G, P, N):
@@ -79,16 +100,16 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(kernel):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
-    when absent or taken on a different version of the kernel source."""
+def load_traffic(op):
+    """HBM bytes per launch (FETCH + WRITE, scaled by the copy-kernel factor)
+    from profiles/traffic.json, or None when absent or stale."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(kernel)
-    if not ent or ent.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+    ent = data.get("kernels", {}).get(KERNELS[op][0])
+    if not ent or ent.get("source_sha") != source_hash(KERNELS[op][1]):
         return None
     return ent.get("bytes_per_launch")
 
@@ -123,10 +144,96 @@ def cpu_baseline(w, batch):
                       f"conv1d + gates + timestep recurrence), {dt:.2f} s on {used} threads"}
 
 
+def run_prefill(args, gdn, wl, torch, dev, stream):
+    w = wl.WORKLOADS["prefill"]
+    d = wl.prefill_inputs(w)
+    x, cw = d["x"].to(dev), d["w"].to(dev)
+    a, b = d["a"].to(dev), d["b"].to(dev)
+    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
+    y = torch.empty_like(x)
+    g = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    o = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((w.B, w.H, w.K, w.V), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(w.B, w.T, w.H, w.Hk, w.K, w.V, 0,
+                                                      torch.bfloat16), dtype=torch.uint8, device=dev)
+    q, k, v = gdn.split_qkv(y, w.Hk, w.K, w.H, w.V)
+    ops = ["conv1d", "gate_prepare", "chunk_prepare", "chunk_scan"]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        gdn.gdn_conv1d_causal(x, cw, y=y, silu=True)
+        if evs:
+            evs[1].record(stream)
+        gdn.gdn_gate_prepare(a, b, A_log, dt_bias, g=g, beta=beta)
+        if evs:
+            evs[2].record(stream)
+        gdn.gdn_chunk_prepare(q, k, g, beta, ws)
+        if evs:
+            evs[3].record(stream)
+        gdn.gdn_chunk_scan(q, k, v, o, ws, final_state=fs)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+             for j, op in enumerate(ops)}
+    return w, op_ms, wall * 1e3 / args.steps
+
+
+def run_decode(args, gdn, wl, torch, dev, stream):
+    wd = wl.WORKLOADS["decode"]
+    st = wl.decode_state_inputs(wd)
+    state = st["state"].to(dev)
+    A_log, dt_bias = st["A_log"].to(dev), st["dt_bias"].to(dev)
+    xl, bl = wl.decode_row_sizes(wd.M, wd.H, wd.G, wd.V, wd.K)
+    steps = args.decode_steps
+    # per-step inputs pre-staged in HBM (same distributions as the parity tests,
+    # drawn on the device with a seeded generator)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wd.seed)
+    xs = torch.randn((steps, wd.n, xl), generator=gen, device=dev).to(torch.bfloat16)
+    bas = torch.randn((steps, wd.n, bl), generator=gen, device=dev).to(torch.bfloat16)
+    o = torch.empty((wd.n, wd.H, wd.V), dtype=torch.bfloat16, device=dev)
+    for i in range(min(10, steps)):
+        gdn.gdn_recurrent_decode(xs[i], bas[i], A_log, dt_bias, state, wd.M, wd.H, wd.G, wd.V,
+                                 wd.K, o=o)
+    state.copy_(st["state"].to(dev))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        gdn.gdn_recurrent_decode(xs[i], bas[i], A_log, dt_bias, state, wd.M, wd.H, wd.G, wd.V,
+                                 wd.K, o=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_s = ms / steps / 1e3
+    nbytes = decode_accounting(wd.n, wd.M, wd.H, wd.G, wd.V, wd.K)
+    return {"req_per_s": wd.n * steps / (ms / 1e3), "us_per_step": per_s * 1e6,
+            "kernel": KERNELS["decode"][0],
+            "roofline": {"bound": "hbm", "achieved": nbytes / per_s / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": nbytes / per_s / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("decode")},
+            "algorithmic_bytes_per_step": nbytes,
+            "workload": f"decode bf16 n={wd.n} M={wd.M} H={wd.H} G={wd.G} P=N={wd.K}, "
+                        f"fp32 state in place, {steps} steps"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; runs on several GPUs "
                                    "are not part of this build", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -137,145 +244,51 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    result = {}
 
     w = wl.WORKLOADS["prefill"]
-    acc = prefill_accounting(w.B, w.T, w.H, w.Hk, w.K, w.V)
-    tokens = w.B * w.T
+    out = {"metric": "GDN prefill tokens/s (conv1d + gates + chunk_fwd; H=16, d=128, T=4096)",
+           "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"prefill bf16 B={w.B} H={w.H} Hk={w.Hk} T={w.T} K=V={w.K} "
+                                  "chunk=64, conv1d W=4 + SiLU over C=6144, fp32 state",
+                      "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"}}
 
     if args.only != "decode":
-        d = wl.prefill_inputs(w)
-        x, cw = d["x"].to(dev), d["w"].to(dev)
-        a, b = d["a"].to(dev), d["b"].to(dev)
-        A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
-        bufs = {
-            "y": torch.empty_like(x),
-            "g": torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev),
-            "beta": torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev),
-            "o": torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev),
-            "final_state": torch.empty((w.B, w.H, w.K, w.V), dtype=torch.float32, device=dev),
-            "workspace": torch.empty(gdn.gdn_chunk_fwd_workspace_size(
-                w.B, w.T, w.H, w.Hk, w.K, w.V, 0, torch.bfloat16), dtype=torch.uint8, device=dev),
-        }
-
-        def step(evs=None):
-            if evs:
-                evs[0].record(stream)
-            y = gdn.gdn_conv1d_causal(x, cw, y=bufs["y"], silu=True)
-            if evs:
-                evs[1].record(stream)
-            g, beta = gdn.gdn_gate_prepare(a, b, A_log, dt_bias, g=bufs["g"], beta=bufs["beta"])
-            if evs:
-                evs[2].record(stream)
-            q, k, v = gdn.split_qkv(y, w.Hk, w.K, w.H, w.V)
-            gdn.gdn_chunk_fwd(q, k, v, g, beta, workspace=bufs["workspace"], o=bufs["o"],
-                              final_state=bufs["final_state"])
-            if evs:
-                evs[3].record(stream)
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        # per-op events inside the timed region
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        conv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-        gate_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        chunk_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        step_ms = wall * 1e3 / args.steps
-        result["prefill"] = dict(step_ms=step_ms, conv_ms=conv_ms, gate_ms=gate_ms,
-                                 chunk_ms=chunk_ms, tokens=tokens)
-
+        w, op_ms, step_ms = run_prefill(args, gdn, wl, torch, dev, stream)
+        acc = prefill_accounting(w.B, w.T, w.H, w.Hk, w.K, w.V)
+        tokens = w.B * w.T
+        out["value"] = tokens / (step_ms / 1e3)
+        out["ms_per_step"] = step_ms
+        out["ops_us"] = {op: ms * 1e3 for op, ms in op_ms.items()}
+        dom = max(op_ms, key=op_ms.get)
+        sec = op_ms[dom] / 1e3
+        ach = acc[dom]["bytes"] / sec / 1e9
+        out["roofline"] = {"kernel": KERNELS[dom][0], "bound": "hbm", "achieved": ach,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                           "traffic": load_traffic(dom),
+                           "algorithmic_bytes": acc[dom]["bytes"]}
+        if "flops" in acc[dom]:
+            out["roofline"]["mfma_frac"] = acc[dom]["flops"] / sec / (BF16_PEAK_TFLOPS * 1e12)
+        chunk_s = (op_ms["chunk_prepare"] + op_ms["chunk_scan"]) / 1e3
+        out["chunk_fwd"] = {
+            "tokens_per_s": tokens / chunk_s, "us": chunk_s * 1e6,
+            "mfma_frac": acc["chunk_fwd"]["flops"] / chunk_s / (BF16_PEAK_TFLOPS * 1e12),
+            "hbm_frac": acc["chunk_fwd"]["bytes"] / chunk_s / (HBM_PEAK_GBS * 1e9),
+            "algorithmic_flops": acc["chunk_fwd"]["flops"],
+            "algorithmic_bytes": acc["chunk_fwd"]["bytes"]}
+        out["kernels"] = {op: {"us": op_ms[op] * 1e3,
+                               "achieved_GBs": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9,
+                               "hbm_frac": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9 / HBM_PEAK_GBS}
+                          for op in op_ms}
     if args.only != "prefill" and not args.no_decode:
-        wd = wl.WORKLOADS["decode"]
-        st = wl.decode_state_inputs(wd)
-        state = st["state"].to(dev)
-        A_log_d, dt_bias_d = st["A_log"].to(dev), st["dt_bias"].to(dev)
-        xl, bl = wl.decode_row_sizes(wd.M, wd.H, wd.G, wd.V, wd.K)
-        steps = args.decode_steps
-        # per-step inputs pre-staged in HBM (same distributions as the parity tests,
-        # drawn on the device with a seeded generator)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(wd.seed)
-        xs = torch.randn((steps, wd.n, xl), generator=gen, device=dev).to(torch.bfloat16)
-        bas = torch.randn((steps, wd.n, bl), generator=gen, device=dev).to(torch.bfloat16)
-        o = torch.empty((wd.n, wd.H, wd.V), dtype=torch.bfloat16, device=dev)
-        for i in range(min(10, steps)):
-            gdn.gdn_recurrent_decode(xs[i], bas[i], A_log_d, dt_bias_d, state, wd.M, wd.H, wd.G,
-                                     wd.V, wd.K, o=o)
-        state.copy_(st["state"].to(dev))
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            gdn.gdn_recurrent_decode(xs[i], bas[i], A_log_d, dt_bias_d, state, wd.M, wd.H, wd.G,
-                                     wd.V, wd.K, o=o)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dec_ms = e0.elapsed_time(e1)
-        per = dec_ms / steps
-        dbytes = decode_accounting(wd.n, wd.M, wd.H, wd.G, wd.V, wd.K)
-        result["decode"] = dict(ms_total=dec_ms, us_per_step=per * 1e3,
-                                req_per_s=wd.n * steps / (dec_ms / 1e3),
-                                achieved_GBs=dbytes / (per / 1e3) / 1e9,
-                                bytes_per_step=dbytes, steps=steps, n=wd.n)
-        del xs, bas
-
+        out["decode"] = run_decode(args, gdn, wl, torch, dev, stream)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-
-    out = {"metric": "GDN prefill tokens/s (conv1d + gates + chunk_fwd; H=16, d=128, T=4096)",
-           "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "prefill bf16 B=4 H=16 Hk=16 T=4096 K=V=128 chunk=64, "
-                                  "conv1d W=4 + SiLU over C=6144, fp32 state",
-                      "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"}}
-    if "prefill" in result:
-        p = result["prefill"]
-        out["value"] = tokens / (p["step_ms"] / 1e3)
-        out["ms_per_step"] = p["step_ms"]
-        chunk_s = p["chunk_ms"] / 1e3
-        conv_s = p["conv_ms"] / 1e3
-        out["ops_ms"] = {"conv1d": p["conv_ms"], "gate_prepare": p["gate_ms"],
-                         "chunk_fwd": p["chunk_ms"]}
-        out["chunk_fwd_tokens_per_s"] = tokens / chunk_s
-        out["chunk_fwd_roofline"] = {
-            "mfma_frac": acc["chunk_flops"] / chunk_s / (BF16_PEAK_TFLOPS * 1e12),
-            "hbm_frac": acc["chunk"] / chunk_s / (HBM_PEAK_GBS * 1e9),
-            "algorithmic_flops": acc["chunk_flops"], "algorithmic_bytes": acc["chunk"]}
-        # the dominant kernel of the step: report its roofline
-        ops = {"conv1d": (conv_s, acc["conv"], "conv1d_causal_kernel")}
-        name, (sec, nbytes, kname) = max(ops.items(), key=lambda kv: kv[1][0])
-        if p["chunk_ms"] > p["conv_ms"]:
-            out["roofline"] = {"kernel": "gdn_chunk_fwd (chunk_prep + chunk_scan)",
-                               "bound": "hbm", "achieved": acc["chunk"] / chunk_s / 1e9,
-                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": acc["chunk"] / chunk_s / 1e9 / HBM_PEAK_GBS,
-                               "traffic": None}
-        else:
-            tr = load_traffic(kname)
-            out["roofline"] = {"kernel": kname, "bound": "hbm",
-                               "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
-                               "traffic": tr}
-    if "decode" in result:
-        dd = result["decode"]
-        out["decode"] = {"req_per_s": dd["req_per_s"], "us_per_step": dd["us_per_step"],
-                         "achieved_GBs": dd["achieved_GBs"],
-                         "hbm_frac": dd["achieved_GBs"] / HBM_PEAK_GBS,
-                         "workload": "decode bf16 n=256 M=2 H=32 G=16 P=N=128, fp32 state "
-                                     f"in place, {dd['steps']} steps",
-                         "traffic": load_traffic("gdp_decode_kernel")}
     if not args.no_cpu and args.only != "decode":
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_batch)
     print(json.dumps(out), flush=True)

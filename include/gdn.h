@@ -128,6 +128,8 @@ int gdn_gate_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t
  *            GDN_FP32 (fp32 MFMA operands throughout).
  *   workspace  device scratch of at least gdn_chunk_fwd_workspace_size(...)
  *            bytes, 256-byte aligned; contents on entry do not matter.
+ *   Token strides times 64 rows must stay below 2^31 bytes (the scan
+ *   addresses a chunk with 32-bit offsets), else GDN_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int Hk, int K, int V,
                                     int n_seqs, int dtype);
@@ -141,6 +143,37 @@ int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t,
                   int B, int T, int H, int Hk, int K, int V,
                   float scale, int qk_l2norm, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_chunk_prepare / gdn_chunk_scan -- the two phases of gdn_chunk_fwd,
+ * exposed separately (same arguments, same workspace) so that each can be
+ * launched and timed on its own; gdn_chunk_fwd(...) is exactly
+ * gdn_chunk_prepare(...) followed by gdn_chunk_scan(...) on one stream.
+ *   gdn_chunk_prepare  [ZZ] item 4 (WY recompute): for every 64-token chunk
+ *            and value head, in parallel, the cumulative log-decay, the
+ *            inverse (I + A)^-1 diag(beta) of the chunk's unit-lower-triangular
+ *            system, the gated intra-chunk attention (q k^T o decay) and the
+ *            per-row scale factors, written to `workspace`.
+ *   gdn_chunk_scan     [ZZ] items 2-3: the sequential inter-chunk state scan
+ *            and the per-chunk outputs, reading the records gdn_chunk_prepare
+ *            left in `workspace` (which must be the result of a prepare call
+ *            with the same q, k, g, beta, cu_seqlens, sizes, scale, qk_l2norm
+ *            and dtype; the workspace is otherwise unchecked).
+ * Error codes as for gdn_chunk_fwd (the prepare call checks V as if 64).
+ * ---------------------------------------------------------------------- */
+int gdn_chunk_prepare(const void* q, const void* k, int64_t qk_stride_t,
+                      const float* g, const float* beta,
+                      const int32_t* cu_seqlens, int n_seqs,
+                      int B, int T, int H, int Hk, int K,
+                      float scale, int qk_l2norm, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t,
+                   const void* v, int64_t v_stride_t,
+                   const float* initial_state, float* final_state, void* o,
+                   const int32_t* cu_seqlens, int n_seqs,
+                   int B, int T, int H, int Hk, int K, int V, int dtype,
+                   const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * gdn_recurrent_decode -- [GDP] "gdp_decode_prepare" fused with the

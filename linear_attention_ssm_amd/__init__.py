@@ -19,8 +19,8 @@ import torch
 
 __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
-    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_recurrent_decode", "prefill_chain",
-    "split_qkv",
+    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
+    "gdn_recurrent_decode", "prefill_chain", "split_qkv",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +49,12 @@ _lib.gdn_chunk_fwd_workspace_size.restype = _sz
 _lib.gdn_chunk_fwd.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
                                + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_chunk_fwd.restype = _i32
+_lib.gdn_chunk_prepare.argtypes = ([_vp, _vp, _i64, _vp, _vp, _vp, _i32] + [_i32] * 5
+                                   + [_f32, _i32, _i32, _vp, _sz, _vp])
+_lib.gdn_chunk_prepare.restype = _i32
+_lib.gdn_chunk_scan.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32] + [_i32] * 7
+                                + [_vp, _sz, _vp])
+_lib.gdn_chunk_scan.restype = _i32
 _lib.gdn_recurrent_decode.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
                                       + [_i32] * 6 + [_f32, _i32, _i32, _vp])
 _lib.gdn_recurrent_decode.restype = _i32
@@ -217,6 +223,39 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                             _stream(q.device))
     _check(rc, "gdn_chunk_fwd")
     return o, final_state
+
+
+def gdn_chunk_prepare(q, k, g, beta, workspace, cu_seqlens=None, scale=1.0, qk_l2norm=True,
+                      H: int | None = None):
+    """Phase 1 of gdn_chunk_fwd (per-chunk WY solve) into `workspace`."""
+    B, T, Hk, K = q.shape
+    H = g.shape[2] if H is None else H
+    st_qk = _token_rows(q, "q", Hk, K)
+    if _token_rows(k, "k", Hk, K) != st_qk:
+        raise ValueError("q and k must share strides")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rc = _lib.gdn_chunk_prepare(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(g, "g"), _dev(beta, "beta"),
+                                _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K,
+                                float(scale), int(bool(qk_l2norm)), _code(q.dtype),
+                                _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(rc, "gdn_chunk_prepare")
+
+
+def gdn_chunk_scan(q, k, v, o, workspace, initial_state=None, final_state=None, cu_seqlens=None):
+    """Phase 2 of gdn_chunk_fwd (state scan + outputs) from a prepared workspace."""
+    B, T, Hk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    st_qk = _token_rows(q, "q", Hk, K)
+    st_v = _token_rows(v, "v", H, V)
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    rc = _lib.gdn_chunk_scan(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(v, "v"), st_v,
+                             _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
+                             _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
+                             _code(q.dtype), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(rc, "gdn_chunk_scan")
+    return o
 
 
 # -------------------------------------------------------------------- decode

@@ -813,21 +813,29 @@ static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const v
     return hipGetLastError();
 }
 
+struct ChunkWs {
+    int32_t* offsets;
+    unsigned char* rec;
+};
+
+static inline ChunkWs carve(void* ws, int n_seqs) {
+    ChunkWs w;
+    w.offsets = (int32_t*)ws;
+    w.rec = (unsigned char*)ws + align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
+    return w;
+}
+
 template <typename T, int KD>
-static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, const void* v,
-                                 int64_t vs, const float* g, const float* beta, const float* S0,
-                                 float* Sf, void* o, const int32_t* cu, int n_seqs, int B,
-                                 int T_len, int H, int Hk, int V, float scale, int l2norm,
-                                 void* ws, hipStream_t stream)
+static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, const float* g,
+                                   const float* beta, const int32_t* cu, int n_seqs, int B,
+                                   int T_len, int H, int Hk, float scale, int l2norm, void* ws,
+                                   hipStream_t stream)
 {
     const bool packed = cu != nullptr;
-    const int N = packed ? n_seqs : B;
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
-    int32_t* offsets = (int32_t*)ws;
-    unsigned char* wsrec = (unsigned char*)ws + align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
-
+    const ChunkWs w = carve(ws, n_seqs);
     if (packed) {
-        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, offsets);
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, w.offsets);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -837,11 +845,22 @@ static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, cons
         hipError_t e = set_smem(kern, smem);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles, Hk), dim3(kPrepThreads), smem, stream,
-                           (const T*)q, (const T*)k, qks, g, beta, cu, offsets, n_seqs, T_len, H,
-                           Hk, scale, l2norm, wsrec);
+                           (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
+                           Hk, scale, l2norm, w.rec);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+template <typename T, int KD>
+static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const void* v,
+                                int64_t vs, const float* S0, float* Sf, void* o, const int32_t* cu,
+                                int n_seqs, int B, int T_len, int H, int Hk, int V, const void* ws,
+                                hipStream_t stream)
+{
+    const int N = cu ? n_seqs : B;
+    const ChunkWs w = carve(const_cast<void*>(ws), n_seqs);
     // columns per workgroup: enough workgroups to cover the 256 CUs, more waves
     // per workgroup (shared staging) when there is parallelism to spare
     const int units = N * H;
@@ -850,30 +869,38 @@ static hipError_t launch_chunk_t(const void* q, const void* k, int64_t qks, cons
     if (units * (slabs / 4) >= 512 && slabs % 4 == 0) nw = 4;
     else if (units * (slabs / 2) >= 256 && slabs % 2 == 0) nw = 2;
     if (nw == 4)
-        return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+        return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
     // the fp32 operand path (small parity workloads) runs with 1 or 4 waves per
     // workgroup only: its 2-wave instance does not get through the gfx950 backend
     if constexpr (sizeof(T) == 2) {
         if (nw == 2)
-            return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+            return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
     }
-    return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, offsets, wsrec, T_len, H, Hk, V, N, stream);
+    return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
 }
 
-hipError_t launch_chunk_fwd(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
-                            const float* g, const float* beta, const float* S0, float* Sf,
-                            void* o, const int32_t* cu, int n_seqs, int B, int T_len, int H,
-                            int Hk, int K, int V, float scale, int l2norm, bool use_bf16, void* ws,
-                            hipStream_t stream)
+hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const float* g,
+                                const float* beta, const int32_t* cu, int n_seqs, int B, int T_len,
+                                int H, int Hk, int K, float scale, int l2norm, bool use_bf16,
+                                void* ws, hipStream_t stream)
 {
-    if (use_bf16) {
-        if (K == 128)
-            return launch_chunk_t<bf16, 128>(q, k, qks, v, vs, g, beta, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, scale, l2norm, ws, stream);
-        return launch_chunk_t<bf16, 64>(q, k, qks, v, vs, g, beta, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, scale, l2norm, ws, stream);
-    }
-    if (K == 128)
-        return launch_chunk_t<float, 128>(q, k, qks, v, vs, g, beta, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, scale, l2norm, ws, stream);
-    return launch_chunk_t<float, 64>(q, k, qks, v, vs, g, beta, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, scale, l2norm, ws, stream);
+    if (use_bf16)
+        return K == 128 ? launch_prepare_t<bf16, 128>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream)
+                        : launch_prepare_t<bf16, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
+    return K == 128 ? launch_prepare_t<float, 128>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream)
+                    : launch_prepare_t<float, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
+}
+
+hipError_t launch_chunk_scan(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
+                             const float* S0, float* Sf, void* o, const int32_t* cu, int n_seqs,
+                             int B, int T_len, int H, int Hk, int K, int V, bool use_bf16,
+                             const void* ws, hipStream_t stream)
+{
+    if (use_bf16)
+        return K == 128 ? launch_scan_t<bf16, 128>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream)
+                        : launch_scan_t<bf16, 64>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream);
+    return K == 128 ? launch_scan_t<float, 128>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream)
+                    : launch_scan_t<float, 64>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream);
 }
 
 }  // namespace gdn

@@ -16,11 +16,14 @@ hipError_t launch_gate_prepare(const void* a, int64_t asr, const void* b, int64_
                                const float* A_log, const float* dt_bias, float* g, float* beta,
                                int R, int H, bool bf16_in, hipStream_t stream);
 size_t chunk_workspace_bytes(int B, int T_len, int H, int n_seqs, bool packed, bool bf16);
-hipError_t launch_chunk_fwd(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
-                            const float* g, const float* beta, const float* S0, float* Sf,
-                            void* o, const int32_t* cu, int n_seqs, int B, int T_len, int H,
-                            int Hk, int K, int V, float scale, int l2norm, bool bf16, void* ws,
-                            hipStream_t stream);
+hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const float* g,
+                                const float* beta, const int32_t* cu, int n_seqs, int B, int T_len,
+                                int H, int Hk, int K, float scale, int l2norm, bool use_bf16,
+                                void* ws, hipStream_t stream);
+hipError_t launch_chunk_scan(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
+                             const float* S0, float* Sf, void* o, const int32_t* cu, int n_seqs,
+                             int B, int T_len, int H, int Hk, int K, int V, bool use_bf16,
+                             const void* ws, hipStream_t stream);
 hipError_t launch_recurrent_decode(const void* x, int64_t xs, const void* ba, int64_t bas,
                                    const float* A_log, const float* dt_bias, float* state,
                                    void* o, int n, int M, int H, int G, int P, int N, float scale,
@@ -104,6 +107,69 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int Hk, int K, int V, i
     return gdn::chunk_workspace_bytes(B, T, H, packed ? n_seqs : 0, packed, dtype == GDN_BF16);
 }
 
+// Checks shared by the chunked-forward entry points (prepare, scan and both).
+static int check_chunk(const void* q, const void* k, int64_t qk_stride_t, const void* v,
+                       int64_t v_stride_t, bool need_v, const float* g, const float* beta,
+                       bool need_gates, const float* S0, const float* Sf, const void* o,
+                       bool need_o, const int32_t* cu, int n_seqs, int B, int T, int H, int Hk,
+                       int K, int V, int qk_l2norm, int dtype, const void* ws, size_t ws_bytes)
+{
+    if (B < 1 || T < 0 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_EINVAL;
+    const bool has_tokens = T > 0;   // with no tokens the token tensors may be NULL
+    if (!ws) return GDN_EINVAL;
+    if (has_tokens && (!q || !k || (need_v && !v) || (need_gates && (!g || !beta)) || (need_o && !o)))
+        return GDN_EINVAL;
+    if (qk_l2norm != 0 && qk_l2norm != 1) return GDN_EINVAL;
+    if (cu && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
+    if ((int64_t)B * T > INT_MAX) return GDN_EINVAL;
+    if (!valid_dtype(dtype) || !head_dim_ok(K) || !head_dim_ok(V)) return GDN_EUNSUPPORTED;
+    if (qk_stride_t < (int64_t)Hk * K || (need_v && v_stride_t < (int64_t)H * V)) return GDN_EINVAL;
+    if (need_o && has_tokens && (o == q || o == k || o == v)) return GDN_EINVAL;
+    if (need_o && Sf && (const void*)Sf == o) return GDN_EINVAL;
+    const int es = elem_size(dtype);
+    if (!aligned16(q) || !aligned16(k) || (need_v && !aligned16(v)) || (need_o && !aligned16(o)) ||
+        !stride16(qk_stride_t, dtype) || (need_v && !stride16(v_stride_t, dtype)) ||
+        (S0 && !aligned16(S0)) || (Sf && !aligned16(Sf)) ||
+        (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return GDN_EUNSUPPORTED;
+    // the scan addresses a 64-token chunk with 32-bit byte offsets
+    if (64 * qk_stride_t * es > INT_MAX || (need_v && 64 * v_stride_t * es > INT_MAX) ||
+        (int64_t)64 * H * V > INT_MAX)
+        return GDN_EUNSUPPORTED;
+    const size_t need = gdn::chunk_workspace_bytes(B, T, H, cu ? n_seqs : 0, cu != nullptr,
+                                                   dtype == GDN_BF16);
+    if (ws_bytes < need) return GDN_EWORKSPACE;
+    return GDN_OK;
+}
+
+int gdn_chunk_prepare(const void* q, const void* k, int64_t qk_stride_t, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, int n_seqs, int B, int T, int H,
+                      int Hk, int K, float scale, int qk_l2norm, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream)
+{
+    const int st = check_chunk(q, k, qk_stride_t, nullptr, 0, false, g, beta, true, nullptr, nullptr,
+                               nullptr, false, cu_seqlens, n_seqs, B, T, H, Hk, K, 64, qk_l2norm,
+                               dtype, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    return status_from(gdn::launch_chunk_prepare(q, k, qk_stride_t, g, beta, cu_seqlens, n_seqs, B, T,
+                                                 H, Hk, K, scale, qk_l2norm, dtype == GDN_BF16,
+                                                 workspace, (hipStream_t)stream));
+}
+
+int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t, const void* v,
+                   int64_t v_stride_t, const float* initial_state, float* final_state, void* o,
+                   const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K, int V,
+                   int dtype, const void* workspace, size_t workspace_bytes, void* stream)
+{
+    const int st = check_chunk(q, k, qk_stride_t, v, v_stride_t, true, nullptr, nullptr, false,
+                               initial_state, final_state, o, true, cu_seqlens, n_seqs, B, T, H, Hk,
+                               K, V, 0, dtype, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    return status_from(gdn::launch_chunk_scan(q, k, qk_stride_t, v, v_stride_t, initial_state,
+                                              final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+                                              dtype == GDN_BF16, workspace, (hipStream_t)stream));
+}
+
 int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t, const void* v,
                   int64_t v_stride_t, const float* g, const float* beta,
                   const float* initial_state, float* final_state, void* o,
@@ -111,28 +177,17 @@ int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t, const void*
                   float scale, int qk_l2norm, int dtype, void* workspace, size_t workspace_bytes,
                   void* stream)
 {
-    if (B < 1 || T < 0 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_EINVAL;
-    const bool has_tokens = T > 0;   // with no tokens the token tensors may be NULL
-    if (!workspace || (has_tokens && (!q || !k || !v || !g || !beta || !o))) return GDN_EINVAL;
-    if (qk_l2norm != 0 && qk_l2norm != 1) return GDN_EINVAL;
-    if (cu_seqlens && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
-    if ((int64_t)B * T > INT_MAX) return GDN_EINVAL;
-    if (!valid_dtype(dtype) || !head_dim_ok(K) || !head_dim_ok(V)) return GDN_EUNSUPPORTED;
-    if (qk_stride_t < (int64_t)Hk * K || v_stride_t < (int64_t)H * V) return GDN_EINVAL;
-    if (has_tokens && (o == q || o == k || o == v)) return GDN_EINVAL;
-    if (final_state && (const void*)final_state == (const void*)o) return GDN_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        !stride16(qk_stride_t, dtype) || !stride16(v_stride_t, dtype) ||
-        (initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return GDN_EUNSUPPORTED;
-    const int ns = cu_seqlens ? n_seqs : 0;
-    const size_t need = gdn::chunk_workspace_bytes(B, T, H, ns, cu_seqlens != nullptr, dtype == GDN_BF16);
-    if (workspace_bytes < need) return GDN_EWORKSPACE;
-    return status_from(gdn::launch_chunk_fwd(q, k, qk_stride_t, v, v_stride_t, g, beta,
-                                             initial_state, final_state, o, cu_seqlens, n_seqs, B,
-                                             T, H, Hk, K, V, scale, qk_l2norm, dtype == GDN_BF16,
-                                             workspace, (hipStream_t)stream));
+    const int st = check_chunk(q, k, qk_stride_t, v, v_stride_t, true, g, beta, true, initial_state,
+                               final_state, o, true, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+                               qk_l2norm, dtype, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    hipError_t e = gdn::launch_chunk_prepare(q, k, qk_stride_t, g, beta, cu_seqlens, n_seqs, B, T, H,
+                                             Hk, K, scale, qk_l2norm, dtype == GDN_BF16, workspace,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return GDN_ELAUNCH;
+    return status_from(gdn::launch_chunk_scan(q, k, qk_stride_t, v, v_stride_t, initial_state,
+                                              final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+                                              dtype == GDN_BF16, workspace, (hipStream_t)stream));
 }
 
 int gdn_recurrent_decode(const void* x, int64_t x_stride_n, const void* ba, int64_t ba_stride_n,

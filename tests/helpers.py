@@ -23,9 +23,21 @@ def rel_err(got, ref) -> float:
     return float(err / denom)
 
 
+def record_parity(what: str, err: float, tol: float) -> None:
+    """Append a measured parity figure to $GDN_PARITY_LOG (JSON lines), if set."""
+    import json
+    import os
+    path = os.environ.get("GDN_PARITY_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": test, "what": what, "err": err, "tol": tol}) + "\n")
+
+
 def assert_close(got, ref, dtype, what=""):
     e = rel_err(got, ref)
     tol = TOL[dtype]
+    record_parity(what, e, tol)
     assert np.isfinite(np.asarray(got, np.float64)).all(), f"{what}: non-finite output"
     assert e <= tol, f"{what}: max-abs-err/max-abs-ref = {e:.3e} > {tol:.0e}"
     return e

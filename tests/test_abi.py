@@ -45,13 +45,16 @@ def lib():
     L.gdn_chunk_fwd.argtypes = ([vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6
                                 + [f32, i32, i32, vp, sz, vp])
     L.gdn_recurrent_decode.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp] + [i32] * 6 + [f32, i32, i32, vp]
+    L.gdn_chunk_prepare.argtypes = [vp, vp, i64, vp, vp, vp, i32] + [i32] * 5 + [f32, i32, i32, vp, sz, vp]
+    L.gdn_chunk_scan.argtypes = [vp, vp, i64, vp, i64, vp, vp, vp, vp, i32] + [i32] * 7 + [vp, sz, vp]
     return L
 
 
 def test_header_declares_the_four_operations():
     fns = declared_functions()
-    for name in ("gdn_conv1d_causal", "gdn_gate_prepare", "gdn_chunk_fwd",
-                 "gdn_chunk_fwd_workspace_size", "gdn_recurrent_decode", "gdn_status_string"):
+    for name in ("gdn_conv1d_causal", "gdn_gate_prepare", "gdn_chunk_fwd", "gdn_chunk_prepare",
+                 "gdn_chunk_scan", "gdn_chunk_fwd_workspace_size", "gdn_recurrent_decode",
+                 "gdn_status_string"):
         assert name in fns
 
 
@@ -148,17 +151,36 @@ def test_chunk_validation(lib):
     assert chunk(lib, wsb=need - 1) == EWS
 
 
+def test_chunk_phase_validation(lib):
+    need = lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    prep = lambda **kw: lib.gdn_chunk_prepare(
+        kw.get("q", P), kw.get("k", P + 4096), kw.get("qks", 6144), kw.get("g", P2), kw.get("beta", P3),
+        None, 0, 4, 4096, kw.get("H", 16), kw.get("Hk", 16), kw.get("K", 128), 1.0, 1, BF16,
+        kw.get("ws", WS), kw.get("wsb", need), None)
+    scan = lambda **kw: lib.gdn_chunk_scan(
+        kw.get("q", P), kw.get("k", P + 4096), 6144, kw.get("v", P + 8192), kw.get("vs", 6144), None,
+        kw.get("Sf", P4), kw.get("o", P5), None, 0, 4, 4096, 16, 16, 128, kw.get("V", 128), BF16,
+        kw.get("ws", WS), kw.get("wsb", need), None)
+    assert prep(g=None) == EINVAL and prep(beta=None) == EINVAL and prep(ws=None) == EINVAL
+    assert prep(H=16, Hk=5) == EINVAL and prep(K=32) == EUNSUP and prep(wsb=need - 1) == EWS
+    assert prep(qks=1 << 40) == EUNSUP                    # 64 rows would overflow 32-bit offsets
+    assert scan(v=None) == EINVAL and scan(o=None) == EINVAL and scan(o=P) == EINVAL
+    assert scan(V=96) == EUNSUP and scan(vs=100) == EINVAL and scan(wsb=need - 1) == EWS
+
+
 def test_chunk_workspace_size(lib):
-    # dense: offsets (256 B) + G (4 B x tiles x H x 64) + T (2 B x tiles x H x 64 x 64)
+    # offsets (one 256-byte block) + one record per (chunk, value head): T and P as 6
+    # MFMA fragments each (64 lanes x 16 B bf16 / 32 B fp32) + 4 x 64 fp32 row factors
+    rec_bf16 = 2 * 6 * 64 * 16 + 4 * 64 * 4
+    rec_fp32 = 2 * 6 * 64 * 32 + 4 * 64 * 4
     tiles, H = 4 * 64, 16
     need = lib.gdn_chunk_fwd_workspace_size(4, 4096, H, H, 128, 128, 0, BF16)
-    assert need == 256 + 4 * tiles * H * 64 + 2 * tiles * H * 64 * 64
-    fp32 = lib.gdn_chunk_fwd_workspace_size(4, 4096, H, H, 128, 128, 0, FP32)
-    assert fp32 > need
+    assert need == 256 + tiles * H * rec_bf16
+    assert lib.gdn_chunk_fwd_workspace_size(4, 4096, H, H, 128, 128, 0, FP32) == 256 + tiles * H * rec_fp32
     # packed: an upper bound on the chunk count, sum(ceil(len/64)) <= (T + 63 n) / 64
     packed = lib.gdn_chunk_fwd_workspace_size(1, 1000, 4, 4, 64, 64, 10, BF16)
     tiles_ub = (1000 + 63 * 10) // 64
-    assert packed >= 4 * tiles_ub * 4 * 64 + 2 * tiles_ub * 4 * 64 * 64
+    assert packed >= tiles_ub * 4 * rec_bf16
     assert lib.gdn_chunk_fwd_workspace_size(0, 10, 4, 4, 64, 64, 0, BF16) == 0
 
 
