@@ -57,6 +57,12 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration runs)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
+                   help="turn a rocprofv3 --stats kernel_stats.csv into a profiles/ summary")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (made with "
+                        "--copy-probe) into profiles/traffic.json")
+    p.add_argument("--command", default="", help="the command that produced the CSVs")
     return p.parse_args()
 
 
@@ -230,8 +236,93 @@ def run_decode(args, gdn, wl, torch, dev, stream):
                         f"fp32 state in place, {steps} steps"}
 
 
+def _kernel_stem(name):
+    import re
+    m = re.match(r"_ZN3gdn\d+(\w+?)I", name)
+    if m:
+        return m.group(1)
+    return name.split("(")[0][:60]
+
+
+def summarize_stats(csv_path, out_md, command):
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
+             f"Command: `{command}`", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or ""
+        calls = int(float(r["Calls"]))
+        avg = float(r["AverageNs"]) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        lines.append(f"| `{_kernel_stem(name)}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f}% |")
+    lines.append("")
+    lines.append("Full symbols:")
+    lines.append("")
+    for r in rows:
+        lines.append(f"- `{(r.get('Name') or '')[:200]}`")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_traffic(fetch_csv, write_csv, command):
+    """Per-kernel HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that makes the plain 1 GiB device copy
+    (the runtime's buffer-copy kernel, --copy-probe) read and write 1 GiB."""
+    import collections
+    import csv
+
+    def per_dispatch(path, counter):
+        acc = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            acc[d] += float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+            names[d] = r["Kernel_Name"]
+        return acc, names
+
+    fetch, fnames = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, wnames = per_dispatch(write_csv, "WRITE_SIZE")
+    gib = float(1 << 30)
+    # the probe copies are the buffer-copy dispatches that move 1 GiB: the last three
+    # of that kernel in each run (earlier ones are uploads and the state reset)
+    def probe(table, names):
+        ids = sorted(d for d, n in names.items() if "copybuffer" in n.lower())[-3:]
+        vals = [table[d] for d in ids]
+        return sum(vals) / len(vals) if vals else None
+    pf, pw = probe(fetch, fnames), probe(write, wnames)
+    ff = gib / pf if pf else None
+    fw = gib / pw if pw else None
+    res = {"command": command, "copy_kernel_bytes": gib, "copy_fetch_raw": pf, "copy_write_raw": pw,
+           "fetch_factor": ff, "write_factor": fw, "kernels": {}}
+    for op, (stem, src) in KERNELS.items():
+        fv = [v for d, v in fetch.items() if stem in fnames[d]]
+        wv = [v for d, v in write.items() if stem in wnames[d]]
+        if not fv or ff is None or fw is None:
+            continue
+        fb = sum(fv) / len(fv) * ff
+        wb = (sum(wv) / len(wv) * fw) if wv else 0.0
+        res["kernels"][stem] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                                "launches": len(fv), "source_sha": source_hash(src)}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command)
+        return
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                                           args.command), indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; runs on several GPUs "
                                    "are not part of this build", "n_gpus": args.gpus}))
