@@ -33,6 +33,9 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-rdc", "-ffp-contract=fast",
+    # matrix-core accumulators in ordinary VGPRs: the kernels keep their
+    # accumulators live across VALU work, and the AGPR form adds a copy per use
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
