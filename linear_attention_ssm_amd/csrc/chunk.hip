@@ -45,6 +45,7 @@
 namespace gdn {
 
 constexpr int kPrepThreads = 256;
+constexpr int kPrepHeads = 4;      // value heads per key head whose gates the prep requests up front
 constexpr int kLowerTiles = 10;     // 16 x 16 tiles on or below the diagonal of a 64 x 64 matrix
 constexpr int kTriFrags = 6;        // non-zero 16 x 32 A-operand blocks of a lower-triangular 64 x 64
 
@@ -190,7 +191,8 @@ struct RowTile {
 #pragma unroll
             for (int e = 0; e < VN; ++e) ss += f[e] * f[e];
             ss = group_sum<SEGS>(ss);
-            if (seg == 0) rnorm[row] = l2norm ? 1.f / sqrtf(ss + 1e-6f) : 1.f;
+            const float rn = l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;   // (v_rsq_f32, ~1 ulp)
+            if (seg == 0) rnorm[row] = rn;
             *reinterpret_cast<typename V::type*>(dst + row * ld + seg * VN) = r;
         }
     }
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets, int n_seqs, int T_len,
-    int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec)
+    int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec, int n_items)
 {
     typedef Mma<T> MT;
     typedef PrepSmem<T, KD> SM;
@@ -209,137 +211,19 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
-    const int tile = blockIdx.x;
-    const int hk = blockIdx.y;
-    ChunkLoc loc;
-    if (!locate_tile(tile, cu, offsets, n_seqs, T_len, loc)) return;
-    const int L = loc.L;
-
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int grp = lane >> 4;
     const int col = lane & 15;
-
-    const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + hk * KD;
-    {
-        RowTile<T, KD, kPrepThreads> kt, qt;
-        kt.load(kp + rowoff, qk_stride, L);
-        qt.load(qp + rowoff, qk_stride, L);
-        kt.store(L, l2norm, sm.k, SM::ldk, sm.rk);
-        qt.store(L, l2norm, sm.q, SM::ldk, sm.rq);
-    }
-    __syncthreads();
-
-    // raw K K^T (tiles 0..9) and Q K^T (tiles 10..19), lower 16 x 16 tiles, 5 per wave
-    f32x4 S[5];
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-        const int t = wave + 4 * j;
-        const int tt = t < kLowerTiles ? t : t - kLowerTiles;
-        const T* am = t < kLowerTiles ? sm.k : sm.q;
-        S[j] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < KD / 32; ++kb)
-            S[j] = MT::mma(MT::lds_frag(am, SM::ldk, 16 * tri_row(tt) + col, 32 * kb, grp),
-                           MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(tt) + col, 32 * kb, grp), S[j]);
-    }
-
     const int per = H / Hk;
-    for (int hv = 0; hv < per; ++hv) {
-        const int h = hk * per + hv;
-        unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
-        if (wave == 0) {
-            // G = inclusive cumsum of g over the chunk (rows >= L carry g = 0)
-            const int lr = min(lane, L - 1);
-            float gv = g[(int64_t)(loc.tok0 + lr) * H + h];
-            float bv = beta[(int64_t)(loc.tok0 + lr) * H + h];
-            if (lane >= L) { gv = 0.f; bv = 0.f; }
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                float up = __shfl_up(gv, d, kWave);
-                if (lane >= d) gv += up;
-            }
-            sm.G[lane] = gv;
-            sm.beta[lane] = bv;
-            const float GL = __shfl(gv, kWave - 1, kWave);
-            const bool live = lane < L;
-            const float gam = __expf(gv);
-            float* fac = reinterpret_cast<float*>(rec + RC::fac);
-            fac[0 * kChunk + lane] = live ? gam * sm.rk[lane] : 0.f;
-            fac[1 * kChunk + lane] = live ? scale * gam * sm.rq[lane] : 0.f;
-            fac[2 * kChunk + lane] = live ? __expf(GL - gv) * sm.rk[lane] : 0.f;
-            fac[3 * kChunk + lane] = __expf(GL);
-        }
-        __syncthreads();
 
-        // A (normalised keys, strictly lower) and P (scaled, lower incl. diagonal)
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int t = wave + 4 * j;
-            const bool isA = t < kLowerTiles;
-            const int tt = isA ? t : t - kLowerTiles;
-            const int s = 16 * tri_col(tt) + col;
-            const float Gs = sm.G[s];
-            const float rks = sm.rk[s];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * tri_row(tt) + 4 * grp + e;
-                const float decay = __expf(fminf(sm.G[r] - Gs, 0.f));
-                if (isA) {
-                    sm.a[r * SM::lda + s] = (s < r) ? sm.beta[r] * decay * sm.rk[r] * rks * S[j][e] : 0.f;
-                } else {
-                    sm.p[r * SM::ldp + s] =
-                        from_f32<T>((s <= r) ? scale * decay * sm.rq[r] * rks * S[j][e] : 0.f);
-                }
-            }
-        }
-        __syncthreads();
-
-        // diagonal blocks: wave w inverts I + A_ww by forward substitution,
-        // lane j < 16 solving for column j.
-        if (lane < 16) {
-            const int b0 = 16 * wave;
-            float xcol[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc -= sm.a[(b0 + r) * SM::lda + b0 + s] * xcol[s];
-                xcol[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.n[(b0 + r) * SM::lda + b0 + lane] = xcol[r];
-        }
-        __syncthreads();
-
-        // off-diagonal blocks by block rows: N_iw = -N_ii sum_{k=w}^{i-1} A_ik N_kw
-        for (int i = 1; i < 4; ++i) {
-            if (wave < i) {
-                const int w = wave;
-                f32x4 X = zero4();
-                for (int kk = w; kk < i; ++kk) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float av = sm.a[(16 * i + col) * SM::lda + 16 * kk + 4 * grp + s];
-                        const float bv = sm.n[(16 * kk + 4 * grp + s) * SM::lda + 16 * w + col];
-                        X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, X, 0, 0, 0);
-                    }
-                }
-                f32x4 Y = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float av = sm.n[(16 * i + col) * SM::lda + 16 * i + 4 * grp + s];
-                    Y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, X[s], Y, 0, 0, 0);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm.n[(16 * i + 4 * grp + e) * SM::lda + 16 * w + col] = -Y[e];
-            }
-            __syncthreads();
-        }
-
-        // T = N diag(beta) and P as A-operand fragments: 12 fragments, 3 per wave
+    // Persistent workgroups: item it = (tile, key head) = (it / Hk, it % Hk). The
+    // next item's K and Q rows are loaded into registers while this one is
+    // computed, so their HBM latency is hidden behind the arithmetic.
+    // T = N diag(beta) and P as A-operand fragments: 12 fragments, 3 per wave.
+    // Operand slots j < 4 and j >= 4 are 4 consecutive columns each.
+    auto write_frags = [&](unsigned char* rec) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int f = wave + 4 * j;
@@ -349,11 +233,18 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             const int kb = tri_frag_kb(ff);
             f32x8 v;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int c = 32 * kb + slot_k(grp, jj);
-                float x = 0.f;
-                if (c <= r) x = isT ? sm.n[r * SM::lda + c] * sm.beta[c] : to_f32(sm.p[r * SM::ldp + c]);
-                v[jj] = x;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c0 = 32 * kb + 16 * hh + 4 * grp;     // slots 4 hh .. 4 hh + 3
+                f32x4 x;
+                if (isT) {
+                    x = *reinterpret_cast<const f32x4*>(&sm.n[r * SM::lda + c0]) *
+                        *reinterpret_cast<const f32x4*>(&sm.beta[c0]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = to_f32(sm.p[r * SM::ldp + c0 + e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * hh + e] = (c0 + e <= r) ? x[e] : 0.f;
             }
             typename MT::Frag fr;
             if constexpr (sizeof(typename MT::Frag) == 16) fr = __builtin_convertvector(v, bf16x8);
@@ -361,8 +252,192 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             *reinterpret_cast<typename MT::Frag*>(rec + (isT ? RC::tfrag : RC::pfrag) +
                                                   (ff * kWave + lane) * RC::frag_bytes) = fr;
         }
-        __syncthreads();
+    };
+    unsigned char* pend = nullptr;     // record whose fragments are still to be written
+
+    // gate values (g, beta) of the first kPrepHeads value heads of an item,
+    // lane = row (rows past the end repeat the last one; they are masked later)
+    float gn[kPrepHeads], bn[kPrepHeads];
+    auto load_gates = [&](int hk_, const ChunkLoc& l) {
+        const int lr = min(lane, l.L - 1);
+#pragma unroll
+        for (int i = 0; i < kPrepHeads; ++i) {
+            const int hh = hk_ * per + min(i, per - 1);
+            gn[i] = g[(int64_t)(l.tok0 + lr) * H + hh];
+            bn[i] = beta[(int64_t)(l.tok0 + lr) * H + hh];
+        }
+    };
+    RowTile<T, KD, kPrepThreads> kt, qt;
+    int it = blockIdx.x;
+    ChunkLoc loc;
+    bool have = it < n_items && locate_tile(it / Hk, cu, offsets, n_seqs, T_len, loc);
+    if (have) {
+        load_gates(it % Hk, loc);
+        const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + (it % Hk) * KD;
+        kt.load(kp + rowoff, qk_stride, loc.L);
+        qt.load(qp + rowoff, qk_stride, loc.L);
     }
+    while (it < n_items) {
+        const int tile = it / Hk;
+        const int hk = it - tile * Hk;
+        const ChunkLoc cur = loc;
+        const bool cur_ok = have;
+        const int L = cur.L;
+        // Order of the vector-memory operations at the top of an item (their
+        // counter retires in issue order): the wait for this item's rows and
+        // gate values (both requested one item earlier), then the next item's
+        // gate values and rows, then the previous item's last fragments. Every
+        // wave issues the same operations, so the counts do not depend on the wave.
+        if (cur_ok) {
+            kt.store(L, l2norm, sm.k, SM::ldk, sm.rk);
+            qt.store(L, l2norm, sm.q, SM::ldk, sm.rq);
+        }
+        float gv[kPrepHeads], bv[kPrepHeads];
+#pragma unroll
+        for (int i = 0; i < kPrepHeads; ++i) { gv[i] = gn[i]; bv[i] = bn[i]; }
+        const int nit = it + gridDim.x;
+        have = nit < n_items && locate_tile(nit / Hk, cu, offsets, n_seqs, T_len, loc);
+        if (have) {
+            load_gates(nit % Hk, loc);
+            const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + (nit % Hk) * KD;
+            kt.load(kp + rowoff, qk_stride, loc.L);
+            qt.load(qp + rowoff, qk_stride, loc.L);
+        }
+        if (pend) {   // the previous item's last fragments (its LDS results are intact)
+            write_frags(pend);
+            pend = nullptr;
+        }
+        if (!cur_ok) { it = nit; continue; }   // (uniform: a packed item past the last chunk)
+        __syncthreads();
+
+        // raw K K^T (tiles 0..9) and Q K^T (tiles 10..19), lower 16 x 16 tiles, 5 per wave
+        f32x4 S[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int t = wave + 4 * j;
+            const int tt = t < kLowerTiles ? t : t - kLowerTiles;
+            const T* am = t < kLowerTiles ? sm.k : sm.q;
+            S[j] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KD / 32; ++kb)
+                S[j] = MT::mma(MT::lds_frag(am, SM::ldk, 16 * tri_row(tt) + col, 32 * kb, grp),
+                               MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(tt) + col, 32 * kb, grp), S[j]);
+        }
+
+        for (int hv = 0; hv < per; ++hv) {
+            const int h = hk * per + hv;
+            unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
+            if (wave == 0) {
+                // G = inclusive cumsum of g over the chunk (rows >= L carry g = 0)
+                float gh = 0.f, bh = 0.f;
+#pragma unroll
+                for (int i = 0; i < kPrepHeads; ++i)
+                    if (i == hv) { gh = gv[i]; bh = bv[i]; }
+                if (hv >= kPrepHeads) {   // (more value heads per key head than held above)
+                    const int lr = min(lane, L - 1);
+                    gh = g[(int64_t)(cur.tok0 + lr) * H + h];
+                    bh = beta[(int64_t)(cur.tok0 + lr) * H + h];
+                }
+                float gc = lane < L ? gh : 0.f;
+                const float bc = lane < L ? bh : 0.f;
+                gc = wave_inclusive_scan(gc);
+                sm.G[lane] = gc;
+                sm.beta[lane] = bc;
+                const float GL = lane_value(gc, kWave - 1);
+                const bool live = lane < L;
+                const float gam = __expf(gc);
+                float* fac = reinterpret_cast<float*>(rec + RC::fac);
+                fac[0 * kChunk + lane] = live ? gam * sm.rk[lane] : 0.f;
+                fac[1 * kChunk + lane] = live ? scale * gam * sm.rq[lane] : 0.f;
+                fac[2 * kChunk + lane] = live ? __expf(GL - gc) * sm.rk[lane] : 0.f;
+                fac[3 * kChunk + lane] = __expf(GL);
+            }
+            __syncthreads();
+
+            // A (normalised keys, strictly lower) and P (scaled, lower incl. diagonal)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                const int t = wave + 4 * j;
+                const bool isA = t < kLowerTiles;
+                const int tt = isA ? t : t - kLowerTiles;
+                const int s = 16 * tri_col(tt) + col;
+                const int r0 = 16 * tri_row(tt) + 4 * grp;
+                const float Gs = sm.G[s];
+                const float rks = sm.rk[s];
+                const f32x4 Gr = *reinterpret_cast<const f32x4*>(&sm.G[r0]);
+                const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[r0]);
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(isA ? &sm.rk[r0] : &sm.rq[r0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r0 + e;
+                    const float decay = __expf(fminf(Gr[e] - Gs, 0.f));
+                    if (isA) {
+                        sm.a[r * SM::lda + s] = (s < r) ? br[e] * decay * rr[e] * rks * S[j][e] : 0.f;
+                    } else {
+                        sm.p[r * SM::ldp + s] =
+                            from_f32<T>((s <= r) ? scale * decay * rr[e] * rks * S[j][e] : 0.f);
+                    }
+                }
+            }
+            __syncthreads();
+
+            // diagonal blocks: wave w inverts I + A_ww by forward substitution,
+            // lane j < 16 solving for column j.
+            if (lane < 16) {
+                const int b0 = 16 * wave;
+                float xcol[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+                    for (int s = 0; s < r; ++s) acc -= sm.a[(b0 + r) * SM::lda + b0 + s] * xcol[s];
+                    xcol[r] = acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.n[(b0 + r) * SM::lda + b0 + lane] = xcol[r];
+            }
+            __syncthreads();
+
+            // off-diagonal blocks by block rows: N_iw = -N_ii sum_{k=w}^{i-1} A_ik N_kw
+            for (int i = 1; i < 4; ++i) {
+                if (wave < i) {
+                    const int w = wave;
+                    f32x4 X = zero4();
+                    for (int kk = w; kk < i; ++kk) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const float av = sm.a[(16 * i + col) * SM::lda + 16 * kk + 4 * grp + s];
+                            const float bvv = sm.n[(16 * kk + 4 * grp + s) * SM::lda + 16 * w + col];
+                            X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bvv, X, 0, 0, 0);
+                        }
+                    }
+                    f32x4 Y = zero4();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float av = sm.n[(16 * i + col) * SM::lda + 16 * i + 4 * grp + s];
+                        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, X[s], Y, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sm.n[(16 * i + 4 * grp + e) * SM::lda + 16 * w + col] = -Y[e];
+                }
+                __syncthreads();
+            }
+
+            // T = N diag(beta) and P as A-operand fragments. The last value head's
+            // are written at the start of the next item instead: global stores
+            // issued just before the next item's rows are needed would otherwise
+            // be waited for together with those loads.
+            if (hv + 1 < per) {
+                write_frags(rec);
+                __syncthreads();
+            } else {
+                pend = rec;
+            }
+        }
+        it = nit;
+    }
+    if (pend) write_frags(pend);
 }
 
 // ------------------------------------------------------------ chunk_scan
@@ -1283,9 +1358,12 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         auto kern = chunk_prep_kernel<T, KD>;
         hipError_t e = set_smem(kern, smem);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)tiles, Hk), dim3(kPrepThreads), smem, stream,
+        // persistent workgroups, two per CU (LDS), each walking the (tile, key head) items
+        const int64_t items = tiles * Hk;
+        const int grid = (int)(items < 2 * 256 ? items : 2 * 256);
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
-                           Hk, scale, l2norm, w.rec);
+                           Hk, scale, l2norm, w.rec, (int)items);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

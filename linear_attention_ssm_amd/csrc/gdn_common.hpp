@@ -58,18 +58,60 @@ template <> struct V16<float> {
     static __device__ __forceinline__ type from_float(ftype v) { return v; }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// Lane moves within the wave that stay in the VALU (no LDS round trip): DPP
+// patterns inside 4-, 8- and 16-lane rows, and gfx950's row / half-wave swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8 <- lane 7 - i
+constexpr int kDppRowMirror = 0x140;  // lane i of each 16 <- lane 15 - i
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64); every
+// lane of a group ends with the same value.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(width >= 1 && width <= 64 && (width & (width - 1)) == 0, "group width");
+    if constexpr (width >= 2) v += dpp_mov<kDppQuadSwap1>(v);
+    if constexpr (width >= 4) v += dpp_mov<kDppQuadSwap2>(v);
+    if constexpr (width >= 8) v += dpp_mov<kDppHalfMirror>(v);
+    if constexpr (width >= 16) v += dpp_mov<kDppRowMirror>(v);
+    if constexpr (width >= 32) {
+        // after the swap the two results hold rows (0, 0, 2, 2) and (1, 1, 3, 3)
+        const int b = __builtin_bit_cast(int, v);
+        const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        v = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+    }
+    if constexpr (width >= 64) {
+        const int b = __builtin_bit_cast(int, v);
+        const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        v = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+    }
     return v;
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
-template <int width>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = width / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside 16-lane rows,
+// then the row totals carried across rows with row broadcasts).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true);
+    return v + __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
     return v;
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 // ---------------------------------------------------------------- MFMA
