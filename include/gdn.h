@@ -64,8 +64,8 @@ const char* gdn_status_string(int status);
  * batch row or across a packed-sequence boundary.
  *   x        [B, T, C] in `dtype`, channel dim contiguous; element (b,t,c) at
  *            x + b*x_stride_b + t*x_stride_t + c.
- *   w        [C, W] in `dtype`, contiguous (w[c][W-1] multiplies x_t).
- *   bias     [C] in `dtype`, or NULL for none.
+ *   w        [C, W] in `dtype`, contiguous, 16-byte aligned (w[c][W-1] multiplies x_t).
+ *   bias     [C] in `dtype`, 16-byte aligned, or NULL for none.
  *   y        [B, T, C] in `dtype`, same addressing with y strides. y must not
  *            overlap x (GDN_EINVAL when the base pointers are equal).
  *   cu_seqlens  int32 [n_seqs + 1] device array of packed-sequence offsets,

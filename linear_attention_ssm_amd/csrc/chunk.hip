@@ -45,6 +45,7 @@
 namespace gdn {
 
 constexpr int kPrepThreads = 256;
+constexpr int kPrepWavesPerEU = 2;
 constexpr int kPrepHeads = 4;      // value heads per key head whose gates the prep requests up front
 constexpr int kLowerTiles = 10;     // 16 x 16 tiles on or below the diagonal of a 64 x 64 matrix
 constexpr int kTriFrags = 6;        // non-zero 16 x 32 A-operand blocks of a lower-triangular 64 x 64
@@ -144,10 +145,18 @@ struct PrepSmem {
     static constexpr int ldk = KD + Pad<T>::row;
     static constexpr int lda = kChunk + 4;
     static constexpr int ldp = kChunk + Pad<T>::row;
-    T k[kChunk * ldk];         // raw k rows (rows >= L zero)
-    T q[kChunk * ldk];         // raw q rows
-    float a[kChunk * lda];     // A, strictly lower
-    float n[kChunk * lda];     // N = (I + A)^-1, lower
+    // the raw rows are only read by the products that open an item; A and N
+    // take their place for the rest of it
+    union {
+        struct {
+            T k[kChunk * ldk];     // raw k rows (rows >= L zero)
+            T q[kChunk * ldk];     // raw q rows
+        };
+        struct {
+            float a[kChunk * lda]; // A, strictly lower
+            float n[kChunk * lda]; // N = (I + A)^-1, lower
+        };
+    };
     T p[kChunk * ldp];         // P
     float G[kChunk];
     float beta[kChunk];
@@ -198,8 +207,11 @@ struct RowTile {
     }
 };
 
+// Two workgroups per CU (registers sized for it): the item's steps
+// are short dependent chains, hidden by the other workgroups.
 template <typename T, int KD>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(kPrepWavesPerEU)))
+void chunk_prep_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets, int n_seqs, int T_len,
@@ -253,7 +265,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
                                                   (ff * kWave + lane) * RC::frag_bytes) = fr;
         }
     };
-    unsigned char* pend = nullptr;     // record whose fragments are still to be written
 
     // gate values (g, beta) of the first kPrepHeads value heads of an item,
     // lane = row (rows past the end repeat the last one; they are masked later)
@@ -286,8 +297,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         // Order of the vector-memory operations at the top of an item (their
         // counter retires in issue order): the wait for this item's rows and
         // gate values (both requested one item earlier), then the next item's
-        // gate values and rows, then the previous item's last fragments. Every
-        // wave issues the same operations, so the counts do not depend on the wave.
+        // gate values and rows. Every wave issues the same operations, so the
+        // counts do not depend on the wave.
         if (cur_ok) {
             kt.store(L, l2norm, sm.k, SM::ldk, sm.rk);
             qt.store(L, l2norm, sm.q, SM::ldk, sm.rq);
@@ -302,10 +313,6 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
             const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + (nit % Hk) * KD;
             kt.load(kp + rowoff, qk_stride, loc.L);
             qt.load(qp + rowoff, qk_stride, loc.L);
-        }
-        if (pend) {   // the previous item's last fragments (its LDS results are intact)
-            write_frags(pend);
-            pend = nullptr;
         }
         if (!cur_ok) { it = nit; continue; }   // (uniform: a packed item past the last chunk)
         __syncthreads();
@@ -424,20 +431,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
                 __syncthreads();
             }
 
-            // T = N diag(beta) and P as A-operand fragments. The last value head's
-            // are written at the start of the next item instead: global stores
-            // issued just before the next item's rows are needed would otherwise
-            // be waited for together with those loads.
-            if (hv + 1 < per) {
-                write_frags(rec);
-                __syncthreads();
-            } else {
-                pend = rec;
-            }
+            // T = N diag(beta) and P as A-operand fragments
+            write_frags(rec);
+            __syncthreads();
         }
         it = nit;
     }
-    if (pend) write_frags(pend);
 }
 
 // ------------------------------------------------------------ chunk_scan
@@ -1358,9 +1357,13 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         auto kern = chunk_prep_kernel<T, KD>;
         hipError_t e = set_smem(kern, smem);
         if (e != hipSuccess) return e;
-        // persistent workgroups, two per CU (LDS), each walking the (tile, key head) items
+        // persistent workgroups (as many as are resident at once), each walking
+        // the (tile, key head) items
         const int64_t items = tiles * Hk;
-        const int grid = (int)(items < 2 * 256 ? items : 2 * 256);
+        const int per_cu = kPrepWavesPerEU * 4 / (kPrepThreads / kWave);
+        const int fit = (int)((160 * 1024) / smem);
+        const int64_t cap = 256 * (int64_t)(fit < per_cu ? (fit > 0 ? fit : 1) : per_cu);
+        const int grid = (int)(items < cap ? items : cap);
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
                            Hk, scale, l2norm, w.rec, (int)items);

@@ -39,15 +39,27 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     const int t0 = (blockIdx.x % runs_per_row) * RUN;
     const int c0 = cg * VN;
 
-    // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e]
+    // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e]; the group's VN x W taps
+    // are contiguous, read as W 16-byte vectors
     float wt[kConvW][VN];
 #pragma unroll
-    for (int e = 0; e < VN; ++e)
+    for (int i = 0; i < kConvW; ++i) {
+        const typename V::ftype f = V::to_float(*reinterpret_cast<const typename V::type*>(w + (int64_t)c0 * kConvW + i * VN));
 #pragma unroll
-        for (int j = 0; j < kConvW; ++j) wt[j][e] = to_f32(w[(int64_t)(c0 + e) * kConvW + j]);
+        for (int u = 0; u < VN; ++u) {
+            const int flat = i * VN + u;            // = e * W + j
+            wt[flat % kConvW][flat / kConvW] = f[u];
+        }
+    }
     float bs[VN];
+    if (bias) {
+        const typename V::ftype f = V::to_float(*reinterpret_cast<const typename V::type*>(bias + c0));
 #pragma unroll
-    for (int e = 0; e < VN; ++e) bs[e] = bias ? to_f32(bias[c0 + e]) : 0.f;
+        for (int e = 0; e < VN; ++e) bs[e] = f[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) bs[e] = 0.f;
+    }
 
     const T* xb = x + (int64_t)b * xsb + c0;
     T* yb = y + (int64_t)b * ysb + c0;
@@ -103,7 +115,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
             acc = fmaf(wt[1][e], win[1][e], acc);
             acc = fmaf(wt[2][e], win[2][e], acc);
             acc = fmaf(wt[3][e], xf[e], acc);
-            out[e] = silu ? acc / (1.f + __expf(-acc)) : acc;
+            out[e] = silu ? acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc)) : acc;   // (v_rcp_f32, ~1 ulp)
             win[0][e] = win[1][e];
             win[1][e] = win[2][e];
             win[2][e] = xf[e];

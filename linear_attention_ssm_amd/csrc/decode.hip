@@ -136,9 +136,11 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
         }
     }
 
+    // the updated state streams out: nothing reads it back within this launch,
+    // and non-temporal writes keep it from displacing other data on its way out
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
-        *reinterpret_cast<f32x4*>(st + (int64_t)(rg + RG * j) * PV + 4 * cg) = S[j];
+        __builtin_nontemporal_store(S[j], reinterpret_cast<f32x4*>(st + (int64_t)(rg + RG * j) * PV + 4 * cg));
 }
 
 template <typename T, int NK, int PV>

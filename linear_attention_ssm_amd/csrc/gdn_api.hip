@@ -73,7 +73,8 @@ int gdn_conv1d_causal(const void* x, int64_t x_stride_b, int64_t x_stride_t, con
     if (!valid_dtype(dtype) || W != 4) return GDN_EUNSUPPORTED;
     const int vn = 16 / elem_size(dtype);
     if (C % vn != 0) return GDN_EUNSUPPORTED;
-    if (!aligned16(x) || !aligned16(y) || !stride16(x_stride_t, dtype) ||
+    if (!aligned16(x) || !aligned16(y) || !aligned16(w) || (bias && !aligned16(bias)) ||
+        !stride16(x_stride_t, dtype) ||
         !stride16(y_stride_t, dtype) || (B > 1 && (!stride16(x_stride_b, dtype) || !stride16(y_stride_b, dtype))))
         return GDN_EUNSUPPORTED;
     if (T == 0) return GDN_OK;
