@@ -21,9 +21,10 @@
 //     h' = gamma_L h + K^T (c o U),  c_r = gamma_L / (gamma_r n_r)
 //
 // Split for CDNA4 (two kernels on one stream):
-//   chunk_prep  one workgroup per (chunk, q/k head), every chunk in parallel:
-//               row norms, K K^T and Q K^T on MFMA (shared by the value heads
-//               of a GQA group), then per value head the cumsum, A, the
+//   chunk_prep  one wave per (chunk, q/k head), every chunk in parallel:
+//               K K^T and Q K^T on MFMA straight from the rows in registers
+//               (shared by the value heads of a GQA group; the row norms are
+//               their diagonals), then per value head the cumsum, A, the
 //               64 x 64 unit-lower-triangular inverse (16 x 16 diagonal blocks
 //               by forward substitution, off-diagonal blocks by block
 //               substitution on fp32 MFMA), T, P and the factors a, b, c,
@@ -44,27 +45,15 @@
 
 namespace gdn {
 
-constexpr int kPrepThreads = 256;
-constexpr int kPrepWavesPerEU = 2;
-constexpr int kPrepHeads = 4;      // value heads per key head whose gates the prep requests up front
 constexpr int kLowerTiles = 10;     // 16 x 16 tiles on or below the diagonal of a 64 x 64 matrix
 constexpr int kTriFrags = 6;        // non-zero 16 x 32 A-operand blocks of a lower-triangular 64 x 64
 
-// Lower tile t (0..9) in row order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
-__device__ __forceinline__ int tri_row(int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); }
-__device__ __forceinline__ int tri_col(int t) { const int r = tri_row(t); return t - r * (r + 1) / 2; }
 // A-operand block (row tile rt, 32-wide contraction block kb) of a lower-triangular matrix:
 // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 __device__ __forceinline__ int tri_frag(int rt, int kb) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + kb; }
-__device__ __forceinline__ int tri_frag_rt(int f) { return f < 2 ? f : 2 + (f - 2) / 2; }
-__device__ __forceinline__ int tri_frag_kb(int f) { return f < 2 ? 0 : (f - 2) % 2; }
 
 // Contraction index of operand slot j of lane group grp (see gdn_common.hpp).
 __device__ __forceinline__ int slot_k(int grp, int j) { return j < 4 ? 4 * grp + j : 12 + 4 * grp + j; }
-
-// LDS row padding (elements) of the prep kernel's staged tiles.
-template <typename T> struct Pad { static constexpr int row = 8; };
-template <> struct Pad<float> { static constexpr int row = 4; };
 
 // Per (chunk, value head) record written by chunk_prep and read by chunk_scan:
 //   T fragments [6][64 lanes], P fragments [6][64 lanes], factors float [4][64]
@@ -139,78 +128,99 @@ __device__ __forceinline__ bool locate_tile(int tile, const int32_t* __restrict_
 }
 
 // ------------------------------------------------------------ chunk_prep
+//
+// One wave per (chunk, key head) item and nothing shared between waves, so
+// no workgroup barriers: eight items are in flight per CU and each hides the
+// others' memory latency. The raw K and Q rows go straight from global memory
+// into MFMA operand registers; every later step works on 16 x 16 fp32 tiles
+// held as MFMA accumulators. For such a tile M (lane l, c = l & 15,
+// g = l >> 4, element e = 0..3) two layouts are used:
+//     column layout C(M): lane holds M[4 g + e][c]   (what an MFMA yields)
+//     row layout    R(M): lane holds M[c][4 g + e]   (= C(M^T))
+// A 16 x 16 x 16 product D = X Y as four v_mfma_f32_16x16x4f32 steps, step s
+// taking contraction index 4 g + s in every lane, reads X in R and Y in C and
+// yields C(D). The record's A-operand fragments of T and P are R tiles in
+// pairs, so the tiles are built in R: S = K K^T and Q K^T come out of the
+// products already in R by feeding the K rows as the first operand.
 
-template <typename T, int KD>
-struct PrepSmem {
-    static constexpr int ldk = KD + Pad<T>::row;
-    static constexpr int lda = kChunk + 4;
-    static constexpr int ldp = kChunk + Pad<T>::row;
-    // the raw rows are only read by the products that open an item; A and N
-    // take their place for the rest of it
-    union {
-        struct {
-            T k[kChunk * ldk];     // raw k rows (rows >= L zero)
-            T q[kChunk * ldk];     // raw q rows
-        };
-        struct {
-            float a[kChunk * lda]; // A, strictly lower
-            float n[kChunk * lda]; // N = (I + A)^-1, lower
-        };
-    };
-    T p[kChunk * ldp];         // P
-    float G[kChunk];
-    float beta[kChunk];
+// Per-wave LDS: the row vectors of the item and a scratch area for 16 x 16
+// blocks (first the four diagonal blocks of -A and of N, then the six
+// off-diagonal blocks of N on their way from C to R).
+constexpr int kBlk = 272;     // diagonal block stride (floats): 256 + 16 keeps the 4 blocks on distinct banks
+constexpr int kTrRow = 20;    // transpose staging: row stride and block stride (floats)
+constexpr int kTrBlk = 320;
+struct PrepLds {
+    float G2[kChunk];          // log2(e) x inclusive cumsum of g (rows >= L: g taken as 0)
+    float beta[kChunk];        // beta (rows >= L: 0)
     float rk[kChunk];          // 1 / |k_r| (1 without normalisation)
-    float rq[kChunk];
+    float rq[kChunk];          // 1 / |q_r|
+    float blk[8 * kBlk];
 };
+static_assert(6 * kTrBlk <= 8 * kBlk, "transpose staging fits the block scratch");
 
-// A 64 x KD tile of token rows, loaded by NT threads in 16-byte segments (thread
-// tid owns segment tid % SEGS of rows tid / SEGS + p * RPP). All loads are
-// issued before any is used; rows >= L read row L-1 and are zeroed on store.
-template <typename T, int KD, int NT>
-struct RowTile {
-    typedef V16<T> V;
-    static constexpr int VN = V::n;
-    static constexpr int SEGS = KD / VN;
-    static constexpr int RPP = NT / SEGS;
-    static constexpr int NP = kChunk / RPP;
-    static_assert(SEGS <= kWave && NT % SEGS == 0 && kChunk % RPP == 0, "staging shape");
-    typename V::type raw[NP];
+// Index of lower tile (i, j), j <= i, in row order, and of strictly-lower tile (i, j), j < i.
+__host__ __device__ constexpr int low_t(int i, int j) { return i * (i + 1) / 2 + j; }
+__host__ __device__ constexpr int off_t(int i, int j) { return i * (i - 1) / 2 + j; }
 
-    __device__ __forceinline__ void load(const T* __restrict__ src, int64_t stride, int L) {
-        const int tid = threadIdx.x;
+__device__ __forceinline__ float pick4(const f32x4& v, int e) {
+    return e == 0 ? v[0] : (e == 1 ? v[1] : (e == 2 ? v[2] : v[3]));
+}
+// X (R layout) times Y (C layout) plus Z, 16 x 16 x 16 in fp32.
+__device__ __forceinline__ f32x4 mma16(const f32x4& x, const f32x4& y, f32x4 z) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = p * RPP + tid / SEGS;
-            raw[p] = *reinterpret_cast<const typename V::type*>(src + min(row, L - 1) * stride +
-                                                                (tid % SEGS) * VN);
-        }
+    for (int s = 0; s < 4; ++s) z = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], z, 0, 0, 0);
+    return z;
+}
+// This wave's LDS writes are complete (and the compiler keeps LDS accesses in
+// program order around it); the wave's later LDS reads see them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Operand fragment of one row: eight consecutive elements (any assignment of
+// contraction indices to slots works as long as both operands share it, and
+// both come from rows loaded the same way). Rows past the chunk lie outside
+// the buffer resource and read as zero.
+template <typename T> struct RowFrag;
+template <> struct RowFrag<bf16> {
+    static __device__ __forceinline__ bf16x8 load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
-    // Store into a padded row-major LDS tile and record each row's inverse L2 norm.
-    __device__ __forceinline__ void store(int L, int l2norm, T* dst, int ld, float* rnorm) const {
-        const int tid = threadIdx.x;
-        const int seg = tid % SEGS;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = p * RPP + tid / SEGS;
-            typename V::type r = raw[p];
-            if (row >= L) r = typename V::type{};
-            typename V::ftype f = V::to_float(r);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < VN; ++e) ss += f[e] * f[e];
-            ss = group_sum<SEGS>(ss);
-            const float rn = l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;   // (v_rsq_f32, ~1 ulp)
-            if (seg == 0) rnorm[row] = rn;
-            *reinterpret_cast<typename V::type*>(dst + row * ld + seg * VN) = r;
-        }
+};
+template <> struct RowFrag<float> {
+    static __device__ __forceinline__ f32x8 load(rsrc_t r, uint32_t off) {
+        const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
 
-// Two workgroups per CU (registers sized for it): the item's steps
-// are short dependent chains, hidden by the other workgroups.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag pack_frag(const f32x4& lo, const f32x4& hi) {
+    const f32x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (sizeof(typename Mma<T>::Frag) == 16) return __builtin_convertvector(v, bf16x8);
+    else return v;
+}
+
+// Forward substitution rows R.. of a unit-lower-triangular 16 x 16 solve
+// (I + A) x = e_c, with -A's row r held in `arow` by lane r of the lane's
+// 16-lane row: x[r] = [r == c] + sum_{s<r} (-A)[r][s] x[s].
+template <int R>
+__device__ __forceinline__ void subst_rows(const float (&arow)[16], float (&x)[16], int c) {
+    if constexpr (R < 16) {
+        float acc = R == c ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < R; ++s) acc += dpp_mov<kDppRowBcast + R>(arow[s]) * x[s];
+        x[R] = acc;
+        subst_rows<R + 1>(arow, x, c);
+    }
+}
+
+// Two waves per SIMD: registers sized for it.
 template <typename T, int KD>
-__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(kPrepWavesPerEU)))
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void chunk_prep_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta,
@@ -218,224 +228,205 @@ void chunk_prep_kernel(
     int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec, int n_items)
 {
     typedef Mma<T> MT;
-    typedef PrepSmem<T, KD> SM;
+    typedef typename MT::Frag Frag;
     typedef Rec<T> RC;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+    constexpr int ES = (int)sizeof(T);
+    __shared__ __align__(16) PrepLds sm;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int grp = lane >> 4;
-    const int col = lane & 15;
-    const int per = H / Hk;
-
-    // Persistent workgroups: item it = (tile, key head) = (it / Hk, it % Hk). The
-    // next item's K and Q rows are loaded into registers while this one is
-    // computed, so their HBM latency is hidden behind the arithmetic.
-    // T = N diag(beta) and P as A-operand fragments: 12 fragments, 3 per wave.
-    // Operand slots j < 4 and j >= 4 are 4 consecutive columns each.
-    auto write_frags = [&](unsigned char* rec) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int f = wave + 4 * j;
-            const bool isT = f < kTriFrags;
-            const int ff = isT ? f : f - kTriFrags;
-            const int r = 16 * tri_frag_rt(ff) + col;
-            const int kb = tri_frag_kb(ff);
-            f32x8 v;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int c0 = 32 * kb + 16 * hh + 4 * grp;     // slots 4 hh .. 4 hh + 3
-                f32x4 x;
-                if (isT) {
-                    x = *reinterpret_cast<const f32x4*>(&sm.n[r * SM::lda + c0]) *
-                        *reinterpret_cast<const f32x4*>(&sm.beta[c0]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = to_f32(sm.p[r * SM::ldp + c0 + e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * hh + e] = (c0 + e <= r) ? x[e] : 0.f;
-            }
-            typename MT::Frag fr;
-            if constexpr (sizeof(typename MT::Frag) == 16) fr = __builtin_convertvector(v, bf16x8);
-            else fr = v;
-            *reinterpret_cast<typename MT::Frag*>(rec + (isT ? RC::tfrag : RC::pfrag) +
-                                                  (ff * kWave + lane) * RC::frag_bytes) = fr;
-        }
-    };
-
-    // gate values (g, beta) of the first kPrepHeads value heads of an item,
-    // lane = row (rows past the end repeat the last one; they are masked later)
-    float gn[kPrepHeads], bn[kPrepHeads];
-    auto load_gates = [&](int hk_, const ChunkLoc& l) {
-        const int lr = min(lane, l.L - 1);
-#pragma unroll
-        for (int i = 0; i < kPrepHeads; ++i) {
-            const int hh = hk_ * per + min(i, per - 1);
-            gn[i] = g[(int64_t)(l.tok0 + lr) * H + hh];
-            bn[i] = beta[(int64_t)(l.tok0 + lr) * H + hh];
-        }
-    };
-    RowTile<T, KD, kPrepThreads> kt, qt;
-    int it = blockIdx.x;
+    const int it = blockIdx.x;
+    if (it >= n_items) return;
+    const int tile = it / Hk;
+    const int hk = it - tile * Hk;
     ChunkLoc loc;
-    bool have = it < n_items && locate_tile(it / Hk, cu, offsets, n_seqs, T_len, loc);
-    if (have) {
-        load_gates(it % Hk, loc);
-        const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + (it % Hk) * KD;
-        kt.load(kp + rowoff, qk_stride, loc.L);
-        qt.load(qp + rowoff, qk_stride, loc.L);
-    }
-    while (it < n_items) {
-        const int tile = it / Hk;
-        const int hk = it - tile * Hk;
-        const ChunkLoc cur = loc;
-        const bool cur_ok = have;
-        const int L = cur.L;
-        // Order of the vector-memory operations at the top of an item (their
-        // counter retires in issue order): the wait for this item's rows and
-        // gate values (both requested one item earlier), then the next item's
-        // gate values and rows. Every wave issues the same operations, so the
-        // counts do not depend on the wave.
-        if (cur_ok) {
-            kt.store(L, l2norm, sm.k, SM::ldk, sm.rk);
-            qt.store(L, l2norm, sm.q, SM::ldk, sm.rq);
-        }
-        float gv[kPrepHeads], bv[kPrepHeads];
-#pragma unroll
-        for (int i = 0; i < kPrepHeads; ++i) { gv[i] = gn[i]; bv[i] = bn[i]; }
-        const int nit = it + gridDim.x;
-        have = nit < n_items && locate_tile(nit / Hk, cu, offsets, n_seqs, T_len, loc);
-        if (have) {
-            load_gates(nit % Hk, loc);
-            const int64_t rowoff = (int64_t)loc.tok0 * qk_stride + (nit % Hk) * KD;
-            kt.load(kp + rowoff, qk_stride, loc.L);
-            qt.load(qp + rowoff, qk_stride, loc.L);
-        }
-        if (!cur_ok) { it = nit; continue; }   // (uniform: a packed item past the last chunk)
-        __syncthreads();
+    if (!locate_tile(tile, cu, offsets, n_seqs, T_len, loc)) return;   // packed: past the last chunk
+    const int L = loc.L;
+    const int per = H / Hk;
+    const int lane = threadIdx.x;
+    const int c = lane & 15;
+    const int gq = lane >> 4;
+    const bool live = lane < L;
+    const int lr = min(lane, L - 1);
+    const uint32_t row_bytes = (uint32_t)(qk_stride * ES);
 
-        // raw K K^T (tiles 0..9) and Q K^T (tiles 10..19), lower 16 x 16 tiles, 5 per wave
-        f32x4 S[5];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int t = wave + 4 * j;
-            const int tt = t < kLowerTiles ? t : t - kLowerTiles;
-            const T* am = t < kLowerTiles ? sm.k : sm.q;
-            S[j] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < KD / 32; ++kb)
-                S[j] = MT::mma(MT::lds_frag(am, SM::ldk, 16 * tri_row(tt) + col, 32 * kb, grp),
-                               MT::lds_frag(sm.k, SM::ldk, 16 * tri_col(tt) + col, 32 * kb, grp), S[j]);
-        }
+    // gate values of the first value head (lane = row), requested before the rows
+    float gh = g[(int64_t)(loc.tok0 + lr) * H + hk * per];
+    float bh = beta[(int64_t)(loc.tok0 + lr) * H + hk * per];
 
-        for (int hv = 0; hv < per; ++hv) {
-            const int h = hk * per + hv;
-            unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
-            if (wave == 0) {
-                // G = inclusive cumsum of g over the chunk (rows >= L carry g = 0)
-                float gh = 0.f, bh = 0.f;
+    // ---- S = K K^T and Q K^T (lower tiles, R layout), diagonal tiles of Q Q^T
+    const int64_t base = (int64_t)loc.tok0 * qk_stride + (int64_t)hk * KD;
+    const uint32_t span = (uint32_t)(L - 1) * row_bytes + KD * ES;
+    const rsrc_t rsk = make_rsrc(kp + base, span);
+    const rsrc_t rsq = make_rsrc(qp + base, span);
+    f32x4 skk[kLowerTiles], sqk[kLowerTiles], sqq[4];
 #pragma unroll
-                for (int i = 0; i < kPrepHeads; ++i)
-                    if (i == hv) { gh = gv[i]; bh = bv[i]; }
-                if (hv >= kPrepHeads) {   // (more value heads per key head than held above)
-                    const int lr = min(lane, L - 1);
-                    gh = g[(int64_t)(cur.tok0 + lr) * H + h];
-                    bh = beta[(int64_t)(cur.tok0 + lr) * H + h];
-                }
-                float gc = lane < L ? gh : 0.f;
-                const float bc = lane < L ? bh : 0.f;
-                gc = wave_inclusive_scan(gc);
-                sm.G[lane] = gc;
-                sm.beta[lane] = bc;
-                const float GL = lane_value(gc, kWave - 1);
-                const bool live = lane < L;
-                const float gam = __expf(gc);
-                float* fac = reinterpret_cast<float*>(rec + RC::fac);
-                fac[0 * kChunk + lane] = live ? gam * sm.rk[lane] : 0.f;
-                fac[1 * kChunk + lane] = live ? scale * gam * sm.rq[lane] : 0.f;
-                fac[2 * kChunk + lane] = live ? __expf(GL - gc) * sm.rk[lane] : 0.f;
-                fac[3 * kChunk + lane] = __expf(GL);
+    for (int t = 0; t < kLowerTiles; ++t) { skk[t] = zero4(); sqk[t] = zero4(); }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sqq[i] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KD / 32; ++kb) {
+        Frag kf[4], qf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)(16 * i + c) * row_bytes + (32 * kb + 8 * gq) * ES;
+            kf[i] = RowFrag<T>::load(rsk, off);
+            qf[i] = RowFrag<T>::load(rsq, off);
+        }
+        // C(K_j X_i^T) = R(X_i K_j^T): tile (i, j) of S with the K rows first
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                skk[low_t(i, j)] = MT::mma(kf[j], kf[i], skk[low_t(i, j)]);
+                sqk[low_t(i, j)] = MT::mma(kf[j], qf[i], sqk[low_t(i, j)]);
             }
-            __syncthreads();
-
-            // A (normalised keys, strictly lower) and P (scaled, lower incl. diagonal)
+            sqq[i] = MT::mma(qf[i], qf[i], sqq[i]);
+        }
+    }
+    // row norms from the diagonals: element c & 3 of the lanes with g == c / 4
 #pragma unroll
-            for (int j = 0; j < 5; ++j) {
-                const int t = wave + 4 * j;
-                const bool isA = t < kLowerTiles;
-                const int tt = isA ? t : t - kLowerTiles;
-                const int s = 16 * tri_col(tt) + col;
-                const int r0 = 16 * tri_row(tt) + 4 * grp;
-                const float Gs = sm.G[s];
-                const float rks = sm.rk[s];
-                const f32x4 Gr = *reinterpret_cast<const f32x4*>(&sm.G[r0]);
-                const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[r0]);
-                const f32x4 rr = *reinterpret_cast<const f32x4*>(isA ? &sm.rk[r0] : &sm.rq[r0]);
+    for (int i = 0; i < 4; ++i) {
+        const float kk = pick4(skk[low_t(i, i)], c & 3);
+        const float qq = pick4(sqq[i], c & 3);
+        if (gq == (c >> 2)) {   // (v_rsq_f32, ~1 ulp)
+            sm.rk[16 * i + c] = l2norm ? __builtin_amdgcn_rsqf(kk + 1e-6f) : 1.f;
+            sm.rq[16 * i + c] = l2norm ? __builtin_amdgcn_rsqf(qq + 1e-6f) : 1.f;
+        }
+    }
+
+    for (int hv = 0; hv < per; ++hv) {
+        const int h = hk * per + hv;
+        unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
+        if (hv > 0) {
+            gh = g[(int64_t)(loc.tok0 + lr) * H + h];
+            bh = beta[(int64_t)(loc.tok0 + lr) * H + h];
+        }
+        // ---- cumsum and the per-row factors (lane = row)
+        const float G2 = wave_inclusive_scan(live ? gh : 0.f) * kLog2e;
+        const float GL2 = lane_value(G2, kWave - 1);
+        sm.G2[lane] = G2;
+        sm.beta[lane] = live ? bh : 0.f;
+        wave_lds_sync();   // (also orders the norms written above)
+        {
+            const float rkl = sm.rk[lane];
+            const float gam = __builtin_amdgcn_exp2f(G2);
+            float* fac = reinterpret_cast<float*>(rec + RC::fac);
+            fac[0 * kChunk + lane] = live ? gam * rkl : 0.f;
+            fac[1 * kChunk + lane] = live ? scale * gam * sm.rq[lane] : 0.f;
+            fac[2 * kChunk + lane] = live ? __builtin_amdgcn_exp2f(GL2 - G2) * rkl : 0.f;
+            fac[3 * kChunk + lane] = __builtin_amdgcn_exp2f(GL2);
+        }
+
+        // ---- -A (strictly lower) and P (lower), R layout, row r = 16 i + c and
+        // column s = 16 j + 4 g + e. The decay exp(G_r - G_s) is shared by both;
+        // its exponent is zeroed above the diagonal before exponentiating.
+        f32x4 aR[6];    // R(-A_ij), i > j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * i + c;
+            const float Gr = sm.G2[r];
+            const float fa = -sm.beta[r] * sm.rk[r];
+            const float fp = scale * sm.rq[r];
+            f32x4 pt[4];
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                const f32x4 Gs = *reinterpret_cast<const f32x4*>(&sm.G2[16 * j + 4 * gq]);
+                const f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.rk[16 * j + 4 * gq]);
+                const int t = low_t(i, j);
+                f32x4 a, p;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = r0 + e;
-                    const float decay = __expf(fminf(Gr[e] - Gs, 0.f));
-                    if (isA) {
-                        sm.a[r * SM::lda + s] = (s < r) ? br[e] * decay * rr[e] * rks * S[j][e] : 0.f;
-                    } else {
-                        sm.p[r * SM::ldp + s] =
-                            from_f32<T>((s <= r) ? scale * decay * rr[e] * rks * S[j][e] : 0.f);
+                    float x = Gr - Gs[e];
+                    if (i == j) x = (4 * gq + e <= c) ? x : 0.f;
+                    const float w = ks[e] * __builtin_amdgcn_exp2f(x);
+                    a[e] = fa * w * skk[t][e];
+                    p[e] = fp * w * sqk[t][e];
+                    if (i == j) {
+                        a[e] = (4 * gq + e < c) ? a[e] : 0.f;
+                        p[e] = (4 * gq + e <= c) ? p[e] : 0.f;
                     }
                 }
+                pt[j] = p;
+                if (i == j) *reinterpret_cast<f32x4*>(&sm.blk[kBlk * i + 16 * c + 4 * gq]) = a;
+                else aR[off_t(i, j)] = a;
             }
-            __syncthreads();
-
-            // diagonal blocks: wave w inverts I + A_ww by forward substitution,
-            // lane j < 16 solving for column j.
-            if (lane < 16) {
-                const int b0 = 16 * wave;
-                float xcol[16];
+            // P fragments of row tile i: (tile 2 kb, tile 2 kb + 1), zero above the diagonal
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-                    for (int s = 0; s < r; ++s) acc -= sm.a[(b0 + r) * SM::lda + b0 + s] * xcol[s];
-                    xcol[r] = acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sm.n[(b0 + r) * SM::lda + b0 + lane] = xcol[r];
+            for (int kb = 0; 2 * kb <= i; ++kb) {
+                const f32x4 lo = pt[2 * kb];
+                const f32x4 hi = 2 * kb + 1 <= i ? pt[2 * kb + 1] : zero4();
+                const int f = tri_frag(i, kb);
+                *reinterpret_cast<Frag*>(rec + RC::pfrag + (f * kWave + lane) * RC::frag_bytes) =
+                    pack_frag<T>(lo, hi);
             }
-            __syncthreads();
-
-            // off-diagonal blocks by block rows: N_iw = -N_ii sum_{k=w}^{i-1} A_ik N_kw
-            for (int i = 1; i < 4; ++i) {
-                if (wave < i) {
-                    const int w = wave;
-                    f32x4 X = zero4();
-                    for (int kk = w; kk < i; ++kk) {
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const float av = sm.a[(16 * i + col) * SM::lda + 16 * kk + 4 * grp + s];
-                            const float bvv = sm.n[(16 * kk + 4 * grp + s) * SM::lda + 16 * w + col];
-                            X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bvv, X, 0, 0, 0);
-                        }
-                    }
-                    f32x4 Y = zero4();
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float av = sm.n[(16 * i + col) * SM::lda + 16 * i + 4 * grp + s];
-                        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, X[s], Y, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sm.n[(16 * i + 4 * grp + e) * SM::lda + 16 * w + col] = -Y[e];
-                }
-                __syncthreads();
-            }
-
-            // T = N diag(beta) and P as A-operand fragments
-            write_frags(rec);
-            __syncthreads();
         }
-        it = nit;
+        wave_lds_sync();
+
+        // ---- diagonal blocks of N = (I + A)^-1 by forward substitution: lane
+        // (c, g) holds row c of -A_gg and solves column c of block g; the
+        // entry -A_gg[r][s] comes from lane r of the same 16-lane row
+        {
+            float arow[16], x[16];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(sm.blk + kBlk * gq + 16 * c + 4 * s4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * s4 + e] = av[e];
+            }
+            subst_rows<0>(arow, x, c);
+            float* Nb = sm.blk + 4 * kBlk + kBlk * gq;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Nb[16 * r + c] = x[r];
+        }
+        wave_lds_sync();
+        f32x4 Rd[4], Od[4];   // R(N_ii), C(N_ii)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float* Nb = sm.blk + 4 * kBlk + kBlk * i;
+            Rd[i] = *reinterpret_cast<const f32x4*>(Nb + 16 * c + 4 * gq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Od[i][e] = Nb[16 * (4 * gq + e) + c];
+        }
+
+        // ---- off-diagonal blocks by block rows: N_iw = N_ii sum_{k=w}^{i-1} (-A_ik) N_kw
+        f32x4 nO[6];    // C(N_iw), i > w
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+#pragma unroll
+            for (int w = 0; w < i; ++w) {
+                f32x4 X = zero4();
+#pragma unroll
+                for (int k = w; k < i; ++k) X = mma16(aR[off_t(i, k)], k == w ? Od[w] : nO[off_t(k, w)], X);
+                nO[off_t(i, w)] = mma16(Rd[i], X, zero4());
+            }
+        }
+        // C -> R through LDS (the diagonal blocks are no longer read)
+#pragma unroll
+        for (int b = 0; b < 6; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.blk[kTrBlk * b + kTrRow * (4 * gq + e) + c] = nO[b][e];
+        wave_lds_sync();
+
+        // ---- T = N diag(beta) fragments: (tile 2 kb, tile 2 kb + 1) of row tile i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 tt[4];
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(&sm.beta[16 * j + 4 * gq]);
+                const f32x4 n = i == j ? Rd[i]
+                                       : *reinterpret_cast<const f32x4*>(&sm.blk[kTrBlk * off_t(i, j) + kTrRow * c + 4 * gq]);
+                tt[j] = n * bs;
+            }
+#pragma unroll
+            for (int kb = 0; 2 * kb <= i; ++kb) {
+                const f32x4 lo = tt[2 * kb];
+                const f32x4 hi = 2 * kb + 1 <= i ? tt[2 * kb + 1] : zero4();
+                const int f = tri_frag(i, kb);
+                *reinterpret_cast<Frag*>(rec + RC::tfrag + (f * kWave + lane) * RC::frag_bytes) =
+                    pack_frag<T>(lo, hi);
+            }
+        }
+        wave_lds_sync();   // the next head rewrites the scratch
     }
 }
 
@@ -476,20 +467,6 @@ __device__ __forceinline__ typename Mma<T>::Frag state_frag(const f32x4& t0, con
     return Mma<T>::acc_frag(lo, hi);
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3). The
-// arguments are wave-uniform; reading them from the first lane keeps the
-// resource in scalar registers.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    void* p = (void*)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                             0x00020000);
-}
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // 64 lanes x 16 bytes from rsrc + voffset (+ soffset) to LDS dst + 16 lane
 __device__ __forceinline__ void dma16(rsrc_t r, unsigned char* dst, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
@@ -1089,27 +1066,6 @@ __device__ __forceinline__ void scan_store(const ScanBuf<T, KD, NW>* __restrict_
     }
 }
 
-// s_waitcnt with only the vector-memory count bounded (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for LDS hand-off only. __syncthreads() also fences global
-// memory, which costs a wait for every outstanding vector-memory operation,
-// including the copies of chunks still meant to be in flight. Here the caller
-// waits for exactly what it needs (wait_vmcnt), this wave's LDS accesses are
-// drained, and the signal fences keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // One workgroup per CU (its LDS buffers take most of the 160 KiB), one wave
 // per SIMD: the compiler may spend registers on latency hiding.
 template <typename T, int KD, int NW, int NBUF>
@@ -1353,21 +1309,13 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         if (e != hipSuccess) return e;
     }
     if (tiles > 0) {
-        const size_t smem = sizeof(PrepSmem<T, KD>);
-        auto kern = chunk_prep_kernel<T, KD>;
-        hipError_t e = set_smem(kern, smem);
-        if (e != hipSuccess) return e;
-        // persistent workgroups (as many as are resident at once), each walking
-        // the (tile, key head) items
+        // one single-wave workgroup per (tile, key head) item
         const int64_t items = tiles * Hk;
-        const int per_cu = kPrepWavesPerEU * 4 / (kPrepThreads / kWave);
-        const int fit = (int)((160 * 1024) / smem);
-        const int64_t cap = 256 * (int64_t)(fit < per_cu ? (fit > 0 ? fit : 1) : per_cu);
-        const int grid = (int)(items < cap ? items : cap);
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrepThreads), smem, stream,
+        auto kern = chunk_prep_kernel<T, KD>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kWave), 0, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
                            Hk, scale, l2norm, w.rec, (int)items);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

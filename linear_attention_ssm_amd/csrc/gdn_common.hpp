@@ -68,6 +68,7 @@ constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppHalfMirror = 0x141; // lane i of each 8 <- lane 7 - i
 constexpr int kDppRowMirror = 0x140;  // lane i of each 16 <- lane 15 - i
+constexpr int kDppRowBcast = 0x150;   // + n (row_newbcast): every lane of each 16 <- lane n of it
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64); every
 // lane of a group ends with the same value.
@@ -167,6 +168,41 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n, i
         if (cu[mid] <= t) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3). The
+// arguments are wave-uniform; reading them from the first lane keeps the
+// resource in scalar registers.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void* p = (void*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
+}
+// s_waitcnt with only the vector-memory count bounded (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-off only. __syncthreads() also fences global
+// memory, which costs a wait for every outstanding vector-memory operation,
+// including the copies of chunks still meant to be in flight. Here the caller
+// waits for exactly what it needs (wait_vmcnt), this wave's LDS accesses are
+// drained, and the signal fences keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 }  // namespace gdn
