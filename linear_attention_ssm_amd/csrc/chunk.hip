@@ -30,17 +30,20 @@
 //               substitution on fp32 MFMA), T, P and the factors a, b, c,
 //               gamma_L. T and P are written as ready MFMA A-operand
 //               fragments (only the 6 non-zero 16 x 32 blocks of each).
-//   chunk_scan  one workgroup per (sequence, value head, 16*NW value columns),
-//               sequential over the sequence's chunks. Each wave owns 16 value
-//               columns of the fp32 state, held in MFMA accumulators for the
+//   chunk_scan  one workgroup per (sequence, value head, group of value
+//               columns), sequential over the sequence's chunks. The fp32
+//               state of each 16-column tile stays in MFMA accumulators for the
 //               whole sequence; accumulator tiles feed the next product
 //               directly as B operands (see gdn_common.hpp), so the chain
 //               h -> K h -> U -> h' never leaves registers. The raw K and Q
-//               tiles and the chunk's record are copied global -> LDS with
-//               direct-to-LDS loads one chunk ahead (double buffer), K^T
-//               operands are read from the row-major K tile with the gfx950
+//               tiles, the values and the chunk's record are copied global ->
+//               LDS with direct-to-LDS loads two chunks ahead (three buffers),
+//               K^T operands are read from the row-major K tile with the gfx950
 //               transposing LDS read, and nothing but the outputs and the
-//               final state is written.
+//               final state is written. bf16 operands with up to two column
+//               tiles per workgroup take the role-split form below (chain,
+//               output and copy waves on separate SIMDs); the fp32 operand
+//               path and wide workgroups share one wave per column tile.
 #include "gdn_common.hpp"
 
 namespace gdn {
@@ -567,7 +570,8 @@ struct ScanArgs {
 // sector, loaded into a per-wave LDS scratch word that nothing reads. By the
 // time a chunk is staged into LDS its data is on chip, which keeps far more of
 // the sequence's HBM traffic in flight than the LDS ring can hold.
-constexpr int kPrefetchSlots = 4;      // prefetch loads per wave per chunk
+constexpr int kPrefetchSlots = 2;      // prefetch loads per wave per chunk
+constexpr int kPfSector = 128;         // bytes per prefetch touch (one L2 line)
 constexpr int kPrefetchAhead = 2;      // chunks beyond the furthest staged one
 
 // Per-wave prefetch plan, fixed for the kernel: slot s reads sector lane of
@@ -580,11 +584,11 @@ struct PrefetchPlan {
     uint32_t off[kPrefetchSlots];      // this lane's byte offset in the chunk's block
     __device__ __forceinline__ void init(const ScanArgs<T, KD, NW>& a, int wu, int nwu) {
         constexpr int ES = (int)sizeof(T);
-        constexpr int kq_sh = __builtin_ctz(KD * ES / 64);     // log2 sectors per K/Q row
+        constexpr int kq_sh = __builtin_ctz(KD * ES / kPfSector);     // log2 sectors per K/Q row
         constexpr int kq_spr = 1 << kq_sh;
-        constexpr int rec_slots = (Rec<T>::bytes / 64 + kWave - 1) / kWave;
+        constexpr int rec_slots = (Rec<T>::bytes / kPfSector + kWave - 1) / kWave;
         // value rows: the unit's V * ES bytes, whole power-of-two sectors only
-        const int v_spr0 = a.V * ES / 64;
+        const int v_spr0 = a.V * ES / kPfSector;
         const int v_sh = v_spr0 > 0 ? 31 - __builtin_clz(v_spr0) : 0;
         const int v_spr = v_spr0 > 0 ? 1 << v_sh : 0;
 #pragma unroll
@@ -599,8 +603,8 @@ struct PrefetchPlan {
             row[i] = t <= 1 ? a.qk_row : t == 2 ? a.v_row : t == 3 ? 0u : ~0u;
             const int sct = sub * kWave + a.lane;
             const int sh = t == 2 ? v_sh : kq_sh;
-            off[i] = t >= 3 ? (uint32_t)sct * 64
-                            : (uint32_t)(sct >> sh) * row[i] + (uint32_t)(sct & ((1 << sh) - 1)) * 64;
+            off[i] = t >= 3 ? (uint32_t)sct * kPfSector
+                            : (uint32_t)(sct >> sh) * row[i] + (uint32_t)(sct & ((1 << sh) - 1)) * kPfSector;
         }
     }
 };
@@ -1236,6 +1240,428 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
     }
 }
 
+// ------------------------------------------------------------ chunk_scan, role-split waves (bf16)
+//
+// One workgroup per (sequence, value head, 16 NT value columns) with NT + 2
+// waves, one per SIMD:
+//   chain t owns the fp32 state of column tile t (16 columns) and runs the
+//           dependent part of a chunk: X = K h, U = T (V - a o X), h' =
+//           gamma_L h + K^T (c o U);
+//   output  forms O^T = b o (h^T Q^T) + U^T P^T for the same columns (the
+//           state and U fragments are A operands as they stand, the raw Q
+//           rows and P fragments B operands) and stores O rows straight from
+//           its accumulators;
+//   copy    issues every direct-to-LDS copy (two chunks ahead, half of a
+//           chunk on each side of the mid-step barrier) and the L2
+//           prefetch, and waits for them.
+// With the work of a column group spread over SIMDs this way, each wave's
+// dependent chain is short and the copy engine is kept busy through the
+// whole step (the copies, not the matrix ops, bound the step at this size).
+// The chain waves hand h (at the end of a step) and U (mid-step) to the output
+// wave through LDS. A chain wave reads a chunk's operands one step ahead,
+// right after the mid-step barrier by which the copy wave has seen it land;
+// the output wave reads its own at the start of the step.
+template <int KD, int NT>
+struct RoleHand {
+    bf16x8 h[KD / 32][NT][kWave];   // h of the step's chunk: B operand per contraction block and tile
+    bf16x8 u[2][NT][kWave];         // U: B operand per 32-row block and tile
+};
+
+template <int KD>
+struct ChainOps {
+    bf16x8 kf[4][KD / 32];      // K rows: A operand of X = K h
+    bf16x8 tf[kTriFrags];       // T
+    f32x4 vv[4];                // values of the wave's tile, accumulator layout
+    f32x4 fa[4], fc[4];         // row factors a and c
+    float gL;                   // gamma_L
+};
+template <int KD, int NT>
+__device__ __forceinline__ void chain_load(ChainOps<KD>& op,
+                                                const ScanBuf<bf16, KD, NT>* __restrict__ buf,
+                                                const ScanLane<bf16, KD, NT>& ln, int t, int grp, int lane)
+{
+    typedef ScanBuf<bf16, KD, NT> SB;
+    typedef Rec<bf16> RC;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < KD / 32; ++kb) op.kf[rt][kb] = ld<bf16x8>(buf->k + ln.rf[kb] + 16 * rt * SB::RB);
+#pragma unroll
+    for (int f = 0; f < kTriFrags; ++f) op.tf[f] = ld<bf16x8>(buf->rec + RC::tfrag + (f * kWave + lane) * RC::frag_bytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const s16x4 raw = lds_read_tr16(buf->v[t] + ln.vtr + i * 16 * SB::VRB);
+        op.vv[i] = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        op.fa[i] = ld<f32x4>(buf->rec + RC::fac + (0 * kChunk + 16 * i + 4 * grp) * 4);
+        op.fc[i] = ld<f32x4>(buf->rec + RC::fac + (2 * kChunk + 16 * i + 4 * grp) * 4);
+    }
+    op.gL = ld<float>(buf->rec + RC::fac + 3 * kChunk * 4);
+}
+
+template <int KD>
+struct OutOps {
+    bf16x8 qf[4][KD / 32];      // Q rows: B operand of h^T Q^T
+    bf16x8 pf[kTriFrags];       // P rows: B operand of U^T P^T
+    float fb[4];                // b of chunk row 16 rt + (lane & 15)
+};
+template <int KD, int NT>
+__device__ __forceinline__ void out_load(OutOps<KD>& op,
+                                              const ScanBuf<bf16, KD, NT>* __restrict__ buf,
+                                              const ScanLane<bf16, KD, NT>& ln, int col, int lane)
+{
+    typedef ScanBuf<bf16, KD, NT> SB;
+    typedef Rec<bf16> RC;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < KD / 32; ++kb) op.qf[rt][kb] = ld<bf16x8>(buf->q + ln.rf[kb] + 16 * rt * SB::RB);
+#pragma unroll
+    for (int f = 0; f < kTriFrags; ++f) op.pf[f] = ld<bf16x8>(buf->rec + RC::pfrag + (f * kWave + lane) * RC::frag_bytes);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) op.fb[rt] = ld<float>(buf->rec + RC::fac + (1 * kChunk + 16 * rt + col) * 4);
+}
+
+// One chunk of chain wave t. `hf` holds h as B operand (made when h was
+// last updated) and `op` the chunk's operands; both turn over to the next
+// chunk (its operands read from `ahead`).
+template <int KD, int NT>
+__device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restrict__ cur,
+                                           const ScanBuf<bf16, KD, NT>* __restrict__ ahead,
+                                           RoleHand<KD, NT>* __restrict__ hand,
+                                           const ScanLane<bf16, KD, NT>& ln, int t, int grp, int col,
+                                           f32x4 (&hs)[KD / 16], bf16x8 (&hf)[KD / 32],
+                                           ChainOps<KD>& op)
+{
+    typedef Mma<bf16> MT;
+    typedef bf16x8 Frag;
+    typedef ScanBuf<bf16, KD, NT> SB;
+    constexpr int KB = KD / 32;
+    constexpr int RT = KD / 16;
+    const int lane = 16 * grp + col;
+    const unsigned char* kt = cur->k;
+
+    // K^T operands of this chunk, used once U is known
+    Frag ktf[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const unsigned char* p = kt + ln.tf[rt & 1][rt >> 1] + 32 * half * SB::RB;
+            const s16x4 lo = lds_read_tr16(p);
+            const s16x4 hi = lds_read_tr16(p + 16 * SB::RB);
+            ktf[rt][half] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+
+    // ---- X = K h (row tiles interleaved), U = T (V - a o X)
+    f32x4 X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) X[rt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) X[rt] = MT::mma(op.kf[rt][kb], hf[kb], X[rt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) hs[rt] *= op.gL;   // decayed state: accumulator of the update
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) X[rt] = op.vv[rt] - op.fa[rt] * X[rt];
+    f32x4 U[4];
+    {
+        const Frag vf0 = MT::acc_frag(X[0], X[1]);
+        const Frag vf1 = MT::acc_frag(X[2], X[3]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) U[rt] = MT::mma(op.tf[tri_frag(rt, 0)], vf0, zero4());
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) U[rt] = MT::mma(op.tf[tri_frag(rt, 1)], vf1, U[rt]);
+    }
+    hand->u[0][t][lane] = MT::acc_frag(U[0], U[1]);
+    hand->u[1][t][lane] = MT::acc_frag(U[2], U[3]);
+    f32x4 fc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) fc[rt] = op.fc[rt];
+    lds_barrier();   // U is visible to the output wave; the next chunk has landed
+
+    // ---- the next chunk's operands, then h' = gamma_L h + K^T (c o U)
+    chain_load<KD, NT>(op, ahead, ln, t, grp, lane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) U[rt] *= fc[rt];
+    const Frag df0 = MT::acc_frag(U[0], U[1]);
+    const Frag df1 = MT::acc_frag(U[2], U[3]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) hs[rt] = MT::mma(ktf[rt][half], half ? df1 : df0, hs[rt]);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        hf[kb] = state_frag<bf16>(hs[2 * kb], hs[2 * kb + 1], grp);
+        hand->h[kb][t][lane] = hf[kb];
+    }
+}
+
+// One chunk of the output wave: O^T tiles (lane: chunk row 16 rt + c, value
+// columns 16 t + 4 g .. + 3) stored straight to global memory.
+template <int KD, int NT>
+__device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restrict__ cur,
+                                            const RoleHand<KD, NT>* __restrict__ hand,
+                                            const ScanLane<bf16, KD, NT>& ln, int grp, int col,
+                                            OutOps<KD>& op, rsrc_t ro, uint32_t o_row)
+{
+    typedef Mma<bf16> MT;
+    typedef bf16x8 Frag;
+    constexpr int KB = KD / 32;
+    const int lane = 16 * grp + col;
+
+    Frag hf[NT][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) hf[t][kb] = hand->h[kb][t][lane];
+    out_load<KD, NT>(op, cur, ln, col, lane);
+    // ---- h^T Q^T, scaled by b per chunk row
+    f32x4 O[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[t][rt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) O[t][rt] = MT::mma(hf[t][kb], op.qf[rt][kb], O[t][rt]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[t][rt] *= op.fb[rt];
+    lds_barrier();   // U has been written; the next chunk has landed
+
+    // ---- + U^T P^T, then the next chunk's operands and the stores
+    Frag uf[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        uf[t][0] = hand->u[0][t][lane];
+        uf[t][1] = hand->u[1][t][lane];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            O[t][rt] = MT::mma(uf[t][0], op.pf[tri_frag(rt, 0)], O[t][rt]);
+            if (rt >= 2) O[t][rt] = MT::mma(uf[t][1], op.pf[tri_frag(rt, 1)], O[t][rt]);
+            const bf16x4 ob = __builtin_convertvector(O[t][rt], bf16x4);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
+                                                  (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
+        }
+}
+
+template <int KD, int NT, int NBUF>
+__global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_roles_kernel(
+    const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
+    const bf16* __restrict__ vp, int64_t v_stride,
+    const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
+    const unsigned char* __restrict__ ws_rec,
+    int T_len, int H, int Hk, int V, int units, int groups)
+{
+    typedef bf16 T;
+    typedef ScanBuf<T, KD, NT> SB;
+    typedef ScanLane<T, KD, NT> LN;
+    typedef RoleHand<KD, NT> HD;
+    static_assert(NBUF == 3, "two chunks in flight");
+    constexpr int ES = SB::ES;
+    constexpr int RT = KD / 16;
+    constexpr int TP = SB::tile_pieces;
+    constexpr int RP = SB::rec_pieces;
+    constexpr int loads = 2 * TP + RP + NT * SB::v_pieces;   // copies per chunk
+    static_assert(loads + 2 * kPrefetchSlots < 64, "a step's loads fit the vector-memory counter");
+    extern __shared__ __align__(1024) unsigned char smem_raw[];
+    SB* bufs = reinterpret_cast<SB*>(smem_raw);
+    unsigned char* scratch = smem_raw + NBUF * sizeof(SB);
+    HD* hand = reinterpret_cast<HD*>(smem_raw + NBUF * sizeof(SB) + 256);
+
+    // XCD-aware block order: all column groups of one (seq, head) unit get the
+    // same blockIdx % 8, i.e. run on the same XCD and share its L2.
+    const int bid = blockIdx.x;
+    const int rest = bid >> 3;
+    const int cgrp = rest % groups;
+    const int u = (rest / groups) * 8 + (bid & 7);
+    if (u >= units) return;
+    const int seq = u / H;
+    const int h = u - seq * H;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    // waves 0 .. NT - 1: chain of column tile `role`; NT: output; NT + 1: copy
+    const int role = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    ScanArgs<T, KD, NT> a;
+    a.qp = qp; a.kp = kp; a.qk_stride = qk_stride; a.vp = vp; a.v_stride = v_stride; a.op = o;
+    a.ws_rec = ws_rec; a.H = H; a.V = V; a.h = h; a.hk = h / (H / Hk); a.wave = 0; a.lane = lane;
+    a.c0 = cgrp * NT * 16;                       // the workgroup's first value column
+    if (cu) {
+        a.tok_begin = cu[seq];
+        a.tok_end = cu[seq + 1];
+        a.tile0 = offsets[seq];
+    } else {
+        a.tok_begin = seq * T_len;
+        a.tok_end = a.tok_begin + T_len;
+        a.tile0 = seq * ((T_len + kChunk - 1) / kChunk);
+    }
+    const int nchunks = (a.tok_end - a.tok_begin + kChunk - 1) / kChunk;
+    a.nchunks = nchunks;
+    a.qk_row = (uint32_t)(qk_stride * ES);
+    a.v_row = (uint32_t)(v_stride * ES);
+    a.k0 = (uint64_t)(kp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
+    a.q0 = (uint64_t)(qp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
+    a.v0 = (uint64_t)(vp + (int64_t)a.tok_begin * v_stride + h * V);
+    a.r0 = (uint64_t)(ws_rec + ((int64_t)a.tile0 * H + h) * Rec<T>::bytes);
+
+    // operand offsets (chain and output waves)
+    LN ln;
+#pragma unroll
+    for (int kb = 0; kb < LN::KB; ++kb) {
+        ln.rf[kb] = (uint32_t)tile_off<T, KD, NT>(col, 32 * kb + 8 * grp);
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            ln.tf[par][kb] = (uint32_t)tile_off<T, KD, NT>(4 * grp + (col >> 2), state_row(2 * kb + par, col & 3, 0));
+    }
+    ln.vtr = (uint32_t)((4 * grp + (col >> 2)) * SB::VRB + (col & 3) * 8);
+
+    // A partial last chunk leaves the rows past the sequence unfetched: start
+    // them at zero so they hold finite values (their factors are zero).
+    if ((a.tok_end - a.tok_begin) % kChunk != 0) {
+        const f32x4 z = zero4();
+        for (int i = threadIdx.x * 16; i < NBUF * (int)sizeof(SB); i += (NT + 2) * kWave * 16)
+            *reinterpret_cast<f32x4*>(smem_raw + i) = z;
+        lds_barrier();
+    }
+
+    if (role < NT) {
+        // ---------------- chain of column tile t
+        const int t = role;
+        const int vc = a.c0 + 16 * t + col;
+        f32x4 hs[RT];
+        const int64_t sbase = ((int64_t)seq * H + h) * KD * V;
+        if (S0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hs[rt][e] = S0[sbase + (int64_t)state_row(rt, grp, e) * V + vc];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) hs[rt] = zero4();
+        }
+        bf16x8 hf[LN::KB];
+#pragma unroll
+        for (int kb = 0; kb < LN::KB; ++kb) {
+            hf[kb] = state_frag<T>(hs[2 * kb], hs[2 * kb + 1], grp);
+            hand->h[kb][t][lane] = hf[kb];
+        }
+        lds_barrier();
+        ChainOps<KD> op;
+        chain_load<KD, NT>(op, &bufs[0], ln, t, grp, lane);
+        int b = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int bn = b == NBUF - 1 ? 0 : b + 1;
+            role_chain<KD, NT>(&bufs[b], &bufs[bn], hand, ln, t, grp, col, hs, hf, op);
+            lds_barrier();
+            b = bn;
+        }
+        if (Sfin) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sfin[sbase + (int64_t)state_row(rt, grp, e) * V + vc] = hs[rt][e];
+        }
+    } else if (role == NT) {
+        // ---------------- output
+        const int64_t HV = (int64_t)H * V;
+        const uint32_t o_row = (uint32_t)(HV * ES);
+        lds_barrier();
+        OutOps<KD> op;
+        int b = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int bn = b == NBUF - 1 ? 0 : b + 1;
+            const int tok0 = a.tok_begin + c * kChunk;
+            const int L = min(kChunk, a.tok_end - tok0);
+            const rsrc_t ro = make_rsrc(o + (int64_t)tok0 * HV + (int64_t)h * V + a.c0, (uint32_t)L * o_row);
+            role_output<KD, NT>(&bufs[b], hand, ln, grp, col, op, ro, o_row);
+            lds_barrier();
+            b = bn;
+        }
+    } else {
+        // ---------------- copy
+        uint32_t tsrc[TP];
+#pragma unroll
+        for (int j = 0; j < TP; ++j) {
+            const int row = j * SB::RPI + lane / SB::SPR;
+            const int s = (lane % SB::SPR) ^ tile_mask<T, KD, NT>(row);
+            tsrc[j] = (uint32_t)(row * (int64_t)a.qk_row + s * 16);
+        }
+        uint32_t vsrc[SB::v_pieces];
+#pragma unroll
+        for (int p = 0; p < SB::v_pieces; ++p)
+            vsrc[p] = (uint32_t)((p * SB::RPV + lane / SB::LPR) * a.v_row + (lane % SB::LPR) * 16);
+        PrefetchPlan<T, KD, NT> plan;
+        plan.init(a, cgrp, groups);
+        // A chunk's copies go out in two parts, one on each side of the
+        // mid-step barrier, so that the copy engine works through the whole
+        // step: part A (the K tile, the values and the prefetch of chunk cp)
+        // and part B (the Q tile and the record).
+        constexpr int partA = TP + NT * SB::v_pieces + kPrefetchSlots;
+        auto issue_a = [&](int cs, int cp, SB* __restrict__ dst) {
+            const ChunkSpan sp = chunk_span<T, KD, NT>(cs, a, a.c0);
+            const rsrc_t rk = make_rsrc((const void*)sp.k, sp.kq_bytes);
+            const rsrc_t rv = make_rsrc((const void*)sp.v, sp.v_bytes);
+#pragma unroll
+            for (int j = 0; j < TP; ++j) dma16(rk, dst->k + j * 1024, tsrc[j], 0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int p = 0; p < SB::v_pieces; ++p) dma16(rv, dst->v[t] + p * 1024, vsrc[p], t * 16 * ES);
+            const bool pvalid = cp < nchunks;
+            const int pc = pvalid ? cp : 0;
+            const uint32_t pL = pvalid ? (uint32_t)min(kChunk, a.tok_end - (a.tok_begin + cp * kChunk)) : 0u;
+#pragma unroll
+            for (int i = 0; i < kPrefetchSlots; ++i) {
+                const uint32_t rb = plan.row[i];
+                const uint32_t bytes = !pvalid || rb == ~0u ? 0u : rb == 0u ? (uint32_t)Rec<T>::bytes : pL * rb;
+                const rsrc_t pr = make_rsrc((const void*)(plan.base[i] + (uint64_t)pc * plan.step[i]), bytes);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)scratch, 4, plan.off[i], 0, 0, 0);
+            }
+        };
+        auto issue_b = [&](int cs, SB* __restrict__ dst) {
+            const ChunkSpan sp = chunk_span<T, KD, NT>(cs, a, a.c0);
+            const rsrc_t rq = make_rsrc((const void*)sp.q, sp.kq_bytes);
+            const rsrc_t rr = make_rsrc((const void*)sp.r, sp.r_bytes);
+#pragma unroll
+            for (int j = 0; j < TP; ++j) dma16(rq, dst->q + j * 1024, tsrc[j], 0);
+#pragma unroll
+            for (int j = 0; j < RP; ++j) dma16(rr, dst->rec + j * 1024, lane * 16, j * 1024);
+        };
+        issue_a(0, NBUF - 1, &bufs[0]);
+        issue_b(0, &bufs[0]);
+        issue_a(1, NBUF, &bufs[1]);
+        issue_b(1, &bufs[1]);
+        wait_vmcnt<loads + kPrefetchSlots>();   // chunk 0 has landed (younger: chunk 1's copies)
+        lds_barrier();
+        int b = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int bp = b == 0 ? NBUF - 1 : b - 1;
+            issue_a(c + NBUF - 1, c + NBUF - 1 + kPrefetchAhead, &bufs[bp]);
+            wait_vmcnt<partA>();   // chunk c + 1 has landed (younger: this step's part A)
+            lds_barrier();         // mid-step
+            issue_b(c + NBUF - 1, &bufs[bp]);
+            lds_barrier();         // end of step
+            b = b == NBUF - 1 ? 0 : b + 1;
+        }
+        wait_vmcnt<0>();   // no copy into LDS may outlive the workgroup
+    }
+}
+
 // ------------------------------------------------------------ launchers
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1279,6 +1705,29 @@ static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const v
     hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3(NW * kWave), smem, stream,
                        (const T*)q, (const T*)k, qks, (const T*)v, vs, S0, Sf, (T*)o, cu, offsets,
                        wsrec, T_len, H, Hk, V, units, groups);
+    return hipGetLastError();
+}
+
+template <int KD, int NT>
+static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, const void* v,
+                                   int64_t vs, const float* S0, float* Sf, void* o,
+                                   const int32_t* cu, const int32_t* offsets,
+                                   const unsigned char* wsrec, int T_len, int H, int Hk, int V,
+                                   int N, hipStream_t stream)
+{
+    const int units = N * H;
+    const int groups = V / (16 * NT);
+    const int upad = (units + 7) / 8 * 8;
+    typedef ScanBuf<bf16, KD, NT> SB;
+    constexpr int NBUF = 3;
+    constexpr size_t smem = NBUF * sizeof(SB) + 256 + sizeof(RoleHand<KD, NT>);
+    static_assert(smem <= 160 * 1024, "scan staging fits in LDS");
+    auto kern = chunk_scan_roles_kernel<KD, NT, NBUF>;
+    hipError_t err = set_smem(kern, smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3((NT + 2) * kWave), smem, stream,
+                       (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf, (bf16*)o,
+                       cu, offsets, wsrec, T_len, H, Hk, V, units, groups);
     return hipGetLastError();
 }
 
@@ -1338,6 +1787,13 @@ static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const
     else if (units * (slabs / 2) >= 256 && slabs % 2 == 0) nw = 2;
     if (nw == 4)
         return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
+    // bf16 operands with one or two column groups per workgroup: the split-role
+    // step, which puts a second wave on each column group
+    if constexpr (sizeof(T) == 2) {
+        if (nw == 2)
+            return launch_scan_roles<KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
+        return launch_scan_roles<KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
+    }
     // the fp32 operand path (small parity workloads) runs with 1 or 4 waves per
     // workgroup only: its 2-wave instance does not get through the gfx950 backend
     if constexpr (sizeof(T) == 2) {

@@ -172,6 +172,7 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n, i
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3). The
 // arguments are wave-uniform; reading them from the first lane keeps the
