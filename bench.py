@@ -38,7 +38,7 @@ KERNELS = {   # bench op -> (kernel symbol stem, source file)
     "conv1d": ("conv1d_causal_kernel", CSRC + "conv1d.hip"),
     "gate_prepare": ("gate_prepare_kernel", CSRC + "gate.hip"),
     "chunk_prepare": ("chunk_prep_kernel", CSRC + "chunk.hip"),
-    "chunk_scan": ("chunk_scan_kernel", CSRC + "chunk.hip"),
+    "chunk_scan": ("chunk_scan_roles_kernel", CSRC + "chunk.hip"),
     "decode": ("gdp_decode_kernel", CSRC + "decode.hip"),
 }
 REC_BYTES_BF16 = 2 * 6 * 64 * 16 + 4 * 64 * 4   # per (chunk, value head) workspace record

@@ -236,10 +236,14 @@ void chunk_prep_kernel(
     constexpr int ES = (int)sizeof(T);
     __shared__ __align__(16) PrepLds sm;
 
-    const int it = blockIdx.x;
+    // XCD-aware order: the key heads of one tile run on the same XCD (blockIdx
+    // % 8) one after another, so the tile's gate rows are fetched into that
+    // XCD's L2 once
+    const int bx = blockIdx.x >> 3;
+    const int tile = (bx / Hk) * 8 + (blockIdx.x & 7);
+    const int hk = bx - (bx / Hk) * Hk;
+    const int it = tile * Hk + hk;
     if (it >= n_items) return;
-    const int tile = it / Hk;
-    const int hk = it - tile * Hk;
     ChunkLoc loc;
     if (!locate_tile(tile, cu, offsets, n_seqs, T_len, loc)) return;   // packed: past the last chunk
     const int L = loc.L;
@@ -1758,10 +1762,12 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         if (e != hipSuccess) return e;
     }
     if (tiles > 0) {
-        // one single-wave workgroup per (tile, key head) item
+        // one single-wave workgroup per (tile, key head) item (tiles padded to
+        // a multiple of the 8 XCDs)
         const int64_t items = tiles * Hk;
+        const int64_t blocks = (tiles + 7) / 8 * 8 * Hk;
         auto kern = chunk_prep_kernel<T, KD>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kWave), 0, stream,
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWave), 0, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
                            Hk, scale, l2norm, w.rec, (int)items);
         hipError_t e = hipGetLastError();
