@@ -62,6 +62,9 @@ def _load():
         lib.oracle_gated_delta_rule.argtypes = (
             [_dp] * 8 + [_ip] + [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int])
         lib.oracle_gdp_decode_prepare.argtypes = [_dp] * 9 + [ctypes.c_int] * 6
+        lib.oracle_conv1d_update.argtypes = [_dp, _dp, _ip, _dp, _dp, _dp] + [ctypes.c_int] * 5
+        lib.oracle_gdp_prefill.argtypes = ([_dp] * 6 + [_ip] + [ctypes.c_int] * 8
+                                           + [ctypes.c_double, ctypes.c_int])
         lib.oracle_gdp_decode.argtypes = (
             [_dp] * 6 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int])
         _lib = lib
@@ -186,4 +189,45 @@ def gdp_decode(x, ba, A_log, dt_bias, state, M, H, G, P, N, scale=1.0, l2norm=Tr
     o = np.empty((n, H, P))
     lib.oracle_gdp_decode(_ptr(x), _ptr(ba), _ptr(A_log), _ptr(dt_bias), _ptr(st), _ptr(o),
                           n, M, H, G, P, N, float(scale), int(bool(l2norm)))
+    return o, st
+
+
+def conv1d_update(x, conv_state, slot, w, bias=None, silu=True):
+    """One decode token's short conv per request. x: [n, C]; conv_state:
+    [S, W-1, C] (not modified; the updated state is returned); slot: [n] ints
+    (outside [0, S): zero output, no update). Returns (y [n, C], new_state)."""
+    lib = _load()
+    x = _f64(x)
+    w = _f64(w)
+    n, C = x.shape
+    W = w.shape[1]
+    st = np.array(conv_state, dtype=np.float64, order="C", copy=True)
+    assert st.shape[1:] == (W - 1, C) and w.shape == (C, W)
+    sl = np.ascontiguousarray(np.asarray(slot, dtype=np.int32))
+    assert sl.shape == (n,)
+    b = None if bias is None else _f64(bias)
+    y = np.empty((n, C), np.float64)
+    lib.oracle_conv1d_update(_ptr(x), _ptr(st), sl.ctypes.data_as(_ip), _ptr(w), _ptr(b), _ptr(y),
+                             n, st.shape[0], C, W, int(bool(silu)))
+    return y, st
+
+
+def gdp_prefill(x, ba, A_log, dt_bias, M, H, G, P, N, S0=None, cu_seqlens=None, scale=1.0,
+                l2norm=True):
+    """Gated DeltaProduct prefill, token by token. x: [B, T, row]; ba: [B, T, M*H+H];
+    S0: [N_seq, H, N, P] or None. Returns (o [B, T, H, P], S_final)."""
+    lib = _load()
+    x = _f64(x)
+    ba = _f64(ba)
+    B, T, row = x.shape
+    assert row == M * H * P + M * G * N + G * N and ba.shape == (B, T, M * H + H)
+    cu, cup, ns = _cu(cu_seqlens)
+    nseq = ns if cu is not None else B
+    if cu is not None:
+        assert B == 1 and cu[0] == 0 and cu[-1] == T
+    st = np.zeros((nseq, H, N, P)) if S0 is None else np.array(S0, dtype=np.float64, order="C", copy=True)
+    assert st.shape == (nseq, H, N, P)
+    o = np.empty((B, T, H, P), np.float64)
+    lib.oracle_gdp_prefill(_ptr(x), _ptr(ba), _ptr(_f64(A_log)), _ptr(_f64(dt_bias)), _ptr(st),
+                           _ptr(o), cup, ns, B, T, M, H, G, P, N, float(scale), int(bool(l2norm)))
     return o, st

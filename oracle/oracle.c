@@ -306,3 +306,65 @@ void oracle_gdp_decode(const double* x, const double* ba, const double* A_log,
     }
     free(qo); free(ko); free(vo); free(bo); free(go);
 }
+
+/* ------------------------------------------------------- decode short conv */
+
+/* The short-conv update of one decode token per request, the step [GDP]'s
+ * module introduction places before the decode preparation, with its padding
+ * rule (a -1 slot zeroes the request's output). The convolution is [ZZ] item
+ * 1's, evaluated at the newest token of a window held per slot:
+ *   state [n_slots][W-1][C]: row j is the input W-1-j tokens back;
+ *   y[r][c] = act(bias[c] + sum_{j<W-1} w[c][j] state[s][j][c] + w[c][W-1] x[r][c]);
+ *   then the slot's rows shift one token and x[r] becomes the newest row.
+ * A slot outside [0, n_slots) (-1 marks padding) gives a zero row and no
+ * update. Requests are independent (distinct slots). */
+void oracle_conv1d_update(const double* x, double* state, const int32_t* slot,
+                          const double* w, const double* bias, double* y,
+                          int n, int n_slots, int C, int W, int silu)
+{
+    for (long r = 0; r < n; ++r) {
+        int s = slot[r];
+        if (s < 0 || s >= n_slots) {
+            for (int c = 0; c < C; ++c) y[r * C + c] = 0.0;
+            continue;
+        }
+        double* st = state + (long)s * (W - 1) * C;
+        for (int c = 0; c < C; ++c) {
+            double acc = bias ? bias[c] : 0.0;
+            for (int j = 0; j < W - 1; ++j) acc += w[(long)c * W + j] * st[(long)j * C + c];
+            acc += w[(long)c * W + W - 1] * x[r * C + c];
+            y[r * C + c] = silu ? acc / (1.0 + exp(-acc)) : acc;
+        }
+        for (int j = 0; j + 1 < W - 1; ++j)
+            for (int c = 0; c < C; ++c) st[(long)j * C + c] = st[(long)(j + 1) * C + c];
+        for (int c = 0; c < C; ++c) st[(long)(W - 2) * C + c] = x[r * C + c];
+    }
+}
+
+/* ------------------------------------------------- Gated DeltaProduct prefill */
+
+/* A Gated DeltaProduct layer over a whole prefill, by its definition: every
+ * token of a sequence is one decode step of oracle_gdp_decode (the M
+ * Householder copies as an M-step sequence, [GDP] module introduction and
+ * "gdp_decode_prepare"), with the state carried from token to token.
+ *   x [rows][M*H*P + M*G*N + G*N], ba [rows][M*H + H]: token t of batch b is
+ *   row b*T + t (packed: B == 1, sequences by cu_seqlens);
+ *   state [n_seq][H][N][P]: the initial state on entry, the final on return;
+ *   o [rows][H][P]. */
+void oracle_gdp_prefill(const double* x, const double* ba, const double* A_log,
+                        const double* dt_bias, double* state, double* o,
+                        const int32_t* cu_seqlens, int n_seqs, int B, int T, int M, int H,
+                        int G, int P, int N, double scale, int l2norm)
+{
+    long row = (long)M * H * P + (long)M * G * N + (long)G * N;
+    long barow = (long)M * H + H;
+    int nseq = cu_seqlens ? n_seqs : B;
+    for (int s = 0; s < nseq; ++s) {
+        long t0 = cu_seqlens ? cu_seqlens[s] : (long)s * T;
+        long t1 = cu_seqlens ? cu_seqlens[s + 1] : (long)(s + 1) * T;
+        double* st = state + (long)s * H * N * P;
+        for (long t = t0; t < t1; ++t)
+            oracle_gdp_decode(x + t * row, ba + t * barow, A_log, dt_bias, st, o + t * H * P,
+                              1, M, H, G, P, N, scale, l2norm);
+    }
+}

@@ -441,3 +441,97 @@ def test_decode_second_copy_with_zero_beta_equals_one_copy():
     o1, s1 = oracle.gdp_decode(x1, ba1, A_log, dt_bias, st0, 1, H, G, P, N)
     np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(s2, s1, rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------- decode short-conv update
+
+def test_conv_update_token_by_token_equals_prefill_conv():
+    # Fed one token at a time from a zero window, the update is the prefill
+    # convolution (same taps, zero padding at the start), here with a bias.
+    rng = np.random.default_rng(11)
+    T, C, W = 9, 12, 4
+    x = rng.standard_normal((1, T, C))
+    w = rng.standard_normal((C, W))
+    bias = rng.standard_normal(C)
+    ref = oracle.conv1d_causal(x, w, bias=bias, silu=True)[0]
+    st = np.zeros((2, W - 1, C))
+    for t in range(T):
+        y, st = oracle.conv1d_update(x[0, t:t + 1], st, [1], w, bias=bias, silu=True)
+        np.testing.assert_allclose(y[0], ref[t], rtol=1e-14, atol=1e-15)
+    assert (st[0] == 0).all()                               # the other slot is untouched
+    np.testing.assert_array_equal(st[1], x[0, T - (W - 1):])  # the window holds the last W-1 inputs
+
+
+def test_conv_update_window_is_the_last_inputs_and_padding_zeroes():
+    # Hand example, W = 4, one channel: y = w0 s0 + w1 s1 + w2 s2 + w3 x.
+    w = np.array([[2.0, -1.0, 3.0, 0.5]])
+    st = np.array([[[1.0], [2.0], [-4.0]], [[7.0], [8.0], [9.0]]])   # slots 0, 1
+    y, st2 = oracle.conv1d_update(np.array([[6.0], [5.0]]), st, [0, -1], w, silu=False)
+    assert y[0, 0] == 2 * 1 - 1 * 2 + 3 * (-4) + 0.5 * 6      # = -9
+    assert y[1, 0] == 0.0                                   # padding request: zero row
+    np.testing.assert_array_equal(st2[0, :, 0], [2.0, -4.0, 6.0])
+    np.testing.assert_array_equal(st2[1], st[1])            # padding leaves every slot alone
+    ys, _ = oracle.conv1d_update(np.array([[6.0]]), st, [0], w, silu=True)
+    assert ys[0, 0] == pytest.approx(-9.0 / (1.0 + np.exp(9.0)), rel=1e-15)
+
+
+# ------------------------------------------------ Gated DeltaProduct prefill
+
+def _gdp_prefill_case(B, T, M, H, G, P, N, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, T, M * H * P + M * G * N + G * N))
+    ba = rng.standard_normal((B, T, M * H + H))
+    A_log = np.log(rng.uniform(1, 16, H))
+    dt_bias = rng.normal(0, 0.1, H)
+    S0 = rng.standard_normal((B, H, N, P)) * 0.05
+    return x, ba, A_log, dt_bias, S0
+
+
+def _interleave(x, ba, A_log, dt_bias, M, H, G, P, N):
+    """The M*T-position sequence of the GDP prefill, built by explicit indexing
+    (row t*M + m = copy m of token t; query on copy M-1, decay on copy 0)."""
+    B, T, _ = x.shape
+    q = np.zeros((B, M * T, G, N)); k = np.zeros((B, M * T, G, N)); v = np.zeros((B, M * T, H, P))
+    g = np.zeros((B, M * T, H)); beta = np.zeros((B, M * T, H))
+    kb, qb = M * H * P, M * H * P + M * G * N
+    for t in range(T):
+        for m in range(M):
+            p = t * M + m
+            v[:, p] = x[:, t, m * H * P:(m + 1) * H * P].reshape(B, H, P)
+            k[:, p] = x[:, t, kb + m * G * N:kb + (m + 1) * G * N].reshape(B, G, N)
+            if m == M - 1:
+                q[:, p] = x[:, t, qb:qb + G * N].reshape(B, G, N)
+            beta[:, p] = expit(ba[:, t, m * H:(m + 1) * H])
+            if m == 0:
+                xa = ba[:, t, M * H:] + dt_bias
+                g[:, p] = -np.exp(A_log) * np.where(xa > 20, xa, np.logaddexp(0, xa))
+    return q, k, v, g, beta
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_gdp_prefill_equals_recurrence_over_interleaved_sequence(M):
+    # The token-by-token GDP layer is the gated delta rule (pinned above by
+    # closed forms and brute force) over the interleaved M*T sequence, with
+    # token t's output at position t*M + M-1 and the same final state.
+    B, T, H, G, P, N = 2, 7, 4, 2, 5, 6
+    x, ba, A_log, dt_bias, S0 = _gdp_prefill_case(B, T, M, H, G, P, N, seed=20 + M)
+    o, sf = oracle.gdp_prefill(x, ba, A_log, dt_bias, M, H, G, P, N, S0=S0, scale=0.8)
+    q, k, v, g, beta = _interleave(x, ba, A_log, dt_bias, M, H, G, P, N)
+    o2, sf2 = oracle.gated_delta_rule(q, k, v, g, beta, S0=S0, scale=0.8)
+    np.testing.assert_allclose(o, o2[:, M - 1::M], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sf, sf2, rtol=1e-12, atol=1e-14)
+    # positions before the last copy carry a zero query: exactly zero output
+    for m in range(M - 1):
+        assert (o2[:, m::M] == 0).all()
+
+
+def test_gdp_prefill_packed_sequences_reset_state():
+    M, H, G, P, N = 2, 2, 1, 4, 4
+    cu = [0, 3, 8]
+    x, ba, A_log, dt_bias, _ = _gdp_prefill_case(1, 8, M, H, G, P, N, seed=31)
+    o, sf = oracle.gdp_prefill(x, ba, A_log, dt_bias, M, H, G, P, N, cu_seqlens=cu)
+    for s in range(2):
+        a, b = cu[s], cu[s + 1]
+        o1, sf1 = oracle.gdp_prefill(x[:, a:b], ba[:, a:b], A_log, dt_bias, M, H, G, P, N)
+        np.testing.assert_allclose(o[:, a:b], o1, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(sf[s], sf1[0], rtol=1e-13, atol=1e-15)
