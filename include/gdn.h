@@ -3,8 +3,10 @@
  *
  * Four operations make the hot path of a Gated DeltaNet / Gated DeltaProduct
  * mixer: the short causal convolution, the gate preparation, the chunked
- * prefill forward and the one-token recurrent decode. Sources (web pages,
- * cited by title and section):
+ * prefill forward and the one-token recurrent decode. Around them: the
+ * decode-step short-conv update, the decode preparation exported on its own,
+ * and the interleave that runs a Gated DeltaProduct prefill through the
+ * chunked forward. Sources (web pages, cited by title and section):
  *   [ZZ]  "ZzCompute", PyTorch Helion Hackathon gallery entry, items 1-4.
  *   [GDP] Megatron-Core API docs, "core.ssm.ops.gdp.decode_prepare".
  *
@@ -202,6 +204,93 @@ int gdn_recurrent_decode(const void* x, int64_t x_stride_n,
                          float* state, void* o,
                          int n, int M, int H, int G, int P, int N,
                          float scale, int qk_l2norm, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_decode_prepare -- [GDP] "gdp_decode_prepare": the five tensors one
+ * decode step's recurrent update consumes, from the post-conv row and the
+ * ba slice (the preparation gdn_recurrent_decode performs internally,
+ * exported on its own).
+ *   x, ba, A_log, dt_bias   as for gdn_recurrent_decode.
+ *   q, k     [n, M, H, N] in `dtype`, contiguous: q is the query of group
+ *            h / (H/G) on copy M-1 and zero on earlier copies; k is copy m's
+ *            key of group h / (H/G). Plain copies: bit-identical to x.
+ *   v        [n, M, H, P] in `dtype`, contiguous: copy m's value of head h.
+ *   beta, g  [n, M, H] fp32, contiguous: beta = sigmoid(b[m][h]); g =
+ *            -exp(A_log[h]) * softplus(a[h] + dt_bias[h]) on copy 0 and 0 on
+ *            later copies (softplus the identity above 20). The same fp32
+ *            formulas as gdn_gate_prepare and gdn_recurrent_decode.
+ *   P, N     64 or 128. H % G == 0.
+ * Errors: NULL pointer, n < 0, M < 1, H % G != 0, short strides, outputs
+ * sharing memory -> GDN_EINVAL; P, N, dtype, alignment (x, its row stride,
+ * q, k, v) -> GDN_EUNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+int gdn_decode_prepare(const void* x, int64_t x_stride_n,
+                       const void* ba, int64_t ba_stride_n,
+                       const float* A_log, const float* dt_bias,
+                       void* q, void* k, void* v, float* beta, float* g,
+                       int n, int M, int H, int G, int P, int N, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_conv1d_update -- the short-conv update of one decode token per
+ * request, the step [GDP] places before the decode preparation, with its
+ * padding rule (a -1 slot zeroes the request's output).
+ *   x          [n, C] in `dtype`: this token's pre-conv row of each request
+ *              (row r at x + r*x_stride_n).
+ *   conv_state [n_slots, W-1, C] in `dtype`, contiguous, updated IN PLACE:
+ *              row j of a slot holds the input W-1-j tokens back (row W-2 is
+ *              the latest), zero for a fresh sequence.
+ *   slot       [n] int32 (device): the conv_state slot of each request; a
+ *              value outside [0, n_slots) (-1 marks padding) zeroes that
+ *              request's output row and leaves every slot untouched. Two
+ *              requests naming the same slot race (unchecked: device data).
+ *   w, bias    [C, W] and [C] (bias may be NULL), as for gdn_conv1d_causal.
+ *   y          [n, C] in `dtype` (row r at y + r*y_stride_n):
+ *              act(sum_{j<W-1} w[c][j] state[j][c] + w[c][W-1] x[c] + bias[c]),
+ *              act = SiLU if silu else identity; then the slot's rows move one
+ *              token on and take x as the latest. The arithmetic is that of
+ *              gdn_conv1d_causal, so a sequence fed one token at a time from a
+ *              zero state gives bit-identical outputs.
+ *   W        4.
+ * Errors: n < 0, n_slots < 1, C < 1, NULL pointer, silu not 0/1, short
+ * strides, x / y / conv_state the same buffer -> GDN_EINVAL; W, dtype, C not
+ * a multiple of 16 bytes, alignment -> GDN_EUNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+int gdn_conv1d_update(const void* x, int64_t x_stride_n, void* conv_state,
+                      const int32_t* slot, const void* w, const void* bias,
+                      void* y, int64_t y_stride_n,
+                      int n, int n_slots, int C, int W, int silu, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_gdp_prefill_prepare -- a Gated DeltaProduct prefill as a gated delta
+ * rule over M*T positions: [GDP]'s interleave of the Householder copies
+ * (query on the last copy, the decay on the first) applied to every token of
+ * a prefill, so that gdn_chunk_fwd runs the layer unchanged.
+ *   x        [B*T, M*H*P + M*G*N + G*N] in `dtype`: post-conv rows, value |
+ *            key | query as for gdn_recurrent_decode; token t of batch b at
+ *            x + (b*T + t)*x_stride_t (packed: B = 1, sequences by cu_seqlens).
+ *   ba       [B*T, M*H + H]: b [M][H] then a [H], row stride ba_stride_t.
+ *   A_log, dt_bias  [H] fp32.
+ *   q, k     [B, M*T, G, N] in `dtype`, contiguous; v [B, M*T, H, P]; g, beta
+ *            [B, M*T, H] fp32. Row t*M + m (within its batch) is copy m of
+ *            token t: k, v, beta of copy m; q of token t on m = M-1, else
+ *            zero; g of token t on m = 0, else zero.
+ *   cu_seqlens, n_seqs  packed sequences of x (B == 1) or NULL; cu_out
+ *            (optional, n_seqs + 1 int32, device) receives M * cu_seqlens,
+ *            the offsets of the interleaved sequence.
+ * Then gdn_chunk_fwd(q, k, G*N, v, H*P, g, beta, ..., T' = M*T, H, Hk = G,
+ * K = N, V = P, cu_seqlens = cu_out) gives the layer: token t's output is
+ * row t*M + M-1 of o, and the final state is the layer's.
+ * Errors: bad sizes, H % G != 0, NULL pointers with T > 0, cu_seqlens with
+ * B != 1, cu_out without cu_seqlens, outputs sharing memory, short strides
+ * -> GDN_EINVAL; P, N, dtype, alignment -> GDN_EUNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+int gdn_gdp_prefill_prepare(const void* x, int64_t x_stride_t,
+                            const void* ba, int64_t ba_stride_t,
+                            const float* A_log, const float* dt_bias,
+                            const int32_t* cu_seqlens, int n_seqs, int32_t* cu_out,
+                            void* q, void* k, void* v, float* g, float* beta,
+                            int B, int T, int M, int H, int G, int P, int N,
+                            int dtype, void* stream);
 
 #ifdef __cplusplus
 }

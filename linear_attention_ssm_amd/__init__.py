@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
-    "gdn_recurrent_decode", "prefill_chain", "split_qkv",
+    "gdn_recurrent_decode", "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
+    "gdp_prefill", "prefill_chain", "split_qkv",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,13 @@ _lib.gdn_chunk_scan.restype = _i32
 _lib.gdn_recurrent_decode.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp]
                                       + [_i32] * 6 + [_f32, _i32, _i32, _vp])
 _lib.gdn_recurrent_decode.restype = _i32
+_lib.gdn_decode_prepare.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_vp]
+_lib.gdn_decode_prepare.restype = _i32
+_lib.gdn_conv1d_update.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64] + [_i32] * 6 + [_vp]
+_lib.gdn_conv1d_update.restype = _i32
+_lib.gdn_gdp_prefill_prepare.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                          _vp, _vp, _vp] + [_i32] * 8 + [_vp])
+_lib.gdn_gdp_prefill_prepare.restype = _i32
 
 
 class GdnError(RuntimeError):
@@ -285,6 +293,97 @@ def gdn_recurrent_decode(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
                                    _stream(x.device))
     _check(rc, "gdn_recurrent_decode")
     return o
+
+
+def gdn_decode_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
+                       dt_bias: torch.Tensor, M: int, H: int, G: int, P: int, N: int):
+    """The five tensors of one decode step: returns (q [n,M,H,N], k [n,M,H,N],
+    v [n,M,H,P] in x's dtype, beta [n,M,H], g [n,M,H] fp32)."""
+    if x.dim() == 3:
+        x = x.reshape(x.shape[0], x.shape[-1])
+    if ba.dim() == 3:
+        ba = ba.reshape(ba.shape[0], ba.shape[-1])
+    n = x.shape[0]
+    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[0] != n or ba.dtype != x.dtype:
+        raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
+    dev = x.device
+    q = torch.empty((n, M, H, N), dtype=x.dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((n, M, H, P), dtype=x.dtype, device=dev)
+    beta = torch.empty((n, M, H), dtype=torch.float32, device=dev)
+    g = torch.empty_like(beta)
+    rc = _lib.gdn_decode_prepare(_dev(x, "x"), x.stride(0), _dev(ba, "ba"), ba.stride(0),
+                                 _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"), _dev(q, "q"),
+                                 _dev(k, "k"), _dev(v, "v"), _dev(beta, "beta"), _dev(g, "g"),
+                                 n, M, H, G, P, N, _code(x.dtype), _stream(dev))
+    _check(rc, "gdn_decode_prepare")
+    return q, k, v, beta, g
+
+
+def gdn_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, slot: torch.Tensor,
+                      w: torch.Tensor, bias: torch.Tensor | None = None,
+                      y: torch.Tensor | None = None, silu: bool = True) -> torch.Tensor:
+    """Short-conv update of one decode token per request. x: [n, C] (rows may be
+    strided); conv_state: [S, W-1, C] contiguous, updated in place; slot: int32
+    [n] (-1 = padding: zero output, no update). Returns y [n, C]."""
+    n, C = x.shape
+    S, Wm1, Cs = conv_state.shape
+    if x.stride(-1) != 1 or Cs != C or not conv_state.is_contiguous() or conv_state.dtype != x.dtype:
+        raise ValueError("conv_state must be a contiguous [S, W-1, C] tensor of x's dtype")
+    if slot.dtype != torch.int32 or slot.numel() != n:
+        raise ValueError("slot must be int32 [n]")
+    if w.shape != (C, Wm1 + 1) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [C, W] tensor")
+    if y is None:
+        y = torch.empty((n, C), dtype=x.dtype, device=x.device)
+    rc = _lib.gdn_conv1d_update(_dev(x, "x"), x.stride(0), _dev(conv_state, "conv_state"),
+                                _dev(slot, "slot"), _dev(w, "w"), _opt(bias, "bias"), _dev(y, "y"),
+                                y.stride(0), n, S, C, Wm1 + 1, int(bool(silu)), _code(x.dtype),
+                                _stream(x.device))
+    _check(rc, "gdn_conv1d_update")
+    return y
+
+
+def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
+                            dt_bias: torch.Tensor, M: int, H: int, G: int, P: int, N: int,
+                            cu_seqlens: torch.Tensor | None = None):
+    """Interleave a Gated DeltaProduct prefill into an M*T-token gated delta
+    rule. x: [B, T, M*H*P + M*G*N + G*N], ba: [B, T, M*H + H] (token rows may
+    be strided, batches evenly strided). Returns (q [B, M*T, G, N], k, v
+    [B, M*T, H, P], g [B, M*T, H], beta, cu_out or None)."""
+    B, T, row = x.shape
+    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[:2] != (B, T) or ba.dtype != x.dtype:
+        raise ValueError("x and ba must be [B, T, row] with contiguous rows of one dtype")
+    for t, name in ((x, "x"), (ba, "ba")):
+        if B > 1 and T > 0 and t.stride(0) != T * t.stride(1):
+            raise ValueError(f"{name}: batches must be evenly strided")
+    dev = x.device
+    q = torch.empty((B, M * T, G, N), dtype=x.dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((B, M * T, H, P), dtype=x.dtype, device=dev)
+    g = torch.empty((B, M * T, H), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    cu_out = None if cu_seqlens is None else torch.empty_like(cu_seqlens)
+    rc = _lib.gdn_gdp_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(ba, "ba"), ba.stride(1),
+                                      _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
+                                      _opt(cu_seqlens, "cu_seqlens"), n_seqs, _opt(cu_out, "cu_out"),
+                                      _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
+                                      _dev(beta, "beta"), B, T, M, H, G, P, N, _code(x.dtype),
+                                      _stream(dev))
+    _check(rc, "gdn_gdp_prefill_prepare")
+    return q, k, v, g, beta, cu_out
+
+
+def gdp_prefill(x, ba, A_log, dt_bias, M, H, G, P, N, initial_state=None, cu_seqlens=None,
+                scale=1.0, qk_l2norm=True, workspace=None):
+    """A Gated DeltaProduct prefill: the interleave above, then gdn_chunk_fwd
+    over the M*T positions. Returns (o [B, T, H, P] -- a view of rows t*M + M-1
+    of the interleaved output --, final_state [N_seq, H, N, P])."""
+    q, k, v, g, beta, cu2 = gdn_gdp_prefill_prepare(x, ba, A_log, dt_bias, M, H, G, P, N, cu_seqlens)
+    o2, fs = gdn_chunk_fwd(q, k, v, g, beta, initial_state=initial_state, cu_seqlens=cu2,
+                           scale=scale, qk_l2norm=qk_l2norm, workspace=workspace)
+    return o2[:, M - 1::M], fs
 
 
 # ------------------------------------------------------------ prefill chain

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "conv1d.hip", "gate.hip", "chunk.hip", "decode.hip"]
+SOURCES = ["gdn_api.hip", "conv1d.hip", "gate.hip", "chunk.hip", "decode.hip", "gdp.hip"]
 ARCH = "gfx950"
 
 

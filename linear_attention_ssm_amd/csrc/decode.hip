@@ -25,10 +25,6 @@ namespace gdn {
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeMaxM = 4;
 
-__device__ __forceinline__ float dec_softplus(float x) {
-    return x > 20.f ? x : log1pf(expf(x));
-}
-
 template <typename T, int NK, int PV>
 __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
     const T* __restrict__ x, int64_t xs, const T* __restrict__ ba, int64_t bas,
@@ -70,10 +66,10 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
     }
     for (int i = tid; i < NK; i += kDecodeThreads) qv[i] = to_f32(xr[q_base + (int64_t)grp * NK + i]);
     // --- gates: beta per copy, the decay on copy 0 only
-    if (tid < M) beta_s[tid] = 1.f / (1.f + expf(-to_f32(br[(int64_t)tid * H + h])));
+    if (tid < M) beta_s[tid] = gate_beta(to_f32(br[(int64_t)tid * H + h]));
     if (tid == kWave) {
         float a = to_f32(br[(int64_t)M * H + h]);
-        alpha_s = expf(-expf(A_log[h]) * dec_softplus(a + dt_bias[h]));
+        alpha_s = expf(gate_g(a, A_log[h], dt_bias[h]));
     }
 
     // --- issue the state loads early: they are the bulk of the traffic

@@ -13,10 +13,6 @@
 
 namespace gdn {
 
-__device__ __forceinline__ float softplus_f32(float x) {
-    return x > 20.f ? x : log1pf(expf(x));
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void gate_prepare_kernel(
     const T* __restrict__ a, int64_t asr, const T* __restrict__ b, int64_t bsr,
@@ -29,8 +25,8 @@ __global__ __launch_bounds__(256) void gate_prepare_kernel(
     const int h = (int)(i - r * H);
     const float av = to_f32(a[r * asr + h]);
     const float bv = to_f32(b[r * bsr + h]);
-    beta[i] = 1.f / (1.f + expf(-bv));
-    g[i] = -expf(A_log[h]) * softplus_f32(av + dt_bias[h]);
+    beta[i] = gate_beta(bv);
+    g[i] = gate_g(av, A_log[h], dt_bias[h]);
 }
 
 hipError_t launch_gate_prepare(const void* a, int64_t asr, const void* b, int64_t bsr,

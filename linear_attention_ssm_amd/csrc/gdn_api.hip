@@ -28,6 +28,18 @@ hipError_t launch_recurrent_decode(const void* x, int64_t xs, const void* ba, in
                                    const float* A_log, const float* dt_bias, float* state,
                                    void* o, int n, int M, int H, int G, int P, int N, float scale,
                                    int l2norm, bool bf16_io, hipStream_t stream);
+hipError_t launch_decode_prepare(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                 const float* A_log, const float* dt_bias, void* q, void* k,
+                                 void* v, float* beta, float* g, int n, int M, int H, int G, int P,
+                                 int N, bool bf16_io, hipStream_t stream);
+hipError_t launch_conv1d_update(const void* x, int64_t xs, void* state, const int32_t* slot,
+                                const void* w, const void* bias, void* y, int64_t ys, int n,
+                                int n_slots, int C, int silu, bool bf16_io, hipStream_t stream);
+hipError_t launch_gdp_prefill_prepare(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                      const float* A_log, const float* dt_bias, const int32_t* cu,
+                                      int n_seqs, int32_t* cu_out, void* q, void* k, void* v,
+                                      float* g, float* beta, int64_t rows, int M, int H, int G,
+                                      int P, int N, bool bf16_io, hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -209,6 +221,78 @@ int gdn_recurrent_decode(const void* x, int64_t x_stride_n, const void* ba, int6
     return status_from(gdn::launch_recurrent_decode(x, x_stride_n, ba, ba_stride_n, A_log, dt_bias,
                                                     state, o, n, M, H, G, P, N, scale, qk_l2norm,
                                                     dtype == GDN_BF16, (hipStream_t)stream));
+}
+
+int gdn_decode_prepare(const void* x, int64_t x_stride_n, const void* ba, int64_t ba_stride_n,
+                       const float* A_log, const float* dt_bias, void* q, void* k, void* v,
+                       float* beta, float* g, int n, int M, int H, int G, int P, int N, int dtype,
+                       void* stream)
+{
+    if (!x || !ba || !A_log || !dt_bias || !q || !k || !v || !beta || !g) return GDN_EINVAL;
+    if (n < 0 || M < 1 || H < 1 || G < 1 || H % G != 0) return GDN_EINVAL;
+    if (q == k || q == v || k == v || (const void*)beta == (const void*)g) return GDN_EINVAL;
+    if (!valid_dtype(dtype) || !head_dim_ok(P) || !head_dim_ok(N)) return GDN_EUNSUPPORTED;
+    const int64_t row = (int64_t)M * H * P + (int64_t)M * G * N + (int64_t)G * N;
+    if (x_stride_n < row || ba_stride_n < (int64_t)M * H + H) return GDN_EINVAL;
+    if (!aligned16(x) || !stride16(x_stride_n, dtype) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(v))
+        return GDN_EUNSUPPORTED;
+    if ((int64_t)n * M > INT_MAX || (int64_t)n * M * H * (P > N ? P : N) > ((int64_t)1 << 40))
+        return GDN_EUNSUPPORTED;
+    if (n == 0) return GDN_OK;
+    return status_from(gdn::launch_decode_prepare(x, x_stride_n, ba, ba_stride_n, A_log, dt_bias, q,
+                                                  k, v, beta, g, n, M, H, G, P, N,
+                                                  dtype == GDN_BF16, (hipStream_t)stream));
+}
+
+int gdn_conv1d_update(const void* x, int64_t x_stride_n, void* conv_state, const int32_t* slot,
+                      const void* w, const void* bias, void* y, int64_t y_stride_n, int n,
+                      int n_slots, int C, int W, int silu, int dtype, void* stream)
+{
+    if (n < 0 || n_slots < 1 || C < 1) return GDN_EINVAL;
+    if (!conv_state || !w || (n > 0 && (!x || !y || !slot))) return GDN_EINVAL;
+    if (silu != 0 && silu != 1) return GDN_EINVAL;
+    if (n > 0 && (x == y || y == conv_state || x == conv_state)) return GDN_EINVAL;
+    if (x_stride_n < C || y_stride_n < C) return GDN_EINVAL;
+    if (!valid_dtype(dtype) || W != 4) return GDN_EUNSUPPORTED;
+    const int vn = 16 / elem_size(dtype);
+    if (C % vn != 0) return GDN_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(conv_state) || !aligned16(w) ||
+        (bias && !aligned16(bias)) || !stride16(x_stride_n, dtype) || !stride16(y_stride_n, dtype))
+        return GDN_EUNSUPPORTED;
+    if ((C / vn + 255) / 256 > 65535) return GDN_EUNSUPPORTED;
+    if (n == 0) return GDN_OK;
+    return status_from(gdn::launch_conv1d_update(x, x_stride_n, conv_state, slot, w, bias, y,
+                                                 y_stride_n, n, n_slots, C, silu,
+                                                 dtype == GDN_BF16, (hipStream_t)stream));
+}
+
+int gdn_gdp_prefill_prepare(const void* x, int64_t x_stride_t, const void* ba, int64_t ba_stride_t,
+                            const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                            int n_seqs, int32_t* cu_out, void* q, void* k, void* v, float* g,
+                            float* beta, int B, int T, int M, int H, int G, int P, int N,
+                            int dtype, void* stream)
+{
+    if (B < 1 || T < 0 || M < 1 || H < 1 || G < 1 || H % G != 0) return GDN_EINVAL;
+    if (!A_log || !dt_bias) return GDN_EINVAL;
+    if (T > 0 && (!x || !ba || !q || !k || !v || !g || !beta)) return GDN_EINVAL;
+    if (cu_seqlens && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
+    if (cu_out && !cu_seqlens) return GDN_EINVAL;
+    if (T > 0 && (q == k || q == v || k == v || (const void*)g == (const void*)beta))
+        return GDN_EINVAL;
+    if (!valid_dtype(dtype) || !head_dim_ok(P) || !head_dim_ok(N)) return GDN_EUNSUPPORTED;
+    const int64_t row = (int64_t)M * H * P + (int64_t)M * G * N + (int64_t)G * N;
+    if (x_stride_t < row || ba_stride_t < (int64_t)M * H + H) return GDN_EINVAL;
+    if (!aligned16(x) || !stride16(x_stride_t, dtype) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(v))
+        return GDN_EUNSUPPORTED;
+    const int64_t rows = (int64_t)B * T;
+    if (rows * M > INT_MAX) return GDN_EUNSUPPORTED;
+    if (T == 0) return GDN_OK;
+    return status_from(gdn::launch_gdp_prefill_prepare(x, x_stride_t, ba, ba_stride_t, A_log,
+                                                       dt_bias, cu_seqlens, n_seqs, cu_out, q, k,
+                                                       v, g, beta, rows, M, H, G, P, N,
+                                                       dtype == GDN_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"

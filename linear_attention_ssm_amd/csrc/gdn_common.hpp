@@ -157,6 +157,17 @@ template <> struct Mma<float> {
     }
 };
 
+// Gates of Megatron-Core API docs, "core.ssm.ops.gdp.decode_prepare"
+// (introduction and the "softplus" entry): softplus is log1p(exp(x)) in fp32,
+// the identity once x exceeds 20; beta = sigmoid(b); g = -exp(A_log) *
+// softplus(a + dt_bias). Accurate device exp / log1p and IEEE division; every
+// kernel that forms a gate uses these, so their results agree bit for bit.
+__device__ __forceinline__ float gate_softplus(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + expf(-b)); }
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
+    return -expf(A_log) * gate_softplus(a + dt_bias);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Index of the packed sequence containing token t: the largest i with

@@ -1,0 +1,220 @@
+// gdp.hip -- the Gated DeltaProduct steps around the recurrent core.
+//
+// Megatron-Core API docs, "core.ssm.ops.gdp.decode_prepare":
+//   * the module introduction places the preparation between the short-conv
+//     update and the recurrent kernel: split the post-conv row into value,
+//     key and query, GQA-expand query and key, interleave the M Householder
+//     copies (query on the last copy, the decay on the first) and gate the ba
+//     slice; a -1 slot zeroes the short-conv output of a padding request;
+//   * "gdp_decode_prepare" returns query, key [n, M, H, N], value [n, M, H, P]
+//     and beta, g [n, M, H] (fp32), the layouts of an M-length sequence per
+//     request.
+// Three kernels:
+//   gdp_decode_prepare_kernel   that five-tensor export for one decode step
+//                               (query / key / value plain copies);
+//   conv1d_update_kernel        the short-conv state update of one decode
+//                               token per request (W - 1 past rows per slot);
+//   gdp_prefill_prepare_kernel  the same interleave for a whole prefill: row
+//                               t * M + m of an M*T-token sequence is copy m of
+//                               token t, so the chunked forward runs a Gated
+//                               DeltaProduct layer unchanged (the decay on copy
+//                               0, the query on copy M - 1; the outputs of token
+//                               t are row t * M + M - 1).
+// All three move whole 16-byte vectors (a row of P or N elements is 128 or 256
+// bytes) and form the gates with the shared formulas of gdn_common.hpp.
+#include "gdn_common.hpp"
+
+namespace gdn {
+
+constexpr int kGdpThreads = 256;
+
+// Copy `units` 16-byte vectors from src to dst (or write zeros), spread over the block.
+template <typename V>
+__device__ __forceinline__ void copy_units(V* __restrict__ dst, const V* __restrict__ src, int units,
+                                           bool zero) {
+    for (int i = threadIdx.x; i < units; i += kGdpThreads) dst[i] = zero ? V{} : src[i];
+}
+
+// One block per (request, copy m): row r of x is v [M][H][P] | k [M][G][N] | q [G][N].
+template <typename T>
+__global__ __launch_bounds__(kGdpThreads) void gdp_decode_prepare_kernel(
+    const T* __restrict__ x, int64_t xs, const T* __restrict__ ba, int64_t bas,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    T* __restrict__ qo, T* __restrict__ ko, T* __restrict__ vo, float* __restrict__ beta,
+    float* __restrict__ g, int M, int H, int G, int P, int N)
+{
+    typedef typename V16<T>::type V;
+    constexpr int VN = V16<T>::n;
+    const int r = blockIdx.x / M;
+    const int m = blockIdx.x - r * M;
+    const int per = H / G;
+    const T* xr = x + (int64_t)r * xs;
+    const int64_t kbase = (int64_t)M * H * P, qbase = kbase + (int64_t)M * G * N;
+    const int64_t orow = (int64_t)r * M + m;     // output row (request, copy)
+    // value: one contiguous run of H * P elements
+    copy_units(reinterpret_cast<V*>(vo + orow * H * P),
+               reinterpret_cast<const V*>(xr + (int64_t)m * H * P), H * P / VN, false);
+    // key and query, GQA-expanded: head h reads group h / per
+    const int nu = N / VN;
+    for (int i = threadIdx.x; i < H * nu; i += kGdpThreads) {
+        const int h = i / nu, u = i - h * nu;
+        const int grp = h / per;
+        const V* ks = reinterpret_cast<const V*>(xr + kbase + ((int64_t)m * G + grp) * N) + u;
+        const V* qs = reinterpret_cast<const V*>(xr + qbase + (int64_t)grp * N) + u;
+        reinterpret_cast<V*>(ko + (orow * H + h) * N)[u] = *ks;
+        reinterpret_cast<V*>(qo + (orow * H + h) * N)[u] = m == M - 1 ? *qs : V{};
+    }
+    // gates: beta per copy, the decay on copy 0 only
+    const T* br = ba + (int64_t)r * bas;
+    for (int h = threadIdx.x; h < H; h += kGdpThreads) {
+        beta[orow * H + h] = gate_beta(to_f32(br[(int64_t)m * H + h]));
+        g[orow * H + h] = m == 0 ? gate_g(to_f32(br[(int64_t)M * H + h]), A_log[h], dt_bias[h]) : 0.f;
+    }
+}
+
+// One thread per (request, 16-byte channel group). conv_state [S, W-1, C]:
+// row j of a slot is x[t - (W - 1) + j] for the next token t.
+template <typename T>
+__global__ __launch_bounds__(kGdpThreads) void conv1d_update_kernel(
+    const T* __restrict__ x, int64_t xs, T* __restrict__ state, const int32_t* __restrict__ slot,
+    const T* __restrict__ w, const T* __restrict__ bias, T* __restrict__ y, int64_t ys,
+    int n_slots, int C, int silu)
+{
+    typedef V16<T> VV;
+    typedef typename VV::type V;
+    constexpr int VN = VV::n;
+    constexpr int W = 4;
+    const int r = blockIdx.x;
+    const int cg = blockIdx.y * kGdpThreads + threadIdx.x;
+    if (cg * VN >= C) return;
+    const int c0 = cg * VN;
+    V* yr = reinterpret_cast<V*>(y + (int64_t)r * ys + c0);
+    const int s = slot[r];
+    if (s < 0 || s >= n_slots) {   // padding request (or a slot outside the pool): zero output
+        *yr = V{};
+        return;
+    }
+    V* st = reinterpret_cast<V*>(state + (int64_t)s * (W - 1) * C + c0);
+    const int64_t srow = C / VN;    // 16-byte vectors per state row
+    const typename VV::ftype xf = VV::to_float(*reinterpret_cast<const V*>(x + (int64_t)r * xs + c0));
+    typename VV::ftype win[W - 1];
+    V raw[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        raw[j] = st[j * srow];
+        win[j] = VV::to_float(raw[j]);
+    }
+    // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e] (as in the prefill kernel)
+    float wt[W][VN];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        const typename VV::ftype f = VV::to_float(*reinterpret_cast<const V*>(w + (int64_t)c0 * W + i * VN));
+#pragma unroll
+        for (int u = 0; u < VN; ++u) {
+            const int flat = i * VN + u;
+            wt[flat % W][flat / W] = f[u];
+        }
+    }
+    typename VV::ftype bs{};
+    if (bias) bs = VV::to_float(*reinterpret_cast<const V*>(bias + c0));
+    typename VV::ftype out;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+        float acc = bias ? bs[e] : 0.f;
+        acc = fmaf(wt[0][e], win[0][e], acc);
+        acc = fmaf(wt[1][e], win[1][e], acc);
+        acc = fmaf(wt[2][e], win[2][e], acc);
+        acc = fmaf(wt[3][e], xf[e], acc);
+        out[e] = silu ? acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc)) : acc;   // (v_rcp_f32, ~1 ulp)
+    }
+    *yr = VV::from_float(out);
+    // the window moves one token on
+    st[0] = raw[1];
+    st[srow] = raw[2];
+    st[2 * srow] = *reinterpret_cast<const V*>(x + (int64_t)r * xs + c0);
+}
+
+// One block per (token row, copy m) of a prefill: output row p = row * M + m.
+template <typename T>
+__global__ __launch_bounds__(kGdpThreads) void gdp_prefill_prepare_kernel(
+    const T* __restrict__ x, int64_t xs, const T* __restrict__ ba, int64_t bas,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const int32_t* __restrict__ cu, int n_seqs, int32_t* __restrict__ cu_out,
+    T* __restrict__ qo, T* __restrict__ ko, T* __restrict__ vo, float* __restrict__ g,
+    float* __restrict__ beta, int M, int H, int G, int P, int N)
+{
+    typedef typename V16<T>::type V;
+    constexpr int VN = V16<T>::n;
+    const int64_t row = blockIdx.x / M;
+    const int m = (int)(blockIdx.x - row * M);
+    const int64_t p = row * M + m;
+    const T* xr = x + row * xs;
+    const int64_t kbase = (int64_t)M * H * P, qbase = kbase + (int64_t)M * G * N;
+    copy_units(reinterpret_cast<V*>(vo + p * H * P), reinterpret_cast<const V*>(xr + (int64_t)m * H * P),
+               H * P / VN, false);
+    copy_units(reinterpret_cast<V*>(ko + p * G * N), reinterpret_cast<const V*>(xr + kbase + (int64_t)m * G * N),
+               G * N / VN, false);
+    copy_units(reinterpret_cast<V*>(qo + p * G * N), reinterpret_cast<const V*>(xr + qbase), G * N / VN,
+               m != M - 1);
+    const T* br = ba + row * bas;
+    for (int h = threadIdx.x; h < H; h += kGdpThreads) {
+        beta[p * H + h] = gate_beta(to_f32(br[(int64_t)m * H + h]));
+        g[p * H + h] = m == 0 ? gate_g(to_f32(br[(int64_t)M * H + h]), A_log[h], dt_bias[h]) : 0.f;
+    }
+    if (cu && cu_out && blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= n_seqs; i += kGdpThreads) cu_out[i] = cu[i] * M;
+}
+
+hipError_t launch_decode_prepare(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                 const float* A_log, const float* dt_bias, void* q, void* k,
+                                 void* v, float* beta, float* g, int n, int M, int H, int G, int P,
+                                 int N, bool bf16_io, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((int64_t)n * M));
+    if (bf16_io)
+        hipLaunchKernelGGL(gdp_decode_prepare_kernel<bf16>, grid, dim3(kGdpThreads), 0, stream,
+                           (const bf16*)x, xs, (const bf16*)ba, bas, A_log, dt_bias, (bf16*)q,
+                           (bf16*)k, (bf16*)v, beta, g, M, H, G, P, N);
+    else
+        hipLaunchKernelGGL(gdp_decode_prepare_kernel<float>, grid, dim3(kGdpThreads), 0, stream,
+                           (const float*)x, xs, (const float*)ba, bas, A_log, dt_bias, (float*)q,
+                           (float*)k, (float*)v, beta, g, M, H, G, P, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d_update(const void* x, int64_t xs, void* state, const int32_t* slot,
+                                const void* w, const void* bias, void* y, int64_t ys, int n,
+                                int n_slots, int C, int silu, bool bf16_io, hipStream_t stream)
+{
+    const int vn = bf16_io ? 8 : 4;
+    const dim3 grid((unsigned)n, (unsigned)((C / vn + kGdpThreads - 1) / kGdpThreads));
+    if (bf16_io)
+        hipLaunchKernelGGL(conv1d_update_kernel<bf16>, grid, dim3(kGdpThreads), 0, stream,
+                           (const bf16*)x, xs, (bf16*)state, slot, (const bf16*)w, (const bf16*)bias,
+                           (bf16*)y, ys, n_slots, C, silu);
+    else
+        hipLaunchKernelGGL(conv1d_update_kernel<float>, grid, dim3(kGdpThreads), 0, stream,
+                           (const float*)x, xs, (float*)state, slot, (const float*)w,
+                           (const float*)bias, (float*)y, ys, n_slots, C, silu);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdp_prefill_prepare(const void* x, int64_t xs, const void* ba, int64_t bas,
+                                      const float* A_log, const float* dt_bias, const int32_t* cu,
+                                      int n_seqs, int32_t* cu_out, void* q, void* k, void* v,
+                                      float* g, float* beta, int64_t rows, int M, int H, int G,
+                                      int P, int N, bool bf16_io, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(rows * M));
+    if (bf16_io)
+        hipLaunchKernelGGL(gdp_prefill_prepare_kernel<bf16>, grid, dim3(kGdpThreads), 0, stream,
+                           (const bf16*)x, xs, (const bf16*)ba, bas, A_log, dt_bias, cu, n_seqs, cu_out,
+                           (bf16*)q, (bf16*)k, (bf16*)v, g, beta, M, H, G, P, N);
+    else
+        hipLaunchKernelGGL(gdp_prefill_prepare_kernel<float>, grid, dim3(kGdpThreads), 0, stream,
+                           (const float*)x, xs, (const float*)ba, bas, A_log, dt_bias, cu, n_seqs,
+                           cu_out, (float*)q, (float*)k, (float*)v, g, beta, M, H, G, P, N);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

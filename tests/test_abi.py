@@ -47,13 +47,18 @@ def lib():
     L.gdn_recurrent_decode.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp] + [i32] * 6 + [f32, i32, i32, vp]
     L.gdn_chunk_prepare.argtypes = [vp, vp, i64, vp, vp, vp, i32] + [i32] * 5 + [f32, i32, i32, vp, sz, vp]
     L.gdn_chunk_scan.argtypes = [vp, vp, i64, vp, i64, vp, vp, vp, vp, i32] + [i32] * 7 + [vp, sz, vp]
+    L.gdn_decode_prepare.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp] + [i32] * 7 + [vp]
+    L.gdn_conv1d_update.argtypes = [vp, i64, vp, vp, vp, vp, vp, i64] + [i32] * 6 + [vp]
+    L.gdn_gdp_prefill_prepare.argtypes = ([vp, i64, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+                                          + [i32] * 8 + [vp])
     return L
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     fns = declared_functions()
     for name in ("gdn_conv1d_causal", "gdn_gate_prepare", "gdn_chunk_fwd", "gdn_chunk_prepare",
                  "gdn_chunk_scan", "gdn_chunk_fwd_workspace_size", "gdn_recurrent_decode",
+                 "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
                  "gdn_status_string"):
         assert name in fns
 
@@ -225,3 +230,89 @@ def test_product_path_does_not_reference_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+ROW5 = 2 * 32 * 128 + 2 * 16 * 128 + 16 * 128   # decode workload row (M=2, H=32, G=16, P=N=128)
+
+
+def dprep(lib, **kw):
+    a = dict(x=P, xs=ROW5, ba=P2, bas=96, A_log=P3, dt=P4, q=P5, k=P6, v=0x70000, beta=0x80000,
+             g=0x90000, n=256, M=2, H=32, G=16, Pd=128, N=128, dtype=BF16)
+    a.update(kw)
+    return lib.gdn_decode_prepare(a["x"], a["xs"], a["ba"], a["bas"], a["A_log"], a["dt"], a["q"],
+                                  a["k"], a["v"], a["beta"], a["g"], a["n"], a["M"], a["H"],
+                                  a["G"], a["Pd"], a["N"], a["dtype"], None)
+
+
+def test_decode_prepare_validation(lib):
+    for key in ("x", "ba", "A_log", "dt", "q", "k", "v", "beta", "g"):
+        assert dprep(lib, **{key: None}) == EINVAL
+    assert dprep(lib, n=-1) == EINVAL
+    assert dprep(lib, M=0) == EINVAL
+    assert dprep(lib, G=5) == EINVAL                    # H % G
+    assert dprep(lib, k=P5) == EINVAL                   # q and k alias
+    assert dprep(lib, g=0x80000) == EINVAL              # beta and g alias
+    assert dprep(lib, xs=ROW5 - 8) == EINVAL            # row stride shorter than a row
+    assert dprep(lib, bas=95) == EINVAL
+    assert dprep(lib, Pd=96) == EUNSUP
+    assert dprep(lib, N=32) == EUNSUP
+    assert dprep(lib, dtype=3) == EUNSUP
+    assert dprep(lib, x=P + 2) == EUNSUP                # misaligned
+    assert dprep(lib, xs=ROW5 + 4) == EUNSUP            # row stride not 16-byte aligned
+    assert dprep(lib, q=P5 + 8) == EUNSUP
+    assert dprep(lib, n=0) == OK
+
+
+def cupd(lib, **kw):
+    a = dict(x=P, xs=6144, st=P2, slot=P3, w=P4, bias=None, y=P5, ys=6144, n=8, n_slots=16, C=6144,
+             W=4, silu=1, dtype=BF16)
+    a.update(kw)
+    return lib.gdn_conv1d_update(a["x"], a["xs"], a["st"], a["slot"], a["w"], a["bias"], a["y"],
+                                 a["ys"], a["n"], a["n_slots"], a["C"], a["W"], a["silu"], a["dtype"],
+                                 None)
+
+
+def test_conv_update_validation(lib):
+    for key in ("x", "st", "slot", "w", "y"):
+        assert cupd(lib, **{key: None}) == EINVAL
+    assert cupd(lib, n=-1) == EINVAL
+    assert cupd(lib, n_slots=0) == EINVAL
+    assert cupd(lib, C=0) == EINVAL
+    assert cupd(lib, silu=3) == EINVAL
+    assert cupd(lib, y=P) == EINVAL                     # y aliases x
+    assert cupd(lib, y=P2) == EINVAL                    # y aliases the state
+    assert cupd(lib, xs=100) == EINVAL
+    assert cupd(lib, W=3) == EUNSUP
+    assert cupd(lib, dtype=9) == EUNSUP
+    assert cupd(lib, C=6140, xs=6144, ys=6144) == EUNSUP
+    assert cupd(lib, st=P2 + 4) == EUNSUP
+    assert cupd(lib, bias=P6 + 2) == EUNSUP
+    assert cupd(lib, n=0, x=None, y=None, slot=None) == OK
+
+
+def gprep(lib, **kw):
+    a = dict(x=P, xs=ROW5, ba=P2, bas=96, A_log=P3, dt=P4, cu=None, n_seqs=0, cu_out=None, q=P5,
+             k=P6, v=0x70000, g=0x80000, beta=0x90000, B=2, T=64, M=2, H=32, G=16, Pd=128, N=128,
+             dtype=BF16)
+    a.update(kw)
+    return lib.gdn_gdp_prefill_prepare(a["x"], a["xs"], a["ba"], a["bas"], a["A_log"], a["dt"],
+                                       a["cu"], a["n_seqs"], a["cu_out"], a["q"], a["k"], a["v"],
+                                       a["g"], a["beta"], a["B"], a["T"], a["M"], a["H"], a["G"],
+                                       a["Pd"], a["N"], a["dtype"], None)
+
+
+def test_gdp_prefill_prepare_validation(lib):
+    for key in ("x", "ba", "A_log", "dt", "q", "k", "v", "g", "beta"):
+        assert gprep(lib, **{key: None}) == EINVAL
+    assert gprep(lib, B=0) == EINVAL
+    assert gprep(lib, T=-1) == EINVAL
+    assert gprep(lib, M=0) == EINVAL
+    assert gprep(lib, G=3) == EINVAL
+    assert gprep(lib, cu=0xA0000, n_seqs=2) == EINVAL   # packed needs B == 1
+    assert gprep(lib, cu_out=0xB0000) == EINVAL          # cu_out without cu_seqlens
+    assert gprep(lib, v=P5) == EINVAL                    # q and v alias
+    assert gprep(lib, xs=ROW5 - 1) == EINVAL
+    assert gprep(lib, Pd=100) == EUNSUP
+    assert gprep(lib, x=P + 4) == EUNSUP
+    assert gprep(lib, T=0, x=None, ba=None, q=None, k=None, v=None, g=None, beta=None) == OK
+    assert gprep(lib, B=1, cu=0xA0000, n_seqs=2, cu_out=0xB0000, T=0) == OK
