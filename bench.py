@@ -236,6 +236,102 @@ def run_decode(args, gdn, wl, torch, dev, stream):
                         f"fp32 state in place, {steps} steps"}
 
 
+def _time_launches(torch, stream, fn, reps):
+    """Average µs of fn() over reps launches, HIP events on the launch stream."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def _time_graph(torch, fn, reps):
+    """Average µs per launch of fn() replayed from a captured HIP graph of reps
+    launches (no per-launch host overhead: what a decode loop captured in a
+    graph sees)."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    graph.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def _hbm(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": us, "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def run_gdp_steps(gdn, wl, torch, dev, stream):
+    """The Gated DeltaProduct steps around the core, each on its own: the
+    decode short-conv update and the five-tensor decode preparation at the
+    decode workload's shape (timed as graph replays: one decode token's launches
+    are that small), and a GDP prefill (interleave + chunked forward)."""
+    wd = wl.WORKLOADS["decode"]
+    n, M, H, G, P, N = wd.n, wd.M, wd.H, wd.G, wd.V, wd.K
+    xl, bl = wl.decode_row_sizes(M, H, G, P, N)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wd.seed + 1)
+    bf = torch.bfloat16
+    x = torch.randn((n, xl), generator=gen, device=dev).to(bf)
+    ba = torch.randn((n, bl), generator=gen, device=dev).to(bf)
+    cw = (torch.randn((xl, 4), generator=gen, device=dev) * 0.5).to(bf)
+    cst = torch.randn((n, 3, xl), generator=gen, device=dev).to(bf)
+    slot = torch.randperm(n, generator=gen, device=dev).to(torch.int32)
+    A_log = torch.log(1 + 15 * torch.rand(H, generator=gen, device=dev))
+    dt_bias = torch.randn(H, generator=gen, device=dev) * 0.1
+    y = torch.empty_like(x)
+    out = {}
+    us = _time_graph(torch, lambda: gdn.gdn_conv1d_update(x, cst, slot, cw, y=y), 100)
+    out["conv1d_update"] = _hbm(2 * n * xl * 2 + 2 * n * 3 * xl * 2 + xl * 4 * 2, us)
+    out["conv1d_update"]["workload"] = f"n={n} requests, C={xl} bf16, W=4, one slot each"
+    dq = torch.empty((n, M, H, N), dtype=bf, device=dev)
+    dout = (dq, torch.empty_like(dq), torch.empty((n, M, H, P), dtype=bf, device=dev),
+            torch.empty((n, M, H), device=dev), torch.empty((n, M, H), device=dev))
+    us = _time_graph(torch, lambda: gdn.gdn_decode_prepare(x, ba, A_log, dt_bias, M, H, G, P, N,
+                                                           out=dout), 100)
+    out["decode_prepare"] = _hbm(n * xl * 2 + n * bl * 2 + n * M * H * (2 * N + P) * 2
+                                 + 2 * n * M * H * 4, us)
+    out["decode_prepare"]["workload"] = f"n={n} M={M} H={H} G={G} P=N={N} bf16"
+    # GDP prefill at the decode layer's shape: B sequences of T tokens
+    B, T = 2, 2048
+    xp = torch.randn((B, T, xl), generator=gen, device=dev).to(bf)
+    bp = torch.randn((B, T, bl), generator=gen, device=dev).to(bf)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, M * T, H, G, N, P, 0, bf),
+                     dtype=torch.uint8, device=dev)
+    q, k, v, g, beta, _ = gdn.gdn_gdp_prefill_prepare(xp, bp, A_log, dt_bias, M, H, G, P, N)
+    us_prep = _time_launches(torch, stream, lambda: gdn.gdn_gdp_prefill_prepare(
+        xp, bp, A_log, dt_bias, M, H, G, P, N, out=(q, k, v, g, beta)), 20)
+    o = torch.empty((B, M * T, H, P), dtype=bf, device=dev)
+    us_fwd = _time_launches(torch, stream, lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, workspace=ws, o=o), 20)
+    prep_bytes = B * T * (xl + bl) * 2 + B * M * T * (2 * G * N + H * P) * 2 + 2 * B * M * T * H * 4
+    out["gdp_prefill"] = {"tokens_per_s": B * T / ((us_prep + us_fwd) * 1e-6), "us": us_prep + us_fwd,
+                          "interleave": _hbm(prep_bytes, us_prep), "chunk_fwd_us": us_fwd,
+                          "workload": f"B={B} T={T} M={M} H={H} G={G} P=N={N} bf16 "
+                                      f"(chunked forward over {M * T} positions per sequence)"}
+    return out
+
+
 def _kernel_stem(name):
     import re
     m = re.match(r"_ZN3gdn\d+(\w+?)I", name)
@@ -374,6 +470,7 @@ def main():
                           for op in op_ms}
     if args.only != "prefill" and not args.no_decode:
         out["decode"] = run_decode(args, gdn, wl, torch, dev, stream)
+        out["gdp_steps"] = run_gdp_steps(gdn, wl, torch, dev, stream)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -296,9 +296,11 @@ def gdn_recurrent_decode(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
 
 
 def gdn_decode_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
-                       dt_bias: torch.Tensor, M: int, H: int, G: int, P: int, N: int):
+                       dt_bias: torch.Tensor, M: int, H: int, G: int, P: int, N: int,
+                       out: tuple | None = None):
     """The five tensors of one decode step: returns (q [n,M,H,N], k [n,M,H,N],
-    v [n,M,H,P] in x's dtype, beta [n,M,H], g [n,M,H] fp32)."""
+    v [n,M,H,P] in x's dtype, beta [n,M,H], g [n,M,H] fp32). `out` may hold
+    preallocated contiguous (q, k, v, beta, g)."""
     if x.dim() == 3:
         x = x.reshape(x.shape[0], x.shape[-1])
     if ba.dim() == 3:
@@ -307,11 +309,19 @@ def gdn_decode_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
     if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[0] != n or ba.dtype != x.dtype:
         raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
     dev = x.device
-    q = torch.empty((n, M, H, N), dtype=x.dtype, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((n, M, H, P), dtype=x.dtype, device=dev)
-    beta = torch.empty((n, M, H), dtype=torch.float32, device=dev)
-    g = torch.empty_like(beta)
+    if out is None:
+        q = torch.empty((n, M, H, N), dtype=x.dtype, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((n, M, H, P), dtype=x.dtype, device=dev)
+        beta = torch.empty((n, M, H), dtype=torch.float32, device=dev)
+        g = torch.empty_like(beta)
+    else:
+        q, k, v, beta, g = out
+        for t, shp, dt in ((q, (n, M, H, N), x.dtype), (k, (n, M, H, N), x.dtype),
+                           (v, (n, M, H, P), x.dtype), (beta, (n, M, H), torch.float32),
+                           (g, (n, M, H), torch.float32)):
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"output tensors must be contiguous {shp} {dt}")
     rc = _lib.gdn_decode_prepare(_dev(x, "x"), x.stride(0), _dev(ba, "ba"), ba.stride(0),
                                  _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"), _dev(q, "q"),
                                  _dev(k, "k"), _dev(v, "v"), _dev(beta, "beta"), _dev(g, "g"),
@@ -346,7 +356,7 @@ def gdn_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, slot: torch.Ten
 
 def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
                             dt_bias: torch.Tensor, M: int, H: int, G: int, P: int, N: int,
-                            cu_seqlens: torch.Tensor | None = None):
+                            cu_seqlens: torch.Tensor | None = None, out: tuple | None = None):
     """Interleave a Gated DeltaProduct prefill into an M*T-token gated delta
     rule. x: [B, T, M*H*P + M*G*N + G*N], ba: [B, T, M*H + H] (token rows may
     be strided, batches evenly strided). Returns (q [B, M*T, G, N], k, v
@@ -358,11 +368,19 @@ def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tens
         if B > 1 and T > 0 and t.stride(0) != T * t.stride(1):
             raise ValueError(f"{name}: batches must be evenly strided")
     dev = x.device
-    q = torch.empty((B, M * T, G, N), dtype=x.dtype, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((B, M * T, H, P), dtype=x.dtype, device=dev)
-    g = torch.empty((B, M * T, H), dtype=torch.float32, device=dev)
-    beta = torch.empty_like(g)
+    if out is None:
+        q = torch.empty((B, M * T, G, N), dtype=x.dtype, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((B, M * T, H, P), dtype=x.dtype, device=dev)
+        g = torch.empty((B, M * T, H), dtype=torch.float32, device=dev)
+        beta = torch.empty_like(g)
+    else:
+        q, k, v, g, beta = out
+        for t, shp, dt in ((q, (B, M * T, G, N), x.dtype), (k, (B, M * T, G, N), x.dtype),
+                           (v, (B, M * T, H, P), x.dtype), (g, (B, M * T, H), torch.float32),
+                           (beta, (B, M * T, H), torch.float32)):
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"output tensors must be contiguous {shp} {dt}")
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     cu_out = None if cu_seqlens is None else torch.empty_like(cu_seqlens)
     rc = _lib.gdn_gdp_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(ba, "ba"), ba.stride(1),

@@ -237,8 +237,8 @@ int gdn_decode_prepare(const void* x, int64_t x_stride_n, const void* ba, int64_
     if (!aligned16(x) || !stride16(x_stride_n, dtype) || !aligned16(q) || !aligned16(k) ||
         !aligned16(v))
         return GDN_EUNSUPPORTED;
-    if ((int64_t)n * M > INT_MAX || (int64_t)n * M * H * (P > N ? P : N) > ((int64_t)1 << 40))
-        return GDN_EUNSUPPORTED;
+    // one thread per 16-byte output vector: the grid must fit 32 bits of blocks
+    if ((int64_t)n * M * H * (P + 2 * N + 16) / 4 / 256 >= ((int64_t)1 << 31)) return GDN_EUNSUPPORTED;
     if (n == 0) return GDN_OK;
     return status_from(gdn::launch_decode_prepare(x, x_stride_n, ba, ba_stride_n, A_log, dt_bias, q,
                                                   k, v, beta, g, n, M, H, G, P, N,

@@ -11,7 +11,8 @@
 //     request.
 // Three kernels:
 //   gdp_decode_prepare_kernel   that five-tensor export for one decode step
-//                               (query / key / value plain copies);
+//                               (query / key / value plain copies, one thread
+//                               per 16-byte output vector);
 //   conv1d_update_kernel        the short-conv state update of one decode
 //                               token per request (W - 1 past rows per slot);
 //   gdp_prefill_prepare_kernel  the same interleave for a whole prefill: row
@@ -35,40 +36,55 @@ __device__ __forceinline__ void copy_units(V* __restrict__ dst, const V* __restr
     for (int i = threadIdx.x; i < units; i += kGdpThreads) dst[i] = zero ? V{} : src[i];
 }
 
-// One block per (request, copy m): row r of x is v [M][H][P] | k [M][G][N] | q [G][N].
+// One thread per 16-byte vector of the value, key and query outputs (in that
+// order, output-major), then one per gate element: row r of x is
+// v [M][H][P] | k [M][G][N] | q [G][N].
 template <typename T>
 __global__ __launch_bounds__(kGdpThreads) void gdp_decode_prepare_kernel(
     const T* __restrict__ x, int64_t xs, const T* __restrict__ ba, int64_t bas,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     T* __restrict__ qo, T* __restrict__ ko, T* __restrict__ vo, float* __restrict__ beta,
-    float* __restrict__ g, int M, int H, int G, int P, int N)
+    float* __restrict__ g, int n, int M, int H, int G, int P, int N)
 {
     typedef typename V16<T>::type V;
     constexpr int VN = V16<T>::n;
-    const int r = blockIdx.x / M;
-    const int m = blockIdx.x - r * M;
-    const int per = H / G;
-    const T* xr = x + (int64_t)r * xs;
+    // 32-bit index arithmetic (the entry point bounds the work); P / VN and
+    // N / VN are powers of two
+    const uint32_t psh = __builtin_ctz((uint32_t)(P / VN)), nsh = __builtin_ctz((uint32_t)(N / VN));
+    const uint32_t MH = (uint32_t)(M * H);
+    const uint32_t rows = (uint32_t)n * MH;             // (request, copy, head) rows
+    const uint32_t nv = rows << psh, nk = rows << nsh;
+    uint32_t i = blockIdx.x * kGdpThreads + threadIdx.x;
     const int64_t kbase = (int64_t)M * H * P, qbase = kbase + (int64_t)M * G * N;
-    const int64_t orow = (int64_t)r * M + m;     // output row (request, copy)
-    // value: one contiguous run of H * P elements
-    copy_units(reinterpret_cast<V*>(vo + orow * H * P),
-               reinterpret_cast<const V*>(xr + (int64_t)m * H * P), H * P / VN, false);
-    // key and query, GQA-expanded: head h reads group h / per
-    const int nu = N / VN;
-    for (int i = threadIdx.x; i < H * nu; i += kGdpThreads) {
-        const int h = i / nu, u = i - h * nu;
-        const int grp = h / per;
-        const V* ks = reinterpret_cast<const V*>(xr + kbase + ((int64_t)m * G + grp) * N) + u;
-        const V* qs = reinterpret_cast<const V*>(xr + qbase + (int64_t)grp * N) + u;
-        reinterpret_cast<V*>(ko + (orow * H + h) * N)[u] = *ks;
-        reinterpret_cast<V*>(qo + (orow * H + h) * N)[u] = m == M - 1 ? *qs : V{};
+    if (i < nv) {
+        // value: output row (r, m, h) is x[r][(m H + h) P ..]
+        const uint32_t o = i >> psh, u = i & ((1u << psh) - 1);
+        const uint32_t r = o / MH, mh = o - r * MH;
+        reinterpret_cast<V*>(vo)[i] = reinterpret_cast<const V*>(x + (int64_t)r * xs + (int64_t)mh * P)[u];
+        return;
     }
-    // gates: beta per copy, the decay on copy 0 only
-    const T* br = ba + (int64_t)r * bas;
-    for (int h = threadIdx.x; h < H; h += kGdpThreads) {
-        beta[orow * H + h] = gate_beta(to_f32(br[(int64_t)m * H + h]));
-        g[orow * H + h] = m == 0 ? gate_g(to_f32(br[(int64_t)M * H + h]), A_log[h], dt_bias[h]) : 0.f;
+    i -= nv;
+    if (i < 2 * nk) {
+        // key (i < nk) or query: head h reads group h / (H/G)
+        const bool isq = i >= nk;
+        const uint32_t j = isq ? i - nk : i;
+        const uint32_t o = j >> nsh, u = j & ((1u << nsh) - 1);
+        const uint32_t r = o / MH, mh = o - r * MH;
+        const uint32_t m = mh / (uint32_t)H, h = mh - m * (uint32_t)H;
+        const uint32_t grp = h / (uint32_t)(H / G);
+        const T* src = x + (int64_t)r * xs + (isq ? qbase + (int64_t)grp * N : kbase + ((int64_t)m * G + grp) * N);
+        const V val = isq && (int)m != M - 1 ? V{} : reinterpret_cast<const V*>(src)[u];
+        reinterpret_cast<V*>(isq ? qo : ko)[j] = val;
+        return;
+    }
+    i -= 2 * nk;
+    if (i < rows) {
+        // gates: beta per copy, the decay on copy 0 only
+        const uint32_t r = i / MH, mh = i - r * MH;
+        const uint32_t m = mh / (uint32_t)H, h = mh - m * (uint32_t)H;
+        const T* br = ba + (int64_t)r * bas;
+        beta[i] = gate_beta(to_f32(br[(int64_t)m * H + h]));
+        g[i] = m == 0 ? gate_g(to_f32(br[(int64_t)M * H + h]), A_log[h], dt_bias[h]) : 0.f;
     }
 }
 
@@ -170,15 +186,18 @@ hipError_t launch_decode_prepare(const void* x, int64_t xs, const void* ba, int6
                                  void* v, float* beta, float* g, int n, int M, int H, int G, int P,
                                  int N, bool bf16_io, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((int64_t)n * M));
+    const int vn = bf16_io ? 8 : 4;
+    const int64_t rows = (int64_t)n * M * H;
+    const int64_t work = rows * (P + 2 * N) / vn + rows;
+    const dim3 grid((unsigned)((work + kGdpThreads - 1) / kGdpThreads));
     if (bf16_io)
         hipLaunchKernelGGL(gdp_decode_prepare_kernel<bf16>, grid, dim3(kGdpThreads), 0, stream,
                            (const bf16*)x, xs, (const bf16*)ba, bas, A_log, dt_bias, (bf16*)q,
-                           (bf16*)k, (bf16*)v, beta, g, M, H, G, P, N);
+                           (bf16*)k, (bf16*)v, beta, g, n, M, H, G, P, N);
     else
         hipLaunchKernelGGL(gdp_decode_prepare_kernel<float>, grid, dim3(kGdpThreads), 0, stream,
                            (const float*)x, xs, (const float*)ba, bas, A_log, dt_bias, (float*)q,
-                           (float*)k, (float*)v, beta, g, M, H, G, P, N);
+                           (float*)k, (float*)v, beta, g, n, M, H, G, P, N);
     return hipGetLastError();
 }
 
