@@ -28,15 +28,22 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, int64_t ysb, int64_t yst,
     const int32_t* __restrict__ cu, int n_seqs,
-    int T_len, int C, int runs_per_row, int silu)
+    int T_len, int C, int runs_per_row, int runs_total, int runs_pad, int silu)
 {
     typedef V16<T> V;
     constexpr int VN = V::n;
+    // XCD-aware block order: each XCD (blockIdx % 8) takes a contiguous range
+    // of runs, so the W-1 rows before a run were just fetched into the same L2
+    // by the run before it
     const int ncg = C / VN;
-    const int cg = blockIdx.y * kConvThreads + threadIdx.x;
-    if (cg >= ncg) return;
-    const int b = blockIdx.x / runs_per_row;
-    const int t0 = (blockIdx.x % runs_per_row) * RUN;
+    const int per_xcd = runs_pad / 8;
+    const int j = blockIdx.x >> 3;
+    const int cgb = j / per_xcd;
+    const int run = (blockIdx.x & 7) * per_xcd + (j - cgb * per_xcd);
+    const int cg = cgb * kConvThreads + threadIdx.x;
+    if (cg >= ncg || run >= runs_total) return;
+    const int b = run / runs_per_row;
+    const int t0 = (run % runs_per_row) * RUN;
     const int c0 = cg * VN;
 
     // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e]; the group's VN x W taps
@@ -132,10 +139,13 @@ hipError_t launch_conv1d_t(const void* x, int64_t xsb, int64_t xst, const void* 
 {
     const int ncg = C / V16<T>::n;
     const int runs = (T_len + kConvRun - 1) / kConvRun;
-    dim3 grid(runs * B, (ncg + kConvThreads - 1) / kConvThreads);
-    hipLaunchKernelGGL((conv1d_causal_kernel<T, kConvRun>), grid, dim3(kConvThreads), 0, stream,
-                       (const T*)x, xsb, xst, (const T*)w, (const T*)bias, (T*)y, ysb, yst,
-                       cu, n_seqs, T_len, C, runs, silu);
+    const int total = runs * B;
+    const int pad = (total + 7) / 8 * 8;
+    const int cgb = (ncg + kConvThreads - 1) / kConvThreads;
+    hipLaunchKernelGGL((conv1d_causal_kernel<T, kConvRun>), dim3((unsigned)(pad * cgb)),
+                       dim3(kConvThreads), 0, stream, (const T*)x, xsb, xst, (const T*)w,
+                       (const T*)bias, (T*)y, ysb, yst, cu, n_seqs, T_len, C, runs, total, pad,
+                       silu);
     return hipGetLastError();
 }
 

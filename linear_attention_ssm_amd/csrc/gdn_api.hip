@@ -90,7 +90,7 @@ int gdn_conv1d_causal(const void* x, int64_t x_stride_b, int64_t x_stride_t, con
         !stride16(y_stride_t, dtype) || (B > 1 && (!stride16(x_stride_b, dtype) || !stride16(y_stride_b, dtype))))
         return GDN_EUNSUPPORTED;
     if (T == 0) return GDN_OK;
-    if ((C / vn + 255) / 256 > 65535 || (int64_t)((T + 15) / 16) * B > INT_MAX) return GDN_EUNSUPPORTED;
+    if ((int64_t)((T + 15) / 16 * B + 7) * ((C / vn + 255) / 256) > INT_MAX) return GDN_EUNSUPPORTED;
     return status_from(gdn::launch_conv1d(x, x_stride_b, x_stride_t, w, bias, y, y_stride_b,
                                           y_stride_t, cu_seqlens, n_seqs, B, T, C, silu,
                                           dtype == GDN_BF16, (hipStream_t)stream));
