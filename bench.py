@@ -340,26 +340,54 @@ def _kernel_stem(name):
     return name.split("(")[0][:60]
 
 
+def _phases(rows, id_key, name_key):
+    """The benchmark runs its parts in a fixed order: the prefill step, then the
+    decode step, then the Gated DeltaProduct steps. The decode kernel's
+    dispatches mark the boundaries, so a kernel used by two parts (the chunked
+    forward) is summarised per part instead of as a blended average."""
+    ids = [int(r[id_key]) for r in rows if KERNELS["decode"][0] in r[name_key]]
+    lo, hi = (min(ids), max(ids)) if ids else (None, None)
+
+    def phase(r):
+        d = int(r[id_key])
+        if lo is None or d < lo:
+            return "prefill"
+        return "decode" if d <= hi else "gdp steps"
+    return phase
+
+
 def summarize_stats(csv_path, out_md, command):
+    """Kernel time table from rocprofv3's kernel trace (one row per dispatch),
+    one line per (benchmark part, kernel, grid, workgroup)."""
+    import collections
     import csv
     rows = list(csv.DictReader(open(csv_path)))
+    phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
+    groups = collections.OrderedDict()
+    for r in rows:
+        key = (phase(r), r["Kernel_Name"],
+               int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    order = {"prefill": 0, "decode": 1, "gdp steps": 2}
+    items = sorted(groups.items(), key=lambda kv: (order[kv[0][0]], -sum(kv[1])))
     lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
              f"Command: `{command}`", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share |",
-             "|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r.get("Name") or r.get("KernelName") or ""
-        calls = int(float(r["Calls"]))
-        avg = float(r["AverageNs"]) / 1e3
-        mn = float(r.get("MinNs", 0)) / 1e3
-        mx = float(r.get("MaxNs", 0)) / 1e3
-        pct = float(r.get("Percentage", 0))
-        lines.append(f"| `{_kernel_stem(name)}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f}% |")
-    lines.append("")
-    lines.append("Full symbols:")
-    lines.append("")
-    for r in rows:
-        lines.append(f"- `{(r.get('Name') or '')[:200]}`")
+             "One line per part of the benchmark (prefill step, decode step, Gated DeltaProduct",
+             "steps), kernel and launch shape (grid = work-items), from the kernel trace.", "",
+             "| part | kernel | grid | workgroup | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (ph, name, grid, wg), d in items:
+        lines.append(f"| {ph} | `{_kernel_stem(name)}` | {grid} | {wg} | {len(d)} | "
+                     f"{sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
+                     f"{100 * sum(d) / total:.1f}% |")
+    lines += ["", "Full symbols:", ""]
+    seen = set()
+    for (_, name, _, _), _ in items:
+        if name not in seen:
+            seen.add(name)
+            lines.append(f"- `{name[:200]}`")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -371,18 +399,19 @@ def summarize_traffic(fetch_csv, write_csv, command):
     import csv
 
     def per_dispatch(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
         acc = collections.defaultdict(float)
-        names = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
+        names, phases = {}, {}
+        for r in rows:
             d = int(r["Dispatch_Id"])
             acc[d] += float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
             names[d] = r["Kernel_Name"]
-        return acc, names
+            phases[d] = phase(r)
+        return acc, names, phases
 
-    fetch, fnames = per_dispatch(fetch_csv, "FETCH_SIZE")
-    write, wnames = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch, fnames, fphase = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, wnames, wphase = per_dispatch(write_csv, "WRITE_SIZE")
     gib = float(1 << 30)
     # the probe copies are the buffer-copy dispatches that move 1 GiB: the last three
     # of that kernel in each run (earlier ones are uploads and the state reset)
@@ -396,14 +425,19 @@ def summarize_traffic(fetch_csv, write_csv, command):
     res = {"command": command, "copy_kernel_bytes": gib, "copy_fetch_raw": pf, "copy_write_raw": pw,
            "fetch_factor": ff, "write_factor": fw, "kernels": {}}
     for op, (stem, src) in KERNELS.items():
-        fv = [v for d, v in fetch.items() if stem in fnames[d]]
-        wv = [v for d, v in write.items() if stem in wnames[d]]
-        if not fv or ff is None or fw is None:
+        ids = sorted(d for d in fetch if stem in fnames[d])
+        if not ids or ff is None or fw is None:
             continue
+        # the part of the benchmark where the kernel first runs is its own
+        # workload; later launches (the Gated DeltaProduct steps) are kept apart
+        part = fphase[ids[0]]
+        fv = [fetch[d] for d in ids if fphase[d] == part]
+        wv = [v for d, v in write.items() if stem in wnames[d] and wphase[d] == part]
         fb = sum(fv) / len(fv) * ff
         wb = (sum(wv) / len(wv) * fw) if wv else 0.0
-        res["kernels"][stem] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
-                                "launches": len(fv), "source_sha": source_hash(src)}
+        res["kernels"][stem] = {"part": part, "fetch_bytes": fb, "write_bytes": wb,
+                                "bytes_per_launch": fb + wb, "launches": len(fv),
+                                "source_sha": source_hash(src)}
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(res, f, indent=1)
