@@ -178,6 +178,74 @@ int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t,
                    const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gdn_prefill -- the whole prefill of a gated delta rule layer from the
+ * projections: [ZZ] item 1 (causal conv1d, W = 4, + SiLU over the q | k | v
+ * channels), the gates of [GDP] (module introduction and "softplus" entry)
+ * and [ZZ] items 2-4 (the chunked forward). The result is exactly that of
+ *     gdn_conv1d_causal(x, conv_w, conv_bias, silu = 1) -> y = q | k | v,
+ *     gdn_gate_prepare(a, b, A_log, dt_bias)           -> g, beta,
+ *     gdn_chunk_fwd(q, k, v, g, beta, ...)              -> o, final_state
+ * on the same bf16 inputs, bit for bit (the same formulas, rounding points
+ * and accumulation order), in three kernel launches instead of four: the
+ * convolution of the q and k channels, the per-chunk solve forming the gates
+ * itself, and the scan convolving the value rows as it reads them. The value
+ * part of y, g and beta are never written (the convolved q and k rows live
+ * in the workspace).
+ *   x        [B*T, C] bf16 token rows before the convolution, C = 2*Hk*K +
+ *            H*V channels laid out q [Hk][K] | k [Hk][K] | v [H][V]; row t at
+ *            x + t*x_stride_t (batch row b starts at token b*T).
+ *   conv_w   [C, 4] bf16 contiguous taps (conv_w[c][3] multiplies x_t);
+ *   conv_bias  [C] bf16 or NULL.
+ *   a, b     [B*T, H] bf16 gate inputs; row t at a + t*a_stride_row.
+ *   A_log, dt_bias  [H] fp32.
+ *   initial_state, final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+ *   scale, qk_l2norm: as for gdn_chunk_fwd (final_state may be NULL; it may
+ *            equal initial_state for an in-place update).
+ *   dtype    GDN_BF16 only (GDN_EUNSUPPORTED otherwise).
+ *   workspace  device scratch of at least gdn_prefill_workspace_size(...)
+ *            bytes, 256-byte aligned; contents on entry do not matter.
+ * x, conv_w, conv_bias and o must be 16-byte aligned and x_stride_t*2 a
+ * multiple of 16 (else GDN_EUNSUPPORTED); o must not be x, a or b
+ * (GDN_EINVAL). gdn_prefill_workspace_size returns 0 for a dtype other than
+ * GDN_BF16, a head dim other than 64 or 128, or invalid sizes.
+ *
+ * gdn_prefill_prepare / gdn_prefill_scan -- the two phases of gdn_prefill
+ * (same arguments, same workspace), exposed so that each can be launched and
+ * timed on its own; gdn_prefill(...) is exactly gdn_prefill_prepare(...)
+ * followed by gdn_prefill_scan(...) on one stream. The prepare phase runs
+ * the q/k convolution and the per-chunk solve; the scan phase reads what it
+ * left in `workspace` (which must come from a prepare call with the same x,
+ * conv_w, conv_bias, a, b, gate parameters, cu_seqlens, sizes, scale and
+ * qk_l2norm; the workspace is otherwise unchecked).
+ * ---------------------------------------------------------------------- */
+size_t gdn_prefill_workspace_size(int B, int T, int H, int Hk, int K, int V, int n_seqs,
+                                  int dtype);
+
+int gdn_prefill(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
+                const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
+                const float* A_log, const float* dt_bias,
+                const float* initial_state, float* final_state, void* o,
+                const int32_t* cu_seqlens, int n_seqs,
+                int B, int T, int H, int Hk, int K, int V,
+                float scale, int qk_l2norm, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_prefill_prepare(const void* x, int64_t x_stride_t, const void* conv_w,
+                        const void* conv_bias, const void* a, int64_t a_stride_row,
+                        const void* b, int64_t b_stride_row,
+                        const float* A_log, const float* dt_bias,
+                        const int32_t* cu_seqlens, int n_seqs,
+                        int B, int T, int H, int Hk, int K, int V,
+                        float scale, int qk_l2norm, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_prefill_scan(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
+                     const float* initial_state, float* final_state, void* o,
+                     const int32_t* cu_seqlens, int n_seqs,
+                     int B, int T, int H, int Hk, int K, int V, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * gdn_recurrent_decode -- [GDP] "gdp_decode_prepare" fused with the
  * recurrent update it feeds: one decode token for n requests of a Gated
  * DeltaProduct layer with M Householder copies.

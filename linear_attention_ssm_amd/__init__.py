@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
+    "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
     "gdn_recurrent_decode", "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
     "gdp_prefill", "prefill_chain", "split_qkv",
 ]
@@ -50,6 +51,17 @@ _lib.gdn_chunk_fwd_workspace_size.restype = _sz
 _lib.gdn_chunk_fwd.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
                                + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_chunk_fwd.restype = _i32
+_lib.gdn_prefill_workspace_size.argtypes = [_i32] * 8
+_lib.gdn_prefill_workspace_size.restype = _sz
+_lib.gdn_prefill.argtypes = ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _i32] + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
+_lib.gdn_prefill.restype = _i32
+_lib.gdn_prefill_prepare.argtypes = ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32]
+                                     + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
+_lib.gdn_prefill_prepare.restype = _i32
+_lib.gdn_prefill_scan.argtypes = ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32] + [_i32] * 6
+                                  + [_i32, _vp, _sz, _vp])
+_lib.gdn_prefill_scan.restype = _i32
 _lib.gdn_chunk_prepare.argtypes = ([_vp, _vp, _i64, _vp, _vp, _vp, _i32] + [_i32] * 5
                                    + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_chunk_prepare.restype = _i32
@@ -230,6 +242,119 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                             _stream(q.device))
     _check(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_prefill_workspace_size(B: int, T: int, H: int, Hk: int, K: int, V: int,
+                               n_seqs: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(_lib.gdn_prefill_workspace_size(B, T, H, Hk, K, V, n_seqs, _code(dtype)))
+
+
+def _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens):
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [B, T, C] with a contiguous channel dim")
+    B, T, C = x.shape
+    if C != 2 * Hk * K + H * V:
+        raise ValueError(f"x has {C} channels, expected 2*Hk*K + H*V = {2 * Hk * K + H * V}")
+    if B > 1 and T > 0 and x.stride(0) != T * x.stride(1):
+        raise ValueError("x: batch rows must be evenly strided (stride(0) == T * stride(1))")
+    if w.shape != (C, 4) or not w.is_contiguous() or w.dtype != x.dtype:
+        raise ValueError("w must be a contiguous [C, 4] tensor of x's dtype")
+    if bias is not None and (bias.shape != (C,) or bias.dtype != x.dtype or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [C] tensor of x's dtype")
+    for t, n in ((a, "a"), (b, "b")):
+        if t is None:
+            continue
+        if t.shape != (B, T, H) or t.dtype != x.dtype or t.stride(2) != 1 or \
+                (B > 1 and T > 0 and t.stride(0) != T * t.stride(1)):
+            raise ValueError(f"{n} must be [B, T, H] of x's dtype, head dim contiguous, "
+                             "batch rows evenly strided")
+    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != H):
+            raise ValueError(f"{n} must be a contiguous fp32 [H] tensor")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return B, T, n_seqs
+
+
+def _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state, output_final_state,
+                     o, final_state):
+    N = n_seqs if cu_seqlens is not None else B
+    if initial_state is not None and (initial_state.dtype != torch.float32 or
+                                      not initial_state.is_contiguous() or
+                                      initial_state.shape != (N, H, K, V)):
+        raise ValueError(f"initial_state must be a contiguous fp32 [{N}, {H}, {K}, {V}] tensor")
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=x.dtype, device=x.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=x.device)
+    if not output_final_state:
+        final_state = None
+    return o, final_state
+
+
+def _prefill_ws(workspace, x, B, T, H, Hk, K, V, n_seqs):
+    if workspace is None:
+        ws_bytes = gdn_prefill_workspace_size(B, T, H, Hk, K, V, n_seqs, x.dtype)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    return workspace
+
+
+def gdn_prefill(x: torch.Tensor, w: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                A_log: torch.Tensor, dt_bias: torch.Tensor, *, Hk: int, K: int, H: int, V: int,
+                bias: torch.Tensor | None = None, initial_state: torch.Tensor | None = None,
+                output_final_state: bool = True, cu_seqlens: torch.Tensor | None = None,
+                scale: float = 1.0, qk_l2norm: bool = True,
+                workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                final_state: torch.Tensor | None = None):
+    """The whole prefill (conv1d + SiLU over q | k | v, gates, chunked forward)
+    in three launches. x: bf16 [B, T, C] rows before the convolution, C = 2 Hk
+    K + H V, channel dim contiguous; w: [C, 4]; a, b: bf16 [B, T, H] (the head
+    dim contiguous, rows evenly strided). Returns (o [B, T, H, V],
+    final_state [N, H, K, V] or None), equal bit for bit to prefill_chain."""
+    B, T, n_seqs = _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens)
+    o, final_state = _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state,
+                                      output_final_state, o, final_state)
+    workspace = _prefill_ws(workspace, x, B, T, H, Hk, K, V, n_seqs)
+    rc = _lib.gdn_prefill(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
+                          _dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
+                          _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
+                          _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
+                          _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
+                          float(scale), int(bool(qk_l2norm)), _code(x.dtype),
+                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                          _stream(x.device))
+    _check(rc, "gdn_prefill")
+    return o, final_state
+
+
+def gdn_prefill_prepare(x, w, a, b, A_log, dt_bias, workspace, *, Hk, K, H, V, bias=None,
+                        cu_seqlens=None, scale=1.0, qk_l2norm=True):
+    """Phase 1 of gdn_prefill (q/k convolution, gates, per-chunk solve) into `workspace`."""
+    B, T, n_seqs = _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens)
+    rc = _lib.gdn_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
+                                  _dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
+                                  _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
+                                  _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
+                                  float(scale), int(bool(qk_l2norm)), _code(x.dtype),
+                                  _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(rc, "gdn_prefill_prepare")
+
+
+def gdn_prefill_scan(x, w, workspace, *, Hk, K, H, V, bias=None, initial_state=None,
+                     output_final_state=True, cu_seqlens=None, o=None, final_state=None):
+    """Phase 2 of gdn_prefill (value convolution and the state scan). Returns (o, final_state)."""
+    B, T, n_seqs = _prefill_args(x, w, None, None, None, None, Hk, K, H, V, bias, cu_seqlens)
+    o, final_state = _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state,
+                                      output_final_state, o, final_state)
+    rc = _lib.gdn_prefill_scan(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
+                               _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
+                               _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk,
+                               K, V, _code(x.dtype), _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(rc, "gdn_prefill_scan")
     return o, final_state
 
 

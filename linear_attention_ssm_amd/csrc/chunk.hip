@@ -221,15 +221,28 @@ __device__ __forceinline__ void subst_rows(const float (&arow)[16], float (&x)[1
     }
 }
 
+// Gate inputs of the whole-prefill form of chunk_prep: the gates are formed
+// here from a and b (the same formulas as the gate kernel) instead of being
+// read from g and beta.
+struct PrepGates {
+    const bf16* a;        // [token][head], row strides as / bs
+    const bf16* b;
+    int64_t as, bs;
+    const float* A_log;
+    const float* dt_bias;
+};
+
 // Two waves per SIMD: registers sized for it.
-template <typename T, int KD>
+template <typename T, int KD, bool GATES>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void chunk_prep_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets, int n_seqs, int T_len,
-    int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec, int n_items)
+    int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec, int n_items,
+    PrepGates gz)
 {
+    static_assert(!GATES || sizeof(T) == 2, "the whole-prefill form runs on bf16 rows");
     typedef Mma<T> MT;
     typedef typename MT::Frag Frag;
     typedef Rec<T> RC;
@@ -255,9 +268,20 @@ void chunk_prep_kernel(
     const int lr = min(lane, L - 1);
     const uint32_t row_bytes = (uint32_t)(qk_stride * ES);
 
-    // gate values of the first value head (lane = row), requested before the rows
-    float gh = g[(int64_t)(loc.tok0 + lr) * H + hk * per];
-    float bh = beta[(int64_t)(loc.tok0 + lr) * H + hk * per];
+    // gate values of value head h (lane = row): given, or formed from a and b
+    auto gate_of = [&](int h, float& gv, float& bv) {
+        const int64_t row = loc.tok0 + lr;
+        if constexpr (GATES) {
+            gv = gate_g(to_f32(gz.a[row * gz.as + h]), gz.A_log[h], gz.dt_bias[h]);
+            bv = gate_beta(to_f32(gz.b[row * gz.bs + h]));
+        } else {
+            gv = g[row * H + h];
+            bv = beta[row * H + h];
+        }
+    };
+    // those of the first value head, requested before the rows
+    float gh, bh;
+    gate_of(hk * per, gh, bh);
 
     // ---- S = K K^T and Q K^T (lower tiles, R layout), diagonal tiles of Q Q^T
     const int64_t base = (int64_t)loc.tok0 * qk_stride + (int64_t)hk * KD;
@@ -303,10 +327,7 @@ void chunk_prep_kernel(
     for (int hv = 0; hv < per; ++hv) {
         const int h = hk * per + hv;
         unsigned char* rec = ws_rec + ((int64_t)tile * H + h) * RC::bytes;
-        if (hv > 0) {
-            gh = g[(int64_t)(loc.tok0 + lr) * H + h];
-            bh = beta[(int64_t)(loc.tok0 + lr) * H + h];
-        }
+        if (hv > 0) gate_of(h, gh, bh);
         // ---- cumsum and the per-row factors (lane = row)
         const float G2 = wave_inclusive_scan(live ? gh : 0.f) * kLog2e;
         const float GL2 = lane_value(G2, kWave - 1);
@@ -1279,10 +1300,19 @@ struct ChainOps {
     f32x4 fa[4], fc[4];         // row factors a and c
     float gL;                   // gamma_L
 };
-template <int KD, int NT>
+// Short-convolution taps (w0..w3, bias) of a chain lane's value column, for
+// the whole-prefill form, where the staged values are the raw rows before the
+// convolution.
+struct ColTaps {
+    float w0, w1, w2, w3, b;
+};
+
+template <int KD, int NT, bool CONV>
 __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
                                                 const ScanBuf<bf16, KD, NT>* __restrict__ buf,
-                                                const ScanLane<bf16, KD, NT>& ln, int t, int grp, int lane)
+                                                const ScanBuf<bf16, KD, NT>* __restrict__ prev,
+                                                const ScanLane<bf16, KD, NT>& ln, int t, int grp, int lane,
+                                                const ColTaps& cv)
 {
     typedef ScanBuf<bf16, KD, NT> SB;
     typedef Rec<bf16> RC;
@@ -1295,7 +1325,28 @@ __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const s16x4 raw = lds_read_tr16(buf->v[t] + ln.vtr + i * 16 * SB::VRB);
-        op.vv[i] = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+        if constexpr (CONV) {
+            // rows 16 i + 4 g + e need rows back to 16 i + 4 g - 3: the four
+            // before them are 4 rows up in the slab, or, for lane group 0 of
+            // the first row tile, rows 60..63 of the previous chunk (still
+            // staged), or zero at the start of the sequence (prev null)
+            const bool head = i == 0 && grp == 0;
+            const unsigned char* pa = head ? (prev ? prev->v[t] + ln.vtr + 60 * SB::VRB : buf->v[t] + ln.vtr)
+                                           : buf->v[t] + ln.vtr + (16 * i - 4) * SB::VRB;
+            const s16x4 pr = lds_read_tr16(pa);
+            const f32x4 x = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+            f32x4 p = __builtin_convertvector(__builtin_bit_cast(bf16x4, pr), f32x4);
+            if (head && !prev) p = zero4();
+            f32x4 y;
+            y[0] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[1], p[2], p[3], x[0]));
+            y[1] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[2], p[3], x[0], x[1]));
+            y[2] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[3], x[0], x[1], x[2]));
+            y[3] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, x[0], x[1], x[2], x[3]));
+            // the values the scan sees are the bf16 convolution outputs
+            op.vv[i] = __builtin_convertvector(__builtin_convertvector(y, bf16x4), f32x4);
+        } else {
+            op.vv[i] = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1331,13 +1382,13 @@ __device__ __forceinline__ void out_load(OutOps<KD>& op,
 // One chunk of chain wave t. `hf` holds h as B operand (made when h was
 // last updated) and `op` the chunk's operands; both turn over to the next
 // chunk (its operands read from `ahead`).
-template <int KD, int NT>
+template <int KD, int NT, bool CONV>
 __device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restrict__ cur,
                                            const ScanBuf<bf16, KD, NT>* __restrict__ ahead,
                                            RoleHand<KD, NT>* __restrict__ hand,
                                            const ScanLane<bf16, KD, NT>& ln, int t, int grp, int col,
                                            f32x4 (&hs)[KD / 16], bf16x8 (&hf)[KD / 32],
-                                           ChainOps<KD>& op)
+                                           ChainOps<KD>& op, const ColTaps& cv)
 {
     typedef Mma<bf16> MT;
     typedef bf16x8 Frag;
@@ -1388,7 +1439,7 @@ __device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restri
     lds_barrier();   // U is visible to the output wave; the next chunk has landed
 
     // ---- the next chunk's operands, then h' = gamma_L h + K^T (c o U)
-    chain_load<KD, NT>(op, ahead, ln, t, grp, lane);
+    chain_load<KD, NT, CONV>(op, ahead, cur, ln, t, grp, lane, cv);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) U[rt] *= fc[rt];
     const Frag df0 = MT::acc_frag(U[0], U[1]);
@@ -1460,14 +1511,18 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
         }
 }
 
-template <int KD, int NT, int NBUF>
+// CONV (whole-prefill form): vp points at the raw value rows before the
+// short convolution, whose taps and bias for value channel 0 of head 0 are at
+// wv and bv (bv may be null); the chain waves convolve them as they read them.
+template <int KD, int NT, int NBUF, bool CONV>
 __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_roles_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
     const bf16* __restrict__ vp, int64_t v_stride,
     const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
     const unsigned char* __restrict__ ws_rec,
-    int T_len, int H, int Hk, int V, int units, int groups)
+    int T_len, int H, int Hk, int V, int units, int groups,
+    const bf16* __restrict__ wv, const bf16* __restrict__ bv)
 {
     typedef bf16 T;
     typedef ScanBuf<T, KD, NT> SB;
@@ -1564,13 +1619,22 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
             hf[kb] = state_frag<T>(hs[2 * kb], hs[2 * kb + 1], grp);
             hand->h[kb][t][lane] = hf[kb];
         }
+        ColTaps cv{};
+        if constexpr (CONV) {
+            const int64_t chn = (int64_t)h * V + vc;
+            cv.w0 = (float)wv[chn * 4 + 0];
+            cv.w1 = (float)wv[chn * 4 + 1];
+            cv.w2 = (float)wv[chn * 4 + 2];
+            cv.w3 = (float)wv[chn * 4 + 3];
+            cv.b = bv ? (float)bv[chn] : 0.f;
+        }
         lds_barrier();
         ChainOps<KD> op;
-        chain_load<KD, NT>(op, &bufs[0], ln, t, grp, lane);
+        chain_load<KD, NT, CONV>(op, &bufs[0], nullptr, ln, t, grp, lane, cv);
         int b = 0;
         for (int c = 0; c < nchunks; ++c) {
             const int bn = b == NBUF - 1 ? 0 : b + 1;
-            role_chain<KD, NT>(&bufs[b], &bufs[bn], hand, ln, t, grp, col, hs, hf, op);
+            role_chain<KD, NT, CONV>(&bufs[b], &bufs[bn], hand, ln, t, grp, col, hs, hf, op, cv);
             lds_barrier();
             b = bn;
         }
@@ -1712,12 +1776,13 @@ static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const v
     return hipGetLastError();
 }
 
-template <int KD, int NT>
+template <int KD, int NT, bool CONV = false>
 static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, const void* v,
                                    int64_t vs, const float* S0, float* Sf, void* o,
                                    const int32_t* cu, const int32_t* offsets,
                                    const unsigned char* wsrec, int T_len, int H, int Hk, int V,
-                                   int N, hipStream_t stream)
+                                   int N, hipStream_t stream, const void* wv = nullptr,
+                                   const void* bv = nullptr)
 {
     const int units = N * H;
     const int groups = V / (16 * NT);
@@ -1726,12 +1791,13 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
     constexpr int NBUF = 3;
     constexpr size_t smem = NBUF * sizeof(SB) + 256 + sizeof(RoleHand<KD, NT>);
     static_assert(smem <= 160 * 1024, "scan staging fits in LDS");
-    auto kern = chunk_scan_roles_kernel<KD, NT, NBUF>;
+    auto kern = chunk_scan_roles_kernel<KD, NT, NBUF, CONV>;
     hipError_t err = set_smem(kern, smem);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3((NT + 2) * kWave), smem, stream,
                        (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf, (bf16*)o,
-                       cu, offsets, wsrec, T_len, H, Hk, V, units, groups);
+                       cu, offsets, wsrec, T_len, H, Hk, V, units, groups, (const bf16*)wv,
+                       (const bf16*)bv);
     return hipGetLastError();
 }
 
@@ -1747,11 +1813,11 @@ static inline ChunkWs carve(void* ws, int n_seqs) {
     return w;
 }
 
-template <typename T, int KD>
+template <typename T, int KD, bool GATES = false>
 static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, const float* g,
                                    const float* beta, const int32_t* cu, int n_seqs, int B,
                                    int T_len, int H, int Hk, float scale, int l2norm, void* ws,
-                                   hipStream_t stream)
+                                   hipStream_t stream, const PrepGates& gz = PrepGates{})
 {
     const bool packed = cu != nullptr;
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
@@ -1766,10 +1832,10 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         // a multiple of the 8 XCDs)
         const int64_t items = tiles * Hk;
         const int64_t blocks = (tiles + 7) / 8 * 8 * Hk;
-        auto kern = chunk_prep_kernel<T, KD>;
+        auto kern = chunk_prep_kernel<T, KD, GATES>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWave), 0, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
-                           Hk, scale, l2norm, w.rec, (int)items);
+                           Hk, scale, l2norm, w.rec, (int)items, gz);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1784,29 +1850,23 @@ static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const
 {
     const int N = cu ? n_seqs : B;
     const ChunkWs w = carve(const_cast<void*>(ws), n_seqs);
-    // columns per workgroup: enough workgroups to cover the 256 CUs, more waves
-    // per workgroup (shared staging) when there is parallelism to spare
     const int units = N * H;
     const int slabs = V / 16;
-    int nw = 1;
-    if (units * (slabs / 4) >= 512 && slabs % 4 == 0) nw = 4;
-    else if (units * (slabs / 2) >= 256 && slabs % 2 == 0) nw = 2;
-    if (nw == 4)
-        return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
-    // bf16 operands with one or two column groups per workgroup: the split-role
-    // step, which puts a second wave on each column group
     if constexpr (sizeof(T) == 2) {
-        if (nw == 2)
+        // bf16 operands: the split-role step, two column tiles per workgroup
+        // where that still gives a workgroup per CU (the same choice as the
+        // whole-prefill entry, so the two agree bit for bit)
+        if ((int64_t)units * (slabs / 2) >= 256)
             return launch_scan_roles<KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
         return launch_scan_roles<KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
+    } else {
+        // fp32 operands (the small parity workloads): four column tiles per
+        // workgroup (shared staging) when there is parallelism to spare, else
+        // one (the 2-wave instance does not get through the gfx950 backend)
+        if (units * (slabs / 4) >= 512 && slabs % 4 == 0)
+            return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
+        return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
     }
-    // the fp32 operand path (small parity workloads) runs with 1 or 4 waves per
-    // workgroup only: its 2-wave instance does not get through the gfx950 backend
-    if constexpr (sizeof(T) == 2) {
-        if (nw == 2)
-            return launch_scan<T, KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
-    }
-    return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
 }
 
 hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const float* g,
@@ -1814,6 +1874,7 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const
                                 int H, int Hk, int K, float scale, int l2norm, bool use_bf16,
                                 void* ws, hipStream_t stream)
 {
+    if (!cu) n_seqs = 0;   // dense: the workspace holds no sequence offsets
     if (use_bf16)
         return K == 128 ? launch_prepare_t<bf16, 128>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream)
                         : launch_prepare_t<bf16, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
@@ -1821,11 +1882,103 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const
                     : launch_prepare_t<float, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
 }
 
+// Whole prefill in three launches: the short convolution of the q and k
+// channels (into the workspace, after the records), chunk_prep forming the
+// gates from a and b itself, then the role-split scan convolving the value
+// rows as it reads them. Equal, bit for bit, to conv1d + gate_prepare +
+// chunk_prepare + chunk_scan (role-split) on the same inputs; y's value part,
+// g and beta are never written.
+hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w, const void* bias,
+                         void* y, int64_t ysb, int64_t yst, const int32_t* cu, int n_seqs, int B,
+                         int T_len, int C, int silu, bool bf16_io, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int B, int T_len, int H, int Hk, int K, int n_seqs, bool packed) {
+    return align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)) +
+           align256((size_t)B * T_len * 2 * Hk * K * sizeof(bf16));
+}
+
+template <int KD>
+static hipError_t launch_prefill_prepare_t(const bf16* x, int64_t xs, const bf16* cw,
+                                           const bf16* cb, const bf16* a, int64_t as,
+                                           const bf16* b, int64_t bs, const float* A_log,
+                                           const float* dt_bias, const int32_t* cu, int n_seqs,
+                                           int B, int T_len, int H, int Hk, float scale,
+                                           int l2norm, void* ws, hipStream_t stream)
+{
+    const bool packed = cu != nullptr;
+    const int64_t qkc = (int64_t)Hk * KD;            // channels of q (and of k)
+    bf16* qk = (bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)));
+    if (T_len > 0) {
+        hipError_t e = launch_conv1d(x, (int64_t)T_len * xs, xs, cw, cb, qk, (int64_t)T_len * 2 * qkc,
+                                     2 * qkc, cu, n_seqs, B, T_len, (int)(2 * qkc), 1, true, stream);
+        if (e != hipSuccess) return e;
+    }
+    PrepGates gz;
+    gz.a = a; gz.as = as;
+    gz.b = b; gz.bs = bs;
+    gz.A_log = A_log;
+    gz.dt_bias = dt_bias;
+    return launch_prepare_t<bf16, KD, true>(qk, qk + qkc, 2 * qkc, nullptr, nullptr, cu, n_seqs, B,
+                                            T_len, H, Hk, scale, l2norm, ws, stream, gz);
+}
+
+template <int KD>
+static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* cw, const bf16* cb,
+                                        const float* S0, float* Sf, void* o, const int32_t* cu,
+                                        int n_seqs, int B, int T_len, int H, int Hk, int V,
+                                        void* ws, hipStream_t stream)
+{
+    const bool packed = cu != nullptr;
+    const int64_t qkc = (int64_t)Hk * KD;
+    const bf16* qk = (const bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)));
+    const int N = packed ? n_seqs : B;
+    const ChunkWs w = carve(ws, n_seqs);
+    const int slabs = V / 16;
+    const bf16* wv = cw + 2 * qkc * 4;
+    const bf16* bv = cb ? cb + 2 * qkc : nullptr;
+    // two column tiles per workgroup where that still gives a workgroup per CU
+    if ((int64_t)N * H * (slabs / 2) >= 256)
+        return launch_scan_roles<KD, 2, true>(qk, qk + qkc, 2 * qkc, x + 2 * qkc, xs, S0, Sf, o, cu,
+                                              w.offsets, w.rec, T_len, H, Hk, V, N, stream, wv, bv);
+    return launch_scan_roles<KD, 1, true>(qk, qk + qkc, 2 * qkc, x + 2 * qkc, xs, S0, Sf, o, cu,
+                                          w.offsets, w.rec, T_len, H, Hk, V, N, stream, wv, bv);
+}
+
+hipError_t launch_prefill_prepare(const void* x, int64_t xs, const void* cw, const void* cb,
+                                  const void* a, int64_t as, const void* b, int64_t bs,
+                                  const float* A_log, const float* dt_bias, const int32_t* cu,
+                                  int n_seqs, int B, int T_len, int H, int Hk, int K, float scale,
+                                  int l2norm, void* ws, hipStream_t stream)
+{
+    if (!cu) n_seqs = 0;
+    if (K == 128)
+        return launch_prefill_prepare_t<128>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
+                                             (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias,
+                                             cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
+    return launch_prefill_prepare_t<64>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
+                                        (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias, cu,
+                                        n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
+}
+
+hipError_t launch_prefill_scan(const void* x, int64_t xs, const void* cw, const void* cb,
+                               const float* S0, float* Sf, void* o, const int32_t* cu, int n_seqs,
+                               int B, int T_len, int H, int Hk, int K, int V, void* ws,
+                               hipStream_t stream)
+{
+    if (!cu) n_seqs = 0;
+    if (K == 128)
+        return launch_prefill_scan_t<128>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb, S0,
+                                          Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream);
+    return launch_prefill_scan_t<64>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb, S0, Sf,
+                                     o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream);
+}
+
 hipError_t launch_chunk_scan(const void* q, const void* k, int64_t qks, const void* v, int64_t vs,
                              const float* S0, float* Sf, void* o, const int32_t* cu, int n_seqs,
                              int B, int T_len, int H, int Hk, int K, int V, bool use_bf16,
                              const void* ws, hipStream_t stream)
 {
+    if (!cu) n_seqs = 0;
     if (use_bf16)
         return K == 128 ? launch_scan_t<bf16, 128>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream)
                         : launch_scan_t<bf16, 64>(q, k, qks, v, vs, S0, Sf, o, cu, n_seqs, B, T_len, H, Hk, V, ws, stream);

@@ -168,6 +168,23 @@ __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
     return -expf(A_log) * gate_softplus(a + dt_bias);
 }
 
+// Short causal convolution of "ZzCompute" (PyTorch Helion Hackathon gallery),
+// item 1 "Causal Conv1d", width 4: the taps w0..w3 multiply x[t-3] .. x[t]
+// and are accumulated onto the bias in that order with fused multiply-adds;
+// SiLU is z / (1 + exp(-z)) with the reciprocal from v_rcp_f32 (~1 ulp).
+// Every kernel that applies the convolution uses these two, so they agree bit
+// for bit.
+__device__ __forceinline__ float conv_taps4(float w0, float w1, float w2, float w3, float bias,
+                                            float xm3, float xm2, float xm1, float x0) {
+    float acc = bias;
+    acc = fmaf(w0, xm3, acc);
+    acc = fmaf(w1, xm2, acc);
+    acc = fmaf(w2, xm1, acc);
+    acc = fmaf(w3, x0, acc);
+    return acc;
+}
+__device__ __forceinline__ float conv_silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Index of the packed sequence containing token t: the largest i with

@@ -136,12 +136,9 @@ __global__ __launch_bounds__(kGdpThreads) void conv1d_update_kernel(
     typename VV::ftype out;
 #pragma unroll
     for (int e = 0; e < VN; ++e) {
-        float acc = bias ? bs[e] : 0.f;
-        acc = fmaf(wt[0][e], win[0][e], acc);
-        acc = fmaf(wt[1][e], win[1][e], acc);
-        acc = fmaf(wt[2][e], win[2][e], acc);
-        acc = fmaf(wt[3][e], xf[e], acc);
-        out[e] = silu ? acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc)) : acc;   // (v_rcp_f32, ~1 ulp)
+        const float acc = conv_taps4(wt[0][e], wt[1][e], wt[2][e], wt[3][e], bias ? bs[e] : 0.f,
+                                     win[0][e], win[1][e], win[2][e], xf[e]);
+        out[e] = silu ? conv_silu(acc) : acc;
     }
     *yr = VV::from_float(out);
     // the window moves one token on

@@ -51,6 +51,13 @@ def lib():
     L.gdn_conv1d_update.argtypes = [vp, i64, vp, vp, vp, vp, vp, i64] + [i32] * 6 + [vp]
     L.gdn_gdp_prefill_prepare.argtypes = ([vp, i64, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
                                           + [i32] * 8 + [vp])
+    L.gdn_prefill_workspace_size.argtypes = [i32] * 8
+    L.gdn_prefill_workspace_size.restype = sz
+    L.gdn_prefill.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32]
+                              + [i32] * 6 + [f32, i32, i32, vp, sz, vp])
+    L.gdn_prefill_prepare.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, i32] + [i32] * 6
+                                      + [f32, i32, i32, vp, sz, vp])
+    L.gdn_prefill_scan.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6 + [i32, vp, sz, vp]
     return L
 
 
@@ -187,6 +194,69 @@ def test_chunk_workspace_size(lib):
     tiles_ub = (1000 + 63 * 10) // 64
     assert packed >= tiles_ub * 4 * rec_bf16
     assert lib.gdn_chunk_fwd_workspace_size(0, 10, 4, 4, 64, 64, 0, BF16) == 0
+
+
+def prefill(lib, **kw):
+    B, T, H, Hk, K, V = kw.get("B", 4), 4096, kw.get("H", 16), kw.get("Hk", 16), kw.get("K", 128), kw.get("V", 128)
+    C = 2 * Hk * K + H * V
+    need = lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    a = dict(x=P, xs=C, w=P2, bias=None, a=P3, as_=H, b=P3 + 64, bs=H, A_log=P4, dt=P4 + 64,
+             S0=None, Sf=P5, o=P6, cu=None, n=0, scale=1.0, l2=1, dtype=BF16, ws=WS, wsb=need)
+    a.update(kw)
+    return lib.gdn_prefill(a["x"], a["xs"], a["w"], a["bias"], a["a"], a["as_"], a["b"], a["bs"],
+                           a["A_log"], a["dt"], a["S0"], a["Sf"], a["o"], a["cu"], a["n"], B, T, H,
+                           Hk, K, V, a["scale"], a["l2"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation(lib):
+    for key in ("x", "w", "a", "b", "A_log", "dt", "o", "ws"):
+        assert prefill(lib, **{key: None}) == EINVAL, key
+    assert prefill(lib, H=16, Hk=3) == EINVAL            # H % Hk
+    assert prefill(lib, B=0) == EINVAL
+    assert prefill(lib, l2=2) == EINVAL
+    assert prefill(lib, cu=P6 + 4096, n=4) == EINVAL     # packed needs B == 1
+    assert prefill(lib, xs=6143) == EINVAL               # rows shorter than 2 Hk K + H V
+    assert prefill(lib, as_=8) == EINVAL and prefill(lib, bs=15) == EINVAL
+    assert prefill(lib, o=P) == EINVAL                   # o aliases x
+    assert prefill(lib, Sf=P6) == EINVAL                 # final state aliases o
+    assert prefill(lib, dtype=FP32) == EUNSUP            # bf16 only
+    assert prefill(lib, K=96) == EUNSUP and prefill(lib, V=32) == EUNSUP
+    assert prefill(lib, x=P + 2) == EUNSUP and prefill(lib, w=P2 + 8) == EUNSUP
+    assert prefill(lib, bias=P2 + 8) == EUNSUP and prefill(lib, o=P6 + 4) == EUNSUP
+    assert prefill(lib, xs=6148) == EUNSUP               # rows must stay 16-byte aligned
+    assert prefill(lib, xs=1 << 40) == EUNSUP            # 64 rows overflow 32-bit offsets
+    assert prefill(lib, ws=WS + 16) == EUNSUP
+    need = lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    assert prefill(lib, wsb=need - 1) == EWS
+
+
+def test_prefill_phase_validation(lib):
+    need = lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    prep = lambda **kw: lib.gdn_prefill_prepare(
+        kw.get("x", P), kw.get("xs", 6144), kw.get("w", P2), None, kw.get("a", P3), 16,
+        kw.get("b", P3 + 64), 16, kw.get("A_log", P4), P4 + 64, None, 0, 4, 4096, 16, kw.get("Hk", 16),
+        kw.get("K", 128), 128, 1.0, 1, kw.get("dtype", BF16), kw.get("ws", WS), kw.get("wsb", need), None)
+    scan = lambda **kw: lib.gdn_prefill_scan(
+        kw.get("x", P), kw.get("xs", 6144), kw.get("w", P2), None, None, kw.get("Sf", P5),
+        kw.get("o", P6), None, 0, 4, 4096, 16, 16, 128, kw.get("V", 128), kw.get("dtype", BF16),
+        kw.get("ws", WS), kw.get("wsb", need), None)
+    assert prep(a=None) == EINVAL and prep(A_log=None) == EINVAL and prep(ws=None) == EINVAL
+    assert prep(Hk=5) == EINVAL and prep(K=32) == EUNSUP and prep(dtype=FP32) == EUNSUP
+    assert prep(wsb=need - 1) == EWS and prep(xs=100) == EINVAL
+    assert scan(o=None) == EINVAL and scan(o=P) == EINVAL and scan(Sf=P6) == EINVAL
+    assert scan(V=96) == EUNSUP and scan(wsb=need - 1) == EWS and scan(w=None) == EINVAL
+
+
+def test_prefill_workspace_size(lib):
+    # the chunked forward's workspace, then the convolved q and k rows (bf16)
+    chunk = lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
+    qk = 4 * 4096 * 2 * 16 * 128 * 2
+    assert lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16) == chunk + qk
+    packed_chunk = lib.gdn_chunk_fwd_workspace_size(1, 1000, 4, 2, 64, 64, 10, BF16)
+    packed = lib.gdn_prefill_workspace_size(1, 1000, 4, 2, 64, 64, 10, BF16)
+    assert packed == (packed_chunk + 255) // 256 * 256 + (1000 * 2 * 2 * 64 * 2 + 255) // 256 * 256
+    assert lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, FP32) == 0
+    assert lib.gdn_prefill_workspace_size(0, 10, 4, 4, 64, 64, 0, BF16) == 0
 
 
 def decode(lib, **kw):
