@@ -3,11 +3,15 @@
 A step is one pass of the prefill hot path over one batch of the bf16 prefill
 workload (B=4, H=16, T=4096, K=V=128): causal conv1d + SiLU over the q|k|v
 channels (C = 6144), gate preparation, and the chunked forward (per-chunk WY
-solve, then the sequential state scan with the outputs and the final state).
-Inputs are resident in HBM before timing starts. `value` is tokens/s of the
-whole step (16,384 tokens per step). The chunked forward alone and the
-one-token Gated DeltaProduct decode (n=256 requests, M=2, H=32, G=16,
-P=N=128, 1000 steps, fp32 state updated in place) are reported beside it.
+solve, then the sequential state scan with the outputs and the final state),
+run as the library's whole-prefill entry in its three phases: the q/k
+convolution, the per-chunk solve (forming the gates itself) and the scan
+(convolving the value rows as it reads them). Inputs are resident in HBM
+before timing starts. `value` is tokens/s of the whole step (16,384 tokens
+per step). With --chain the same computation is also timed as the four
+per-step calls (conv1d, gates, chunk_prepare, chunk_scan). The one-token Gated
+DeltaProduct decode (n=256 requests, M=2, H=32, G=16, P=N=128, 1000 steps,
+fp32 state updated in place) and the steps around it are reported beside it.
 
 Per-kernel durations come from HIP events recorded between the launches on
 the stream the kernels run on (torch's current stream, which the binding
@@ -16,7 +20,7 @@ time per step; `traffic` comes from committed rocprofv3 counter summaries
 (profiles/traffic.json) and is null when absent or when the kernel's source
 has changed since they were taken.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--chain]
 """
 from __future__ import annotations
 
@@ -35,10 +39,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "linear_attention_ssm_amd/csrc/"
 KERNELS = {   # bench op -> (kernel symbol stem, source file)
-    "conv1d": ("conv1d_causal_kernel", CSRC + "conv1d.hip"),
-    "gate_prepare": ("gate_prepare_kernel", CSRC + "gate.hip"),
-    "chunk_prepare": ("chunk_prep_kernel", CSRC + "chunk.hip"),
-    "chunk_scan": ("chunk_scan_roles_kernel", CSRC + "chunk.hip"),
+    "prefill_conv": ("conv1d_causal_kernel", CSRC + "conv1d.hip"),
+    "prefill_prepare": ("chunk_prep_kernelIDF16bLi128ELb1E", CSRC + "chunk.hip"),
+    "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", CSRC + "chunk.hip"),
     "decode": ("gdp_decode_kernel", CSRC + "decode.hip"),
 }
 REC_BYTES_BF16 = 2 * 6 * 64 * 16 + 4 * 64 * 4   # per (chunk, value head) workspace record
@@ -57,6 +60,8 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration runs)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--chain", action="store_true",
+                   help="also time the four-call chain (conv1d, gates, chunk_prepare, chunk_scan)")
     p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
                    help="turn a rocprofv3 --stats kernel_stats.csv into a profiles/ summary")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -79,7 +84,18 @@ def prefill_accounting(B, T, H, Hk, K, V):
     state = B * H * K * V * 4
     rec = chunks * H * REC_BYTES_BF16
     d, Cc = K, 64
+    ab = 2 * tok * H * 2
     return {
+        # the three launches of the whole prefill: q/k conv (x's q|k channels in,
+        # q|k rows out), per-chunk solve (q|k rows and a, b in; records out), scan
+        # (q|k rows, x's value channels, records in; o and the final state out)
+        "prefill_conv": {"bytes": 2 * qk + 2 * Hk * K * 4 * 2},
+        "prefill_prepare": {"bytes": qk + ab + rec,
+                            "flops": chunks * (Hk * 2 * 10 * 16 * 16 * K * 2 + H * 64 ** 3 / 3)},
+        "prefill_scan": {"bytes": qk + v + rec + o + state,
+                         "flops": chunks * H * (3 * 64 * K * V * 2 + 2 * 0.5 * 64 * 64 * V * 2)},
+        # the whole step, single-pass: x, a, b in; o and the final state out
+        "prefill": {"bytes": tok * C * 2 + ab + o + state},
         "conv1d": {"bytes": 2 * tok * C * 2 + C * 4 * 2},
         "gate_prepare": {"bytes": 2 * tok * H * 2 + gb},
         "chunk_prepare": {"bytes": qk + gb + rec,
@@ -150,7 +166,58 @@ def cpu_baseline(w, batch):
                       f"conv1d + gates + timestep recurrence), {dt:.2f} s on {used} threads"}
 
 
+def _timed_steps(args, torch, stream, step, n_ev):
+    """W untimed steps, then K timed ones with n_ev events each; returns the
+    events and the wall time per step (ms)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    return evs, (time.perf_counter() - t0) * 1e3 / args.steps
+
+
 def run_prefill(args, gdn, wl, torch, dev, stream):
+    """The whole prefill through its three phase entry points (each one kernel),
+    with events between them."""
+    w = wl.WORKLOADS["prefill"]
+    d = wl.prefill_inputs(w)
+    x, cw = d["x"].to(dev), d["w"].to(dev)
+    a, b = d["a"].to(dev), d["b"].to(dev)
+    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
+    o = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((w.B, w.H, w.K, w.V), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(w.B, w.T, w.H, w.Hk, w.K, w.V, 0),
+                     dtype=torch.uint8, device=dev)
+    dims = dict(Hk=w.Hk, K=w.K, H=w.H, V=w.V)
+    ops = ["prefill_conv", "prefill_prepare", "prefill_scan"]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        gdn.gdn_prefill_conv(x, cw, ws, **dims)
+        if evs:
+            evs[1].record(stream)
+        gdn.gdn_prefill_prepare(a, b, A_log, dt_bias, ws, **dims)
+        if evs:
+            evs[2].record(stream)
+        gdn.gdn_prefill_scan(x, cw, ws, o=o, final_state=fs, **dims)
+        if evs:
+            evs[3].record(stream)
+
+    evs, step_ms = _timed_steps(args, torch, stream, step, 4)
+    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+             for j, op in enumerate(ops)}
+    return w, op_ms, step_ms
+
+
+def run_chain(args, gdn, wl, torch, dev, stream):
+    """The same computation as four calls: conv1d over all of q|k|v, gates,
+    chunk_prepare, chunk_scan (the per-step entry points)."""
     w = wl.WORKLOADS["prefill"]
     d = wl.prefill_inputs(w)
     x, cw = d["x"].to(dev), d["w"].to(dev)
@@ -182,19 +249,11 @@ def run_prefill(args, gdn, wl, torch, dev, stream):
         if evs:
             evs[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+    evs, step_ms = _timed_steps(args, torch, stream, step, 5)
+    op_us = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps * 1e3
              for j, op in enumerate(ops)}
-    return w, op_ms, wall * 1e3 / args.steps
+    tokens = w.B * w.T
+    return {"us": step_ms * 1e3, "tokens_per_s": tokens / (step_ms / 1e3), "ops_us": op_us}
 
 
 def run_decode(args, gdn, wl, torch, dev, stream):
@@ -333,11 +392,22 @@ def run_gdp_steps(gdn, wl, torch, dev, stream):
 
 
 def _kernel_stem(name):
+    """Readable name of a kernel symbol: our mangled template kernels become
+    name<args> (bf16 template arguments are beyond the image's c++filt)."""
     import re
+    m = re.match(r"_ZN3gdn\d+(\w+?)I(.*?)EEv", name)
+    if m:
+        parts = []
+        for tok in re.finditer(r"DF16b|Li(\d+)E|Lb([01])E|f", m.group(2)):
+            s = tok.group(0)
+            parts.append("bf16" if s == "DF16b" else "float" if s == "f" else
+                         tok.group(1) if tok.group(1) else ("true" if tok.group(2) == "1" else "false"))
+        return f"{m.group(1)}<{', '.join(parts)}>"
     m = re.match(r"_ZN3gdn\d+(\w+?)I", name)
     if m:
         return m.group(1)
-    return name.split("(")[0][:60]
+    s = name.split("(")[0]
+    return (s[5:] if s.startswith("void ") else s)[:60]
 
 
 def _phases(rows, id_key, name_key):
@@ -491,17 +561,15 @@ def main():
                            "algorithmic_bytes": acc[dom]["bytes"]}
         if "flops" in acc[dom]:
             out["roofline"]["mfma_frac"] = acc[dom]["flops"] / sec / (BF16_PEAK_TFLOPS * 1e12)
-        chunk_s = (op_ms["chunk_prepare"] + op_ms["chunk_scan"]) / 1e3
-        out["chunk_fwd"] = {
-            "tokens_per_s": tokens / chunk_s, "us": chunk_s * 1e6,
-            "mfma_frac": acc["chunk_fwd"]["flops"] / chunk_s / (BF16_PEAK_TFLOPS * 1e12),
-            "hbm_frac": acc["chunk_fwd"]["bytes"] / chunk_s / (HBM_PEAK_GBS * 1e9),
-            "algorithmic_flops": acc["chunk_fwd"]["flops"],
-            "algorithmic_bytes": acc["chunk_fwd"]["bytes"]}
+        step_s = step_ms / 1e3
+        out["step"] = {"algorithmic_bytes": acc["prefill"]["bytes"],
+                       "hbm_frac": acc["prefill"]["bytes"] / step_s / (HBM_PEAK_GBS * 1e9)}
         out["kernels"] = {op: {"us": op_ms[op] * 1e3,
                                "achieved_GBs": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9,
                                "hbm_frac": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9 / HBM_PEAK_GBS}
                           for op in op_ms}
+    if args.chain and args.only != "decode":
+        out["chain"] = run_chain(args, gdn, wl, torch, dev, stream)
     if args.only != "prefill" and not args.no_decode:
         out["decode"] = run_decode(args, gdn, wl, torch, dev, stream)
         out["gdp_steps"] = run_gdp_steps(gdn, wl, torch, dev, stream)

@@ -1882,10 +1882,10 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const
                     : launch_prepare_t<float, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
 }
 
-// Whole prefill in three launches: the short convolution of the q and k
-// channels (into the workspace, after the records), chunk_prep forming the
-// gates from a and b itself, then the role-split scan convolving the value
-// rows as it reads them. Equal, bit for bit, to conv1d + gate_prepare +
+// Whole prefill in three launches (conv, prepare and scan phases): the short
+// convolution of the q and k channels (into the workspace, after the
+// records), chunk_prep forming the gates from a and b itself, then the
+// role-split scan convolving the value rows as it reads them. Equal, bit for bit, to conv1d + gate_prepare +
 // chunk_prepare + chunk_scan (role-split) on the same inputs; y's value part,
 // g and beta are never written.
 hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w, const void* bias,
@@ -1897,22 +1897,32 @@ size_t prefill_workspace_bytes(int B, int T_len, int H, int Hk, int K, int n_seq
            align256((size_t)B * T_len * 2 * Hk * K * sizeof(bf16));
 }
 
-template <int KD>
-static hipError_t launch_prefill_prepare_t(const bf16* x, int64_t xs, const bf16* cw,
-                                           const bf16* cb, const bf16* a, int64_t as,
-                                           const bf16* b, int64_t bs, const float* A_log,
-                                           const float* dt_bias, const int32_t* cu, int n_seqs,
-                                           int B, int T_len, int H, int Hk, float scale,
-                                           int l2norm, void* ws, hipStream_t stream)
+// The q / k rows of the whole-prefill form: after the records in the workspace.
+static inline bf16* prefill_qk(void* ws, int B, int T_len, int H, int n_seqs) {
+    return (bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, n_seqs > 0, true)));
+}
+
+hipError_t launch_prefill_conv(const void* x, int64_t xs, const void* cw, const void* cb,
+                               const int32_t* cu, int n_seqs, int B, int T_len, int H, int Hk,
+                               int K, void* ws, hipStream_t stream)
 {
-    const bool packed = cu != nullptr;
-    const int64_t qkc = (int64_t)Hk * KD;            // channels of q (and of k)
-    bf16* qk = (bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)));
-    if (T_len > 0) {
-        hipError_t e = launch_conv1d(x, (int64_t)T_len * xs, xs, cw, cb, qk, (int64_t)T_len * 2 * qkc,
-                                     2 * qkc, cu, n_seqs, B, T_len, (int)(2 * qkc), 1, true, stream);
-        if (e != hipSuccess) return e;
-    }
+    if (!cu) n_seqs = 0;
+    if (T_len == 0) return hipSuccess;
+    const int64_t qkc = (int64_t)Hk * K;             // channels of q (and of k)
+    return launch_conv1d(x, (int64_t)T_len * xs, xs, cw, cb, prefill_qk(ws, B, T_len, H, n_seqs),
+                         (int64_t)T_len * 2 * qkc, 2 * qkc, cu, n_seqs, B, T_len, (int)(2 * qkc), 1,
+                         true, stream);
+}
+
+template <int KD>
+static hipError_t launch_prefill_prepare_t(const bf16* a, int64_t as, const bf16* b, int64_t bs,
+                                           const float* A_log, const float* dt_bias,
+                                           const int32_t* cu, int n_seqs, int B, int T_len, int H,
+                                           int Hk, float scale, int l2norm, void* ws,
+                                           hipStream_t stream)
+{
+    const int64_t qkc = (int64_t)Hk * KD;
+    const bf16* qk = prefill_qk(ws, B, T_len, H, n_seqs);
     PrepGates gz;
     gz.a = a; gz.as = as;
     gz.b = b; gz.bs = bs;
@@ -1928,10 +1938,9 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
                                         int n_seqs, int B, int T_len, int H, int Hk, int V,
                                         void* ws, hipStream_t stream)
 {
-    const bool packed = cu != nullptr;
     const int64_t qkc = (int64_t)Hk * KD;
-    const bf16* qk = (const bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)));
-    const int N = packed ? n_seqs : B;
+    const bf16* qk = prefill_qk(ws, B, T_len, H, n_seqs);
+    const int N = cu ? n_seqs : B;
     const ChunkWs w = carve(ws, n_seqs);
     const int slabs = V / 16;
     const bf16* wv = cw + 2 * qkc * 4;
@@ -1944,19 +1953,16 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
                                           w.offsets, w.rec, T_len, H, Hk, V, N, stream, wv, bv);
 }
 
-hipError_t launch_prefill_prepare(const void* x, int64_t xs, const void* cw, const void* cb,
-                                  const void* a, int64_t as, const void* b, int64_t bs,
+hipError_t launch_prefill_prepare(const void* a, int64_t as, const void* b, int64_t bs,
                                   const float* A_log, const float* dt_bias, const int32_t* cu,
                                   int n_seqs, int B, int T_len, int H, int Hk, int K, float scale,
                                   int l2norm, void* ws, hipStream_t stream)
 {
     if (!cu) n_seqs = 0;
     if (K == 128)
-        return launch_prefill_prepare_t<128>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
-                                             (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias,
+        return launch_prefill_prepare_t<128>((const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias,
                                              cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
-    return launch_prefill_prepare_t<64>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
-                                        (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias, cu,
+    return launch_prefill_prepare_t<64>((const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias, cu,
                                         n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
 }
 

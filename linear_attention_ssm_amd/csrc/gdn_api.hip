@@ -25,8 +25,10 @@ hipError_t launch_chunk_scan(const void* q, const void* k, int64_t qks, const vo
                              int B, int T_len, int H, int Hk, int K, int V, bool use_bf16,
                              const void* ws, hipStream_t stream);
 size_t prefill_workspace_bytes(int B, int T_len, int H, int Hk, int K, int n_seqs, bool packed);
-hipError_t launch_prefill_prepare(const void* x, int64_t xs, const void* cw, const void* cb,
-                                  const void* a, int64_t as, const void* b, int64_t bs,
+hipError_t launch_prefill_conv(const void* x, int64_t xs, const void* cw, const void* cb,
+                               const int32_t* cu, int n_seqs, int B, int T_len, int H, int Hk,
+                               int K, void* ws, hipStream_t stream);
+hipError_t launch_prefill_prepare(const void* a, int64_t as, const void* b, int64_t bs,
                                   const float* A_log, const float* dt_bias, const int32_t* cu,
                                   int n_seqs, int B, int T_len, int H, int Hk, int K, float scale,
                                   int l2norm, void* ws, hipStream_t stream);
@@ -222,8 +224,10 @@ size_t gdn_prefill_workspace_size(int B, int T, int H, int Hk, int K, int V, int
     return gdn::prefill_workspace_bytes(B, T, H, Hk, K, packed ? n_seqs : 0, packed);
 }
 
-// Checks shared by the whole-prefill entry points (prepare, scan and both).
-static int check_prefill(const void* x, int64_t x_stride_t, const void* conv_w,
+// Checks shared by the whole-prefill entry points (the three phases and all
+// of them); need_x: x and conv_w are read, need_gates: a, b and the gate
+// parameters, need_out: o and the states.
+static int check_prefill(bool need_x, const void* x, int64_t x_stride_t, const void* conv_w,
                          const void* conv_bias, bool need_gates, const void* a,
                          int64_t a_stride_row, const void* b, int64_t b_stride_row,
                          const float* A_log, const float* dt_bias, bool need_out,
@@ -232,26 +236,29 @@ static int check_prefill(const void* x, int64_t x_stride_t, const void* conv_w,
                          int dtype, const void* ws, size_t ws_bytes)
 {
     if (B < 1 || T < 0 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_EINVAL;
-    if (!ws || !conv_w) return GDN_EINVAL;
+    if (!ws || (need_x && !conv_w)) return GDN_EINVAL;
     if (need_gates && (!A_log || !dt_bias)) return GDN_EINVAL;
-    if (T > 0 && (!x || (need_gates && (!a || !b)) || (need_out && !o)))   // no tokens: may be NULL
-        return GDN_EINVAL;
+    if (T > 0 && ((need_x && !x) || (need_gates && (!a || !b)) || (need_out && !o)))
+        return GDN_EINVAL;   // with no tokens the token tensors may be NULL
     if (qk_l2norm != 0 && qk_l2norm != 1) return GDN_EINVAL;
     if (cu && (B != 1 || n_seqs < 1)) return GDN_EINVAL;
     if ((int64_t)B * T > INT_MAX) return GDN_EINVAL;
     if (dtype != GDN_BF16 || !head_dim_ok(K) || !head_dim_ok(V)) return GDN_EUNSUPPORTED;
     const int64_t C = 2 * (int64_t)Hk * K + (int64_t)H * V;
-    if (x_stride_t < C) return GDN_EINVAL;
+    if (need_x && x_stride_t < C) return GDN_EINVAL;
     if (need_gates && (a_stride_row < H || b_stride_row < H)) return GDN_EINVAL;
-    if (need_out && T > 0 && o == x) return GDN_EINVAL;
+    if (need_x && need_out && T > 0 && o == x) return GDN_EINVAL;
     if (need_out && Sf && (const void*)Sf == o) return GDN_EINVAL;
-    if (!aligned16(x) || !aligned16(conv_w) || (conv_bias && !aligned16(conv_bias)) ||
-        (need_out && !aligned16(o)) || !stride16(x_stride_t, dtype) || (S0 && !aligned16(S0)) ||
-        (Sf && !aligned16(Sf)) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    if ((need_x && (!aligned16(x) || !aligned16(conv_w) || (conv_bias && !aligned16(conv_bias)) ||
+                    !stride16(x_stride_t, dtype))) ||
+        (need_out && !aligned16(o)) || (S0 && !aligned16(S0)) || (Sf && !aligned16(Sf)) ||
+        (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return GDN_EUNSUPPORTED;
     // a 64-token chunk is addressed with 32-bit byte offsets; the q/k
     // convolution's grid is one-dimensional
-    if (64 * x_stride_t * 2 > INT_MAX || (int64_t)64 * H * V > INT_MAX) return GDN_EUNSUPPORTED;
+    if ((need_x && 64 * x_stride_t * 2 > INT_MAX) || (int64_t)64 * H * V > INT_MAX ||
+        (int64_t)64 * 2 * Hk * K * 2 > INT_MAX)
+        return GDN_EUNSUPPORTED;
     if ((int64_t)((T + 15) / 16 * B + 7) * ((2 * Hk * K / 8 + 255) / 256) > INT_MAX)
         return GDN_EUNSUPPORTED;
     const size_t need = gdn::prefill_workspace_bytes(B, T, H, Hk, K, cu ? n_seqs : 0, cu != nullptr);
@@ -259,22 +266,32 @@ static int check_prefill(const void* x, int64_t x_stride_t, const void* conv_w,
     return GDN_OK;
 }
 
-int gdn_prefill_prepare(const void* x, int64_t x_stride_t, const void* conv_w,
-                        const void* conv_bias, const void* a, int64_t a_stride_row, const void* b,
-                        int64_t b_stride_row, const float* A_log, const float* dt_bias,
-                        const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K,
-                        int V, float scale, int qk_l2norm, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream)
+int gdn_prefill_conv(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
+                     const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K,
+                     int V, int dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
-    const int st = check_prefill(x, x_stride_t, conv_w, conv_bias, true, a, a_stride_row, b,
+    const int st = check_prefill(true, x, x_stride_t, conv_w, conv_bias, false, nullptr, 0, nullptr,
+                                 0, nullptr, nullptr, false, nullptr, nullptr, nullptr, cu_seqlens,
+                                 n_seqs, B, T, H, Hk, K, V, 0, dtype, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    return status_from(gdn::launch_prefill_conv(x, x_stride_t, conv_w, conv_bias, cu_seqlens, n_seqs,
+                                                B, T, H, Hk, K, workspace, (hipStream_t)stream));
+}
+
+int gdn_prefill_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
+                        const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                        int n_seqs, int B, int T, int H, int Hk, int K, int V, float scale,
+                        int qk_l2norm, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    const int st = check_prefill(false, nullptr, 0, nullptr, nullptr, true, a, a_stride_row, b,
                                  b_stride_row, A_log, dt_bias, false, nullptr, nullptr, nullptr,
                                  cu_seqlens, n_seqs, B, T, H, Hk, K, V, qk_l2norm, dtype, workspace,
                                  workspace_bytes);
     if (st != GDN_OK) return st;
-    return status_from(gdn::launch_prefill_prepare(x, x_stride_t, conv_w, conv_bias, a, a_stride_row,
-                                                   b, b_stride_row, A_log, dt_bias, cu_seqlens,
-                                                   n_seqs, B, T, H, Hk, K, scale, qk_l2norm,
-                                                   workspace, (hipStream_t)stream));
+    return status_from(gdn::launch_prefill_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias,
+                                                   cu_seqlens, n_seqs, B, T, H, Hk, K, scale,
+                                                   qk_l2norm, workspace, (hipStream_t)stream));
 }
 
 int gdn_prefill_scan(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
@@ -282,9 +299,10 @@ int gdn_prefill_scan(const void* x, int64_t x_stride_t, const void* conv_w, cons
                      const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K,
                      int V, int dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
-    const int st = check_prefill(x, x_stride_t, conv_w, conv_bias, false, nullptr, 0, nullptr, 0,
-                                 nullptr, nullptr, true, initial_state, final_state, o, cu_seqlens,
-                                 n_seqs, B, T, H, Hk, K, V, 0, dtype, workspace, workspace_bytes);
+    const int st = check_prefill(true, x, x_stride_t, conv_w, conv_bias, false, nullptr, 0, nullptr,
+                                 0, nullptr, nullptr, true, initial_state, final_state, o,
+                                 cu_seqlens, n_seqs, B, T, H, Hk, K, V, 0, dtype, workspace,
+                                 workspace_bytes);
     if (st != GDN_OK) return st;
     return status_from(gdn::launch_prefill_scan(x, x_stride_t, conv_w, conv_bias, initial_state,
                                                 final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K,
@@ -298,15 +316,18 @@ int gdn_prefill(const void* x, int64_t x_stride_t, const void* conv_w, const voi
                 int H, int Hk, int K, int V, float scale, int qk_l2norm, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    int st = check_prefill(x, x_stride_t, conv_w, conv_bias, true, a, a_stride_row, b, b_stride_row,
-                           A_log, dt_bias, true, initial_state, final_state, o, cu_seqlens, n_seqs,
-                           B, T, H, Hk, K, V, qk_l2norm, dtype, workspace, workspace_bytes);
+    int st = check_prefill(true, x, x_stride_t, conv_w, conv_bias, true, a, a_stride_row, b,
+                           b_stride_row, A_log, dt_bias, true, initial_state, final_state, o,
+                           cu_seqlens, n_seqs, B, T, H, Hk, K, V, qk_l2norm, dtype, workspace,
+                           workspace_bytes);
     if (st != GDN_OK) return st;
     if (T > 0 && (o == a || o == b)) return GDN_EINVAL;
-    hipError_t e = gdn::launch_prefill_prepare(x, x_stride_t, conv_w, conv_bias, a, a_stride_row, b,
-                                               b_stride_row, A_log, dt_bias, cu_seqlens, n_seqs, B,
-                                               T, H, Hk, K, scale, qk_l2norm, workspace,
-                                               (hipStream_t)stream);
+    hipError_t e = gdn::launch_prefill_conv(x, x_stride_t, conv_w, conv_bias, cu_seqlens, n_seqs, B,
+                                            T, H, Hk, K, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return GDN_ELAUNCH;
+    e = gdn::launch_prefill_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias, cu_seqlens,
+                                    n_seqs, B, T, H, Hk, K, scale, qk_l2norm, workspace,
+                                    (hipStream_t)stream);
     if (e != hipSuccess) return GDN_ELAUNCH;
     return status_from(gdn::launch_prefill_scan(x, x_stride_t, conv_w, conv_bias, initial_state,
                                                 final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K,

@@ -157,8 +157,8 @@ def test_prefill_phases_equal_whole(gpu):
     Hk, K, H, V = d["Hk"], d["K"], d["H"], d["V"]
     ws = torch.empty(gpu.gdn_prefill_workspace_size(1, d["T"], H, Hk, K, V, 0), dtype=torch.uint8,
                      device=DEV)
-    gpu.gdn_prefill_prepare(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"], ws, Hk=Hk,
-                            K=K, H=H, V=V)
+    gpu.gdn_prefill_conv(t["x"], t["w"], ws, Hk=Hk, K=K, H=H, V=V)
+    gpu.gdn_prefill_prepare(t["a"], t["b"], t["A_log"], t["dt_bias"], ws, Hk=Hk, K=K, H=H, V=V)
     o, sf = gpu.gdn_prefill_scan(t["x"], t["w"], ws, Hk=Hk, K=K, H=H, V=V, initial_state=S0)
     torch.cuda.synchronize()
     _equal((o, sf), _fused(gpu, d), "phases")
