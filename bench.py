@@ -4,8 +4,8 @@ A step is one pass of the prefill hot path over one batch of the bf16 prefill
 workload (B=4, H=16, T=4096, K=V=128): causal conv1d + SiLU over the q|k|v
 channels (C = 6144), gate preparation, and the chunked forward (per-chunk WY
 solve, then the sequential state scan with the outputs and the final state),
-run as the library's whole-prefill entry in its three phases: the q/k
-convolution, the per-chunk solve (forming the gates itself) and the scan
+run as the library's whole-prefill entry in its two phases: the per-chunk
+solve (convolving the q and k rows and forming the gates itself) and the scan
 (convolving the value rows as it reads them). Inputs are resident in HBM
 before timing starts. `value` is tokens/s of the whole step (16,384 tokens
 per step). With --chain the same computation is also timed as the four
@@ -39,8 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "linear_attention_ssm_amd/csrc/"
 KERNELS = {   # bench op -> (kernel symbol stem, source file)
-    "prefill_conv": ("conv1d_causal_kernel", CSRC + "conv1d.hip"),
-    "prefill_prepare": ("chunk_prep_kernelIDF16bLi128ELb1E", CSRC + "chunk.hip"),
+    "prefill_prepare": ("chunk_prep_kernelIDF16bLi128ELb1ELb1E", CSRC + "chunk.hip"),
     "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", CSRC + "chunk.hip"),
     "decode": ("gdp_decode_kernel", CSRC + "decode.hip"),
 }
@@ -86,11 +85,10 @@ def prefill_accounting(B, T, H, Hk, K, V):
     d, Cc = K, 64
     ab = 2 * tok * H * 2
     return {
-        # the three launches of the whole prefill: q/k conv (x's q|k channels in,
-        # q|k rows out), per-chunk solve (q|k rows and a, b in; records out), scan
-        # (q|k rows, x's value channels, records in; o and the final state out)
-        "prefill_conv": {"bytes": 2 * qk + 2 * Hk * K * 4 * 2},
-        "prefill_prepare": {"bytes": qk + ab + rec,
+        # the two launches of the whole prefill: per-chunk solve (x's q|k channels
+        # and a, b in; convolved q|k rows and records out), scan (q|k rows, x's
+        # value channels, records in; o and the final state out)
+        "prefill_prepare": {"bytes": 2 * qk + 2 * Hk * K * 4 * 2 + ab + rec,
                             "flops": chunks * (Hk * 2 * 10 * 16 * 16 * K * 2 + H * 64 ** 3 / 3)},
         "prefill_scan": {"bytes": qk + v + rec + o + state,
                          "flops": chunks * H * (3 * 64 * K * V * 2 + 2 * 0.5 * 64 * 64 * V * 2)},
@@ -205,22 +203,19 @@ def run_prefill(args, gdn, wl, torch, dev, stream):
     ws = torch.empty(gdn.gdn_prefill_workspace_size(w.B, w.T, w.H, w.Hk, w.K, w.V, 0),
                      dtype=torch.uint8, device=dev)
     dims = dict(Hk=w.Hk, K=w.K, H=w.H, V=w.V)
-    ops = ["prefill_conv", "prefill_prepare", "prefill_scan"]
+    ops = ["prefill_prepare", "prefill_scan"]
 
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        gdn.gdn_prefill_conv(x, cw, ws, **dims)
+        gdn.gdn_prefill_prepare(x, cw, a, b, A_log, dt_bias, ws, **dims)
         if evs:
             evs[1].record(stream)
-        gdn.gdn_prefill_prepare(a, b, A_log, dt_bias, ws, **dims)
-        if evs:
-            evs[2].record(stream)
         gdn.gdn_prefill_scan(x, cw, ws, o=o, final_state=fs, **dims)
         if evs:
-            evs[3].record(stream)
+            evs[2].record(stream)
 
-    evs, step_ms = _timed_steps(args, torch, stream, step, 4)
+    evs, step_ms = _timed_steps(args, torch, stream, step, 3)
     op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
              for j, op in enumerate(ops)}
     return w, op_ms, step_ms

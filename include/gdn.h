@@ -186,11 +186,10 @@ int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t,
  *     gdn_gate_prepare(a, b, A_log, dt_bias)           -> g, beta,
  *     gdn_chunk_fwd(q, k, v, g, beta, ...)              -> o, final_state
  * on the same bf16 inputs, bit for bit (the same formulas, rounding points
- * and accumulation order), in three kernel launches instead of four: the
- * convolution of the q and k channels, the per-chunk solve forming the gates
- * itself, and the scan convolving the value rows as it reads them. The value
- * part of y, g and beta are never written (the convolved q and k rows live
- * in the workspace).
+ * and accumulation order), in two kernel launches instead of four: the
+ * per-chunk solve convolving the q and k rows and forming the gates itself,
+ * and the scan convolving the value rows as it reads them. y, g and beta are
+ * never written (the convolved q and k rows live in the workspace).
  *   x        [B*T, C] bf16 token rows before the convolution, C = 2*Hk*K +
  *            H*V channels laid out q [Hk][K] | k [Hk][K] | v [H][V]; row t at
  *            x + t*x_stride_t (batch row b starts at token b*T).
@@ -209,18 +208,19 @@ int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t,
  * (GDN_EINVAL). gdn_prefill_workspace_size returns 0 for a dtype other than
  * GDN_BF16, a head dim other than 64 or 128, or invalid sizes.
  *
- * gdn_prefill_conv / gdn_prefill_prepare / gdn_prefill_scan -- the three
- * phases of gdn_prefill (the same arguments where they take them, the same
- * workspace), exposed so that each kernel can be launched and timed on its
- * own; gdn_prefill(...) is exactly the three in this order on one stream:
- *   conv     the q and k channels of x convolved (+ SiLU) into `workspace`;
- *   prepare  the gates from a, b, A_log, dt_bias and the per-chunk solve of
- *            gdn_chunk_prepare on those rows, into `workspace`;
+ * gdn_prefill_prepare / gdn_prefill_scan -- the two phases of gdn_prefill
+ * (the same arguments where they take them, the same workspace), exposed so
+ * that each kernel can be launched and timed on its own; gdn_prefill(...) is
+ * exactly the two in this order on one stream:
+ *   prepare  the q and k channels of x convolved (+ SiLU) into `workspace`,
+ *            the gates formed from a, b, A_log, dt_bias, and the per-chunk
+ *            solve of gdn_chunk_prepare on those rows, into `workspace`;
  *   scan     the state scan and outputs of gdn_chunk_scan, the value rows of x
  *            convolved as they are read.
- * Each phase reads what the phases before it left in `workspace`, which must
- * come from calls with the same inputs, cu_seqlens, sizes, scale and
- * qk_l2norm (the workspace is otherwise unchecked).
+ * The scan reads what the prepare call left in `workspace`, which must come
+ * from a call with the same x, conv_w, conv_bias, a, b, gate parameters,
+ * cu_seqlens, sizes, scale and qk_l2norm (the workspace is otherwise
+ * unchecked).
  * ---------------------------------------------------------------------- */
 size_t gdn_prefill_workspace_size(int B, int T, int H, int Hk, int K, int V, int n_seqs,
                                   int dtype);
@@ -234,12 +234,9 @@ int gdn_prefill(const void* x, int64_t x_stride_t, const void* conv_w, const voi
                 float scale, int qk_l2norm, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-int gdn_prefill_conv(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
-                     const int32_t* cu_seqlens, int n_seqs,
-                     int B, int T, int H, int Hk, int K, int V, int dtype,
-                     void* workspace, size_t workspace_bytes, void* stream);
-
-int gdn_prefill_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
+int gdn_prefill_prepare(const void* x, int64_t x_stride_t, const void* conv_w,
+                        const void* conv_bias, const void* a, int64_t a_stride_row,
+                        const void* b, int64_t b_stride_row,
                         const float* A_log, const float* dt_bias,
                         const int32_t* cu_seqlens, int n_seqs,
                         int B, int T, int H, int Hk, int K, int V,

@@ -20,8 +20,7 @@ import torch
 __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
-    "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_conv", "gdn_prefill_prepare",
-    "gdn_prefill_scan",
+    "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
     "gdn_recurrent_decode", "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
     "gdp_prefill", "prefill_chain", "split_qkv",
 ]
@@ -57,10 +56,8 @@ _lib.gdn_prefill_workspace_size.restype = _sz
 _lib.gdn_prefill.argtypes = ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                               _vp, _i32] + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_prefill.restype = _i32
-_lib.gdn_prefill_conv.argtypes = [_vp, _i64, _vp, _vp, _vp, _i32] + [_i32] * 6 + [_i32, _vp, _sz, _vp]
-_lib.gdn_prefill_conv.restype = _i32
-_lib.gdn_prefill_prepare.argtypes = ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32] + [_i32] * 6
-                                     + [_f32, _i32, _i32, _vp, _sz, _vp])
+_lib.gdn_prefill_prepare.argtypes = ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32]
+                                     + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_prefill_prepare.restype = _i32
 _lib.gdn_prefill_scan.argtypes = ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32] + [_i32] * 6
                                   + [_i32, _vp, _sz, _vp])
@@ -312,7 +309,7 @@ def gdn_prefill(x: torch.Tensor, w: torch.Tensor, a: torch.Tensor, b: torch.Tens
                 workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
                 final_state: torch.Tensor | None = None):
     """The whole prefill (conv1d + SiLU over q | k | v, gates, chunked forward)
-    in three launches (gdn_prefill_conv, _prepare, _scan). x: bf16 [B, T, C] rows before the convolution, C = 2 Hk
+    in two launches (gdn_prefill_prepare, gdn_prefill_scan). x: bf16 [B, T, C] rows before the convolution, C = 2 Hk
     K + H V, channel dim contiguous; w: [C, 4]; a, b: bf16 [B, T, H] (the head
     dim contiguous, rows evenly strided). Returns (o [B, T, H, V],
     final_state [N, H, K, V] or None), equal bit for bit to prefill_chain."""
@@ -332,44 +329,23 @@ def gdn_prefill(x: torch.Tensor, w: torch.Tensor, a: torch.Tensor, b: torch.Tens
     return o, final_state
 
 
-def gdn_prefill_conv(x, w, workspace, *, Hk, K, H, V, bias=None, cu_seqlens=None):
-    """Phase 1 of gdn_prefill: the q and k channels of x convolved into `workspace`."""
-    B, T, n_seqs = _prefill_args(x, w, None, None, None, None, Hk, K, H, V, bias, cu_seqlens)
-    rc = _lib.gdn_prefill_conv(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
-                               _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
-                               _code(x.dtype), _dev(workspace, "workspace"),
-                               workspace.numel() * workspace.element_size(), _stream(x.device))
-    _check(rc, "gdn_prefill_conv")
-
-
-def gdn_prefill_prepare(a, b, A_log, dt_bias, workspace, *, Hk, K, H, V, cu_seqlens=None,
-                        scale=1.0, qk_l2norm=True):
-    """Phase 2 of gdn_prefill: gates and the per-chunk solve into `workspace`. a, b:
-    bf16 [B, T, H] (head dim contiguous, rows evenly strided)."""
-    if a.dim() != 3 or a.shape != b.shape or a.dtype != b.dtype or a.shape[2] != H:
-        raise ValueError("a and b must be [B, T, H] tensors of one dtype")
-    B, T = a.shape[:2]
-    for t_, n in ((a, "a"), (b, "b")):
-        if t_.stride(2) != 1 or (B > 1 and T > 0 and t_.stride(0) != T * t_.stride(1)):
-            raise ValueError(f"{n}: head dim contiguous, batch rows evenly strided")
-    for t_, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
-        if t_.dtype != torch.float32 or not t_.is_contiguous() or t_.numel() != H:
-            raise ValueError(f"{n} must be a contiguous fp32 [H] tensor")
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    rc = _lib.gdn_prefill_prepare(_dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
+def gdn_prefill_prepare(x, w, a, b, A_log, dt_bias, workspace, *, Hk, K, H, V, bias=None,
+                        cu_seqlens=None, scale=1.0, qk_l2norm=True):
+    """Phase 1 of gdn_prefill (q/k convolution, gates, per-chunk solve) into `workspace`."""
+    B, T, n_seqs = _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens)
+    rc = _lib.gdn_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
+                                  _dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
                                   _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
                                   _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
-                                  float(scale), int(bool(qk_l2norm)), _code(a.dtype),
+                                  float(scale), int(bool(qk_l2norm)), _code(x.dtype),
                                   _dev(workspace, "workspace"),
-                                  workspace.numel() * workspace.element_size(), _stream(a.device))
+                                  workspace.numel() * workspace.element_size(), _stream(x.device))
     _check(rc, "gdn_prefill_prepare")
 
 
 def gdn_prefill_scan(x, w, workspace, *, Hk, K, H, V, bias=None, initial_state=None,
                      output_final_state=True, cu_seqlens=None, o=None, final_state=None):
-    """Phase 3 of gdn_prefill (value convolution and the state scan). Returns (o, final_state)."""
+    """Phase 2 of gdn_prefill (value convolution and the state scan). Returns (o, final_state)."""
     B, T, n_seqs = _prefill_args(x, w, None, None, None, None, Hk, K, H, V, bias, cu_seqlens)
     o, final_state = _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state,
                                       output_final_state, o, final_state)

@@ -102,8 +102,9 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t* __restri
 }
 
 struct ChunkLoc {
-    int tok0;   // first token row of the chunk
-    int L;      // valid rows (1..64)
+    int tok0;     // first token row of the chunk
+    int L;        // valid rows (1..64)
+    bool first;   // the chunk starts its sequence
 };
 
 // tile -> (sequence, chunk). Dense: tile = seq * nck + c. Packed: offsets
@@ -117,6 +118,7 @@ __device__ __forceinline__ bool locate_tile(int tile, const int32_t* __restrict_
         const int seq = tile / nck, c = tile - seq * nck;
         loc.tok0 = seq * T_len + c * kChunk;
         loc.L = min(kChunk, T_len - c * kChunk);
+        loc.first = c == 0;
         return true;
     }
     if (tile >= offsets[n_seqs]) return false;
@@ -127,6 +129,7 @@ __device__ __forceinline__ bool locate_tile(int tile, const int32_t* __restrict_
     }
     loc.tok0 = cu[lo] + (tile - offsets[lo]) * kChunk;
     loc.L = min(kChunk, cu[lo + 1] - loc.tok0);
+    loc.first = tile == offsets[lo];
     return true;
 }
 
@@ -176,6 +179,12 @@ __device__ __forceinline__ f32x4 mma16(const f32x4& x, const f32x4& y, f32x4 z) 
 }
 // This wave's LDS writes are complete (and the compiler keeps LDS accesses in
 // program order around it); the wave's later LDS reads see them.
+// 64 lanes x 16 bytes from rsrc + voffset (+ soffset) to LDS dst + 16 lane
+// (an inactive lane neither loads nor writes)
+__device__ __forceinline__ void dma16(rsrc_t r, unsigned char* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
@@ -221,33 +230,108 @@ __device__ __forceinline__ void subst_rows(const float (&arow)[16], float (&x)[1
     }
 }
 
-// Gate inputs of the whole-prefill form of chunk_prep: the gates are formed
-// here from a and b (the same formulas as the gate kernel) instead of being
-// read from g and beta.
-struct PrepGates {
+// Inputs of the whole-prefill forms of chunk_prep. GATES: the gates are
+// formed here from a and b (the same formulas as the gate kernel) instead of
+// being read from g and beta. CONV (with GATES): qp / kp point at the raw q /
+// k rows before the short convolution, which is applied here; the convolved
+// rows go to `qk` for the scan, one contiguous block per (chunk, key head),
+// so that every store covers whole cache lines.
+struct PrepFused {
     const bf16* a;        // [token][head], row strides as / bs
     const bf16* b;
     int64_t as, bs;
     const float* A_log;
     const float* dt_bias;
+    const bf16* wq;       // conv taps [channel][4] of q channel 0 of key head 0 (k: wk)
+    const bf16* wk;
+    const bf16* bq;       // conv bias of the same channels, or null
+    const bf16* bk;
+    unsigned char* qk;    // convolved rows out, in (chunk, key head) blocks:
+                          // [q, k][32-column slice][64 rows][64 bytes]
 };
 
+// Bytes of one block of convolved q (or k) rows: 64 rows x KD bf16.
+template <int KD>
+constexpr uint32_t qk_block_bytes() { return (uint32_t)kChunk * KD * 2; }
+
+// LDS staging of the CONV form: per 32-column slice of the raw rows (one
+// contraction block), the three rows before the chunk and then its 64 rows
+// (slot r + 3 for chunk row r), 64 bytes each, for k and for q, in two
+// buffers (the next slice lands while this one is used); the taps and biases
+// of the item's channels. It shares the wave's LDS with PrepLds, which is
+// first used after the last slice. The four 16-byte segments of slot s are
+// stored XOR-ed with (s / 4) % 4: 16 consecutive slots then cover every
+// (bank group, segment) pair once, so the 16 lanes of a read that take one
+// segment of 16 consecutive rows hit distinct banks.
+template <int KD>
+struct PrepStage {
+    static constexpr int kRowB = 64;                    // bytes of a row's 32-column slice
+    static constexpr int kSlice = (3 + kChunk) * kRowB;
+    unsigned char rows[2][2][kSlice];                   // [buffer][k, q]
+    unsigned char taps[2][KD * 4 * 2];                  // [k, q][channel][4 taps] bf16
+    unsigned char bias[2][KD * 2];                      // [k, q][channel] bf16
+};
+
+__device__ __forceinline__ int stage_seg(int slot, int seg) { return seg ^ ((slot >> 2) & 3); }
+
+template <int KD, bool CONV>
+constexpr size_t prep_lds_bytes() {
+    return CONV && sizeof(PrepStage<KD>) > sizeof(PrepLds) ? sizeof(PrepStage<KD>) : sizeof(PrepLds);
+}
+
+// Convolved rows of row tile i of one 32-column slice, from the staged rows
+// `sl` (row r of the chunk at slot r + 3): lane (c, g) forms row 16 i + c,
+// columns 8 g .. 8 g + 7 of the slice, with the slice's taps and biases at
+// `tp` and `bp` (8 columns per lane group); rows at or past L are zero.
+__device__ __forceinline__ bf16x8 conv_rows(const unsigned char* sl, const unsigned char* tp,
+                                            const unsigned char* bp, int i, int c, int g, int L)
+{
+    typedef PrepStage<128> PS;   // (the row layout does not depend on KD)
+    const int r = 16 * i + c;
+    auto row = [&](int s) {   // segment g of slot s
+        return __builtin_convertvector(
+            *reinterpret_cast<const bf16x8*>(sl + s * PS::kRowB + 16 * stage_seg(s, g)), f32x8);
+    };
+    const f32x8 x0 = row(r + 3);
+    const f32x8 x1 = row(r + 2);
+    const f32x8 x2 = row(r + 1);
+    const f32x8 x3 = row(r);
+    const f32x8 bf = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(bp + 16 * g), f32x8);
+    bf16x8 taps[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) taps[j] = *reinterpret_cast<const bf16x8*>(tp + 64 * g + 16 * j);
+    f32x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // taps of column e: flat entries 4 e .. 4 e + 3 of the 32
+        const float w0 = (float)taps[(4 * e + 0) / 8][(4 * e + 0) % 8];
+        const float w1 = (float)taps[(4 * e + 1) / 8][(4 * e + 1) % 8];
+        const float w2 = (float)taps[(4 * e + 2) / 8][(4 * e + 2) % 8];
+        const float w3 = (float)taps[(4 * e + 3) / 8][(4 * e + 3) % 8];
+        const float y = conv_silu(conv_taps4(w0, w1, w2, w3, bf[e], x3[e], x2[e], x1[e], x0[e]));
+        out[e] = r < L ? y : 0.f;
+    }
+    return __builtin_convertvector(out, bf16x8);
+}
+
 // Two waves per SIMD: registers sized for it.
-template <typename T, int KD, bool GATES>
+template <typename T, int KD, bool GATES, bool CONV>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void chunk_prep_kernel(
     const T* __restrict__ qp, const T* __restrict__ kp, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets, int n_seqs, int T_len,
     int H, int Hk, float scale, int l2norm, unsigned char* __restrict__ ws_rec, int n_items,
-    PrepGates gz)
+    PrepFused gz)
 {
-    static_assert(!GATES || sizeof(T) == 2, "the whole-prefill form runs on bf16 rows");
+    static_assert(!GATES || sizeof(T) == 2, "the whole-prefill forms run on bf16 rows");
+    static_assert(!CONV || GATES, "the convolving form also forms the gates");
     typedef Mma<T> MT;
     typedef typename MT::Frag Frag;
     typedef Rec<T> RC;
     constexpr int ES = (int)sizeof(T);
-    __shared__ __align__(16) PrepLds sm;
+    __shared__ __align__(16) unsigned char smem_raw[prep_lds_bytes<KD, CONV>()];
+    PrepLds& sm = *reinterpret_cast<PrepLds*>(smem_raw);
 
     // XCD-aware order: the key heads of one tile run on the same XCD (blockIdx
     // % 8) one after another, so the tile's gate rows are fetched into that
@@ -268,20 +352,32 @@ void chunk_prep_kernel(
     const int lr = min(lane, L - 1);
     const uint32_t row_bytes = (uint32_t)(qk_stride * ES);
 
-    // gate values of value head h (lane = row): given, or formed from a and b
-    auto gate_of = [&](int h, float& gv, float& bv) {
+    // gate values of value head h (lane = row): read (given, or a and b), then
+    // formed from a and b in the whole-prefill forms
+    auto gate_in = [&](int h, float& gv, float& bv) {
         const int64_t row = loc.tok0 + lr;
         if constexpr (GATES) {
-            gv = gate_g(to_f32(gz.a[row * gz.as + h]), gz.A_log[h], gz.dt_bias[h]);
-            bv = gate_beta(to_f32(gz.b[row * gz.bs + h]));
+            gv = to_f32(gz.a[row * gz.as + h]);
+            bv = to_f32(gz.b[row * gz.bs + h]);
         } else {
             gv = g[row * H + h];
             bv = beta[row * H + h];
         }
     };
-    // those of the first value head, requested before the rows
-    float gh, bh;
-    gate_of(hk * per, gh, bh);
+    auto gate_form = [&](int h, float& gv, float& bv) {
+        if constexpr (GATES) {
+            gv = gate_g(gv, gz.A_log[h], gz.dt_bias[h]);
+            bv = gate_beta(bv);
+        }
+    };
+    auto gate_of = [&](int h, float& gv, float& bv) {
+        gate_in(h, gv, bv);
+        gate_form(h, gv, bv);
+    };
+    // those of the first value head, requested before the rows (after the
+    // staging copies in the convolving form, formed once the rows are used)
+    float gh = 0.f, bh = 0.f;
+    if constexpr (!CONV) gate_of(hk * per, gh, bh);
 
     // ---- S = K K^T and Q K^T (lower tiles, R layout), diagonal tiles of Q Q^T
     const int64_t base = (int64_t)loc.tok0 * qk_stride + (int64_t)hk * KD;
@@ -293,14 +389,93 @@ void chunk_prep_kernel(
     for (int t = 0; t < kLowerTiles; ++t) { skk[t] = zero4(); sqk[t] = zero4(); }
 #pragma unroll
     for (int i = 0; i < 4; ++i) sqq[i] = zero4();
+    // CONV: staging of the raw rows (three before the chunk, none at a sequence
+    // start, where the taps read zero), taps, biases, and the convolved rows'
+    // destination
+    PrepStage<KD>* stg = reinterpret_cast<PrepStage<KD>*>(smem_raw);
+    rsrc_t rhk = rsk, rhq = rsq, rok = rsk, roq = rsk;
+    // lane l lands at position l % 4 of slot l / 4 (+ the piece's first slot),
+    // so it fetches the segment stored there
+    auto stage_slice = [&](int kb, int buf) {
+        const uint32_t col = (uint32_t)(64 * kb);
+        if (lane < 12) {
+            const int slot = lane >> 2;
+            const uint32_t off = (uint32_t)slot * row_bytes + col + 16 * stage_seg(slot, lane & 3);
+            dma16(rhk, stg->rows[buf][0], off, 0);
+            dma16(rhq, stg->rows[buf][1], off, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = 16 * p + (lane >> 2);
+            const uint32_t off = (uint32_t)r * row_bytes + col + 16 * stage_seg(r + 3, lane & 3);
+            dma16(rsk, stg->rows[buf][0] + 3 * PrepStage<KD>::kRowB + 1024 * p, off, 0);
+            dma16(rsq, stg->rows[buf][1] + 3 * PrepStage<KD>::kRowB + 1024 * p, off, 0);
+        }
+    };
+    constexpr int kSliceLoads = 2 + 2 * 4;   // copies per slice (k, q: halo + four pieces)
+    constexpr int kStores = 8;               // convolved-row stores per slice
+    if constexpr (CONV) {
+        const uint32_t hspan = loc.first ? 0u : 2 * row_bytes + KD * ES;
+        rhk = make_rsrc(kp + base - 3 * qk_stride, hspan);
+        rhq = make_rsrc(qp + base - 3 * qk_stride, hspan);
+        constexpr uint32_t tb = qk_block_bytes<KD>();
+        unsigned char* blk = gz.qk + ((int64_t)tile * Hk + hk) * 2 * tb;
+        roq = make_rsrc(blk, tb);
+        rok = make_rsrc(blk + tb, tb);
+        // taps and biases of the item's channels (no bias: zero-length, read as zero)
+        const int64_t ch = (int64_t)hk * KD;
+        constexpr int tl = KD * 8 / 16, bl = KD * 2 / 16;   // lanes of 16 bytes
+        if (lane < tl) {
+            dma16(make_rsrc(gz.wk + ch * 4, KD * 8), stg->taps[0], lane * 16, 0);
+            dma16(make_rsrc(gz.wq + ch * 4, KD * 8), stg->taps[1], lane * 16, 0);
+        }
+        if (lane < bl) {
+            dma16(make_rsrc(gz.bk ? gz.bk + ch : gz.wk, gz.bk ? KD * 2 : 0), stg->bias[0], lane * 16, 0);
+            dma16(make_rsrc(gz.bq ? gz.bq + ch : gz.wq, gz.bq ? KD * 2 : 0), stg->bias[1], lane * 16, 0);
+        }
+        stage_slice(0, 0);
+        stage_slice(1, 1);
+        gate_in(hk * per, gh, bh);
+    }
 #pragma unroll
     for (int kb = 0; kb < KD / 32; ++kb) {
         Frag kf[4], qf[4];
+        if constexpr (CONV) {
+            // slice kb has landed once only younger accesses are outstanding: at
+            // kb 0 slice 1's copies and the two gate-input loads, later the
+            // previous slice's stores (the counter retires in issue order)
+            static_assert(KD / 32 > 1, "two slices at least");
+            if (kb == 0) wait_vmcnt<kSliceLoads + 2>();
+            else wait_vmcnt<kStores>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (kb >= 1 && kb + 1 < KD / 32) {
+                stage_slice(kb + 1, (kb + 1) & 1);   // its buffer was read by slice kb - 1
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
+            const unsigned char* sk = stg->rows[kb & 1][0];
+            const unsigned char* sq = stg->rows[kb & 1][1];
+            const int cb = 32 * kb;   // first channel of the slice within the head
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t off = (uint32_t)(16 * i + c) * row_bytes + (32 * kb + 8 * gq) * ES;
-            kf[i] = RowFrag<T>::load(rsk, off);
-            qf[i] = RowFrag<T>::load(rsq, off);
+            for (int i = 0; i < 4; ++i) {
+                kf[i] = conv_rows(sk, stg->taps[0] + cb * 8, stg->bias[0] + cb * 2, i, c, gq, L);
+                qf[i] = conv_rows(sq, stg->taps[1] + cb * 8, stg->bias[1] + cb * 2, i, c, gq, L);
+            }
+            wave_lds_sync();   // this slice's rows are read: its buffer may be refilled
+            // (one store: 16 whole rows of the slice, 1 KiB contiguous; rows past
+            // the chunk are written as zero)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = (uint32_t)(kChunk * 64 * kb + 64 * (16 * i + c) + 16 * gq);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, kf[i]), rok, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, qf[i]), roq, off, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = (uint32_t)(16 * i + c) * row_bytes + (32 * kb + 8 * gq) * ES;
+                kf[i] = RowFrag<T>::load(rsk, off);
+                qf[i] = RowFrag<T>::load(rsq, off);
+            }
         }
         // C(K_j X_i^T) = R(X_i K_j^T): tile (i, j) of S with the K rows first
 #pragma unroll
@@ -313,6 +488,7 @@ void chunk_prep_kernel(
             sqq[i] = MT::mma(qf[i], qf[i], sqq[i]);
         }
     }
+    if constexpr (CONV) gate_form(hk * per, gh, bh);
     // row norms from the diagonals: element c & 3 of the lanes with g == c / 4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -495,10 +671,6 @@ __device__ __forceinline__ typename Mma<T>::Frag state_frag(const f32x4& t0, con
     return Mma<T>::acc_frag(lo, hi);
 }
 
-// 64 lanes x 16 bytes from rsrc + voffset (+ soffset) to LDS dst + 16 lane
-__device__ __forceinline__ void dma16(rsrc_t r, unsigned char* dst, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
-}
 
 // LDS staging of one chunk for the scan: raw K and Q tiles, the chunk's record
 // and each wave's 64 x 16 slab of values, all written by direct-to-LDS loads
@@ -588,6 +760,10 @@ struct ScanArgs {
     // columns (from the head's first column) and its record; bytes per row
     uint64_t k0, q0, v0, r0;
     uint32_t qk_row, v_row;
+    // blocked K / Q (whole-prefill form): bytes of one chunk's block (0: rows
+    // of qk_row bytes instead) and from one chunk's blocks to the next's
+    uint32_t qk_blk;
+    uint64_t kq_step;
 };
 
 // Prefetch of later chunks into L2: the waves of a unit (nwu of them) split the
@@ -605,7 +781,8 @@ template <typename T, int KD, int NW>
 struct PrefetchPlan {
     uint64_t base[kPrefetchSlots];     // chunk-0 address of the slot's tensor block
     uint64_t step[kPrefetchSlots];     // bytes from one chunk to the next
-    uint32_t row[kPrefetchSlots];      // bytes per row (0: the record; ~0u: unused slot)
+    uint32_t row[kPrefetchSlots];      // bytes per row (0: one contiguous block; ~0u: unused slot)
+    uint32_t blk[kPrefetchSlots];      // bytes of a contiguous block
     uint32_t off[kPrefetchSlots];      // this lane's byte offset in the chunk's block
     __device__ __forceinline__ void init(const ScanArgs<T, KD, NW>& a, int wu, int nwu) {
         constexpr int ES = (int)sizeof(T);
@@ -622,14 +799,17 @@ struct PrefetchPlan {
             const int t = j < kq_spr ? 0 : j < 2 * kq_spr ? 1 : j < 2 * kq_spr + v_spr ? 2
                         : j < 2 * kq_spr + v_spr + rec_slots ? 3 : 4;
             const int sub = j - (t == 0 ? 0 : t == 1 ? kq_spr : t == 2 ? 2 * kq_spr : 2 * kq_spr + v_spr);
+            // (a chunk's blocked K or Q is as many sectors as its rows)
+            const bool kq_blk = t <= 1 && a.qk_blk != 0;
             base[i] = t == 0 ? a.k0 : t == 1 ? a.q0 : t == 2 ? a.v0 : a.r0;
-            step[i] = t <= 1 ? (uint64_t)kChunk * a.qk_row : t == 2 ? (uint64_t)kChunk * a.v_row
-                                                                   : (uint64_t)a.H * Rec<T>::bytes;
-            row[i] = t <= 1 ? a.qk_row : t == 2 ? a.v_row : t == 3 ? 0u : ~0u;
+            step[i] = t <= 1 ? (kq_blk ? a.kq_step : (uint64_t)kChunk * a.qk_row)
+                             : t == 2 ? (uint64_t)kChunk * a.v_row : (uint64_t)a.H * Rec<T>::bytes;
+            row[i] = kq_blk ? 0u : t <= 1 ? a.qk_row : t == 2 ? a.v_row : t == 3 ? 0u : ~0u;
+            blk[i] = kq_blk ? a.qk_blk : (uint32_t)Rec<T>::bytes;
             const int sct = sub * kWave + a.lane;
             const int sh = t == 2 ? v_sh : kq_sh;
-            off[i] = t >= 3 ? (uint32_t)sct * kPfSector
-                            : (uint32_t)(sct >> sh) * row[i] + (uint32_t)(sct & ((1 << sh) - 1)) * kPfSector;
+            off[i] = t >= 3 || kq_blk ? (uint32_t)sct * kPfSector
+                                      : (uint32_t)(sct >> sh) * row[i] + (uint32_t)(sct & ((1 << sh) - 1)) * kPfSector;
         }
     }
 };
@@ -648,11 +828,12 @@ __device__ __forceinline__ ChunkSpan chunk_span(int c, const ScanArgs<T, KD, NW>
     const int cc = valid ? c : 0;
     const int L = valid ? min(kChunk, a.tok_end - (a.tok_begin + c * kChunk)) : 0;
     ChunkSpan r;
-    r.k = a.k0 + (uint64_t)cc * (kChunk * a.qk_row);
-    r.q = a.q0 + (uint64_t)cc * (kChunk * a.qk_row);
+    const uint64_t kq_step = a.qk_blk ? a.kq_step : (uint64_t)kChunk * a.qk_row;
+    r.k = a.k0 + (uint64_t)cc * kq_step;
+    r.q = a.q0 + (uint64_t)cc * kq_step;
     r.v = a.v0 + (uint64_t)cc * (kChunk * a.v_row) + vcol * ES;
     r.r = a.r0 + (uint64_t)cc * (uint32_t)(a.H * Rec<T>::bytes);
-    r.kq_bytes = (uint32_t)L * a.qk_row;
+    r.kq_bytes = a.qk_blk ? (valid ? a.qk_blk : 0u) : (uint32_t)L * a.qk_row;
     r.v_bytes = (uint32_t)L * a.v_row;
     r.r_bytes = valid ? (uint32_t)Rec<T>::bytes : 0u;
     return r;
@@ -699,7 +880,7 @@ struct Stager {
 #pragma unroll
         for (int i = 0; i < kPrefetchSlots; ++i) {
             const uint32_t rb = plan.row[i];
-            const uint32_t bytes = !pvalid || rb == ~0u ? 0u : rb == 0u ? (uint32_t)Rec<T>::bytes : pL * rb;
+            const uint32_t bytes = !pvalid || rb == ~0u ? 0u : rb == 0u ? plan.blk[i] : pL * rb;
             pf[i] = make_rsrc((const void*)(plan.base[i] + (uint64_t)pc * plan.step[i]), bytes);
         }
     }
@@ -1150,6 +1331,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
     a.q0 = (uint64_t)(qp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
     a.v0 = (uint64_t)(vp + (int64_t)a.tok_begin * v_stride + h * V);
     a.r0 = (uint64_t)(ws_rec + ((int64_t)a.tile0 * H + h) * Rec<T>::bytes);
+    a.qk_blk = 0;
+    a.kq_step = 0;
 
     // ---- per-lane constants ----
     LN ln;
@@ -1573,10 +1756,21 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
     a.nchunks = nchunks;
     a.qk_row = (uint32_t)(qk_stride * ES);
     a.v_row = (uint32_t)(v_stride * ES);
-    a.k0 = (uint64_t)(kp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
-    a.q0 = (uint64_t)(qp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
     a.v0 = (uint64_t)(vp + (int64_t)a.tok_begin * v_stride + h * V);
     a.r0 = (uint64_t)(ws_rec + ((int64_t)a.tile0 * H + h) * Rec<T>::bytes);
+    if constexpr (CONV) {
+        // q and k in (chunk, key head) blocks from qp: [q, k][slice][row][64 B]
+        constexpr uint32_t tb = qk_block_bytes<KD>();
+        a.qk_blk = tb;
+        a.kq_step = (uint64_t)Hk * 2 * tb;
+        a.q0 = (uint64_t)qp + ((uint64_t)a.tile0 * Hk + a.hk) * 2 * tb;
+        a.k0 = a.q0 + tb;
+    } else {
+        a.k0 = (uint64_t)(kp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
+        a.q0 = (uint64_t)(qp + (int64_t)a.tok_begin * qk_stride + a.hk * KD);
+        a.qk_blk = 0;
+        a.kq_step = 0;
+    }
 
     // operand offsets (chain and output waves)
     LN ln;
@@ -1667,7 +1861,9 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
         for (int j = 0; j < TP; ++j) {
             const int row = j * SB::RPI + lane / SB::SPR;
             const int s = (lane % SB::SPR) ^ tile_mask<T, KD, NT>(row);
-            tsrc[j] = (uint32_t)(row * (int64_t)a.qk_row + s * 16);
+            // (blocked: segment s of a row is segment s % 4 of 32-column slice s / 4)
+            tsrc[j] = CONV ? (uint32_t)((s >> 2) * (kChunk * 64) + row * 64 + (s & 3) * 16)
+                           : (uint32_t)(row * (int64_t)a.qk_row + s * 16);
         }
         uint32_t vsrc[SB::v_pieces];
 #pragma unroll
@@ -1696,7 +1892,7 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int i = 0; i < kPrefetchSlots; ++i) {
                 const uint32_t rb = plan.row[i];
-                const uint32_t bytes = !pvalid || rb == ~0u ? 0u : rb == 0u ? (uint32_t)Rec<T>::bytes : pL * rb;
+                const uint32_t bytes = !pvalid || rb == ~0u ? 0u : rb == 0u ? plan.blk[i] : pL * rb;
                 const rsrc_t pr = make_rsrc((const void*)(plan.base[i] + (uint64_t)pc * plan.step[i]), bytes);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)scratch, 4, plan.off[i], 0, 0, 0);
             }
@@ -1813,11 +2009,11 @@ static inline ChunkWs carve(void* ws, int n_seqs) {
     return w;
 }
 
-template <typename T, int KD, bool GATES = false>
+template <typename T, int KD, bool GATES = false, bool CONV = false>
 static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, const float* g,
                                    const float* beta, const int32_t* cu, int n_seqs, int B,
                                    int T_len, int H, int Hk, float scale, int l2norm, void* ws,
-                                   hipStream_t stream, const PrepGates& gz = PrepGates{})
+                                   hipStream_t stream, const PrepFused& gz = PrepFused{})
 {
     const bool packed = cu != nullptr;
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
@@ -1832,7 +2028,7 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
         // a multiple of the 8 XCDs)
         const int64_t items = tiles * Hk;
         const int64_t blocks = (tiles + 7) / 8 * 8 * Hk;
-        auto kern = chunk_prep_kernel<T, KD, GATES>;
+        auto kern = chunk_prep_kernel<T, KD, GATES, CONV>;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWave), 0, stream,
                            (const T*)q, (const T*)k, qks, g, beta, cu, w.offsets, n_seqs, T_len, H,
                            Hk, scale, l2norm, w.rec, (int)items, gz);
@@ -1882,54 +2078,44 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, int64_t qks, const
                     : launch_prepare_t<float, 64>(q, k, qks, g, beta, cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
 }
 
-// Whole prefill in three launches (conv, prepare and scan phases): the short
-// convolution of the q and k channels (into the workspace, after the
-// records), chunk_prep forming the gates from a and b itself, then the
-// role-split scan convolving the value rows as it reads them. Equal, bit for bit, to conv1d + gate_prepare +
-// chunk_prepare + chunk_scan (role-split) on the same inputs; y's value part,
-// g and beta are never written.
-hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w, const void* bias,
-                         void* y, int64_t ysb, int64_t yst, const int32_t* cu, int n_seqs, int B,
-                         int T_len, int C, int silu, bool bf16_io, hipStream_t stream);
-
+// Whole prefill in two launches (prepare and scan phases): chunk_prep
+// convolving the raw q and k rows and forming the gates itself (the
+// convolved rows go to the workspace, after the records, for the scan), then
+// the role-split scan convolving the value rows as it reads them. Equal, bit
+// for bit, to conv1d + gate_prepare + chunk_prepare + chunk_scan (role-split)
+// on the same inputs; y, g and beta are never written.
 size_t prefill_workspace_bytes(int B, int T_len, int H, int Hk, int K, int n_seqs, bool packed) {
+    const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
     return align256(chunk_workspace_bytes(B, T_len, H, n_seqs, packed, true)) +
-           align256((size_t)B * T_len * 2 * Hk * K * sizeof(bf16));
+           (size_t)tiles * Hk * 2 * kChunk * K * sizeof(bf16);
 }
 
-// The q / k rows of the whole-prefill form: after the records in the workspace.
-static inline bf16* prefill_qk(void* ws, int B, int T_len, int H, int n_seqs) {
-    return (bf16*)((unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, n_seqs > 0, true)));
-}
-
-hipError_t launch_prefill_conv(const void* x, int64_t xs, const void* cw, const void* cb,
-                               const int32_t* cu, int n_seqs, int B, int T_len, int H, int Hk,
-                               int K, void* ws, hipStream_t stream)
-{
-    if (!cu) n_seqs = 0;
-    if (T_len == 0) return hipSuccess;
-    const int64_t qkc = (int64_t)Hk * K;             // channels of q (and of k)
-    return launch_conv1d(x, (int64_t)T_len * xs, xs, cw, cb, prefill_qk(ws, B, T_len, H, n_seqs),
-                         (int64_t)T_len * 2 * qkc, 2 * qkc, cu, n_seqs, B, T_len, (int)(2 * qkc), 1,
-                         true, stream);
+// The q / k blocks of the whole-prefill form: after the records in the workspace.
+static inline unsigned char* prefill_qk(void* ws, int B, int T_len, int H, int n_seqs) {
+    return (unsigned char*)ws + align256(chunk_workspace_bytes(B, T_len, H, n_seqs, n_seqs > 0, true));
 }
 
 template <int KD>
-static hipError_t launch_prefill_prepare_t(const bf16* a, int64_t as, const bf16* b, int64_t bs,
-                                           const float* A_log, const float* dt_bias,
-                                           const int32_t* cu, int n_seqs, int B, int T_len, int H,
-                                           int Hk, float scale, int l2norm, void* ws,
-                                           hipStream_t stream)
+static hipError_t launch_prefill_prepare_t(const bf16* x, int64_t xs, const bf16* cw,
+                                           const bf16* cb, const bf16* a, int64_t as,
+                                           const bf16* b, int64_t bs, const float* A_log,
+                                           const float* dt_bias, const int32_t* cu, int n_seqs,
+                                           int B, int T_len, int H, int Hk, float scale,
+                                           int l2norm, void* ws, hipStream_t stream)
 {
-    const int64_t qkc = (int64_t)Hk * KD;
-    const bf16* qk = prefill_qk(ws, B, T_len, H, n_seqs);
-    PrepGates gz;
+    const int64_t qkc = (int64_t)Hk * KD;             // channels of q (and of k)
+    PrepFused gz;
     gz.a = a; gz.as = as;
     gz.b = b; gz.bs = bs;
     gz.A_log = A_log;
     gz.dt_bias = dt_bias;
-    return launch_prepare_t<bf16, KD, true>(qk, qk + qkc, 2 * qkc, nullptr, nullptr, cu, n_seqs, B,
-                                            T_len, H, Hk, scale, l2norm, ws, stream, gz);
+    gz.wq = cw;
+    gz.wk = cw + qkc * 4;
+    gz.bq = cb;
+    gz.bk = cb ? cb + qkc : nullptr;
+    gz.qk = prefill_qk(ws, B, T_len, H, n_seqs);
+    return launch_prepare_t<bf16, KD, true, true>(x, x + qkc, xs, nullptr, nullptr, cu, n_seqs, B,
+                                                  T_len, H, Hk, scale, l2norm, ws, stream, gz);
 }
 
 template <int KD>
@@ -1939,7 +2125,7 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
                                         void* ws, hipStream_t stream)
 {
     const int64_t qkc = (int64_t)Hk * KD;
-    const bf16* qk = prefill_qk(ws, B, T_len, H, n_seqs);
+    const bf16* qk = (const bf16*)prefill_qk(ws, B, T_len, H, n_seqs);   // blocked q / k
     const int N = cu ? n_seqs : B;
     const ChunkWs w = carve(ws, n_seqs);
     const int slabs = V / 16;
@@ -1947,22 +2133,25 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
     const bf16* bv = cb ? cb + 2 * qkc : nullptr;
     // two column tiles per workgroup where that still gives a workgroup per CU
     if ((int64_t)N * H * (slabs / 2) >= 256)
-        return launch_scan_roles<KD, 2, true>(qk, qk + qkc, 2 * qkc, x + 2 * qkc, xs, S0, Sf, o, cu,
-                                              w.offsets, w.rec, T_len, H, Hk, V, N, stream, wv, bv);
-    return launch_scan_roles<KD, 1, true>(qk, qk + qkc, 2 * qkc, x + 2 * qkc, xs, S0, Sf, o, cu,
-                                          w.offsets, w.rec, T_len, H, Hk, V, N, stream, wv, bv);
+        return launch_scan_roles<KD, 2, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu, w.offsets,
+                                              w.rec, T_len, H, Hk, V, N, stream, wv, bv);
+    return launch_scan_roles<KD, 1, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu, w.offsets,
+                                          w.rec, T_len, H, Hk, V, N, stream, wv, bv);
 }
 
-hipError_t launch_prefill_prepare(const void* a, int64_t as, const void* b, int64_t bs,
+hipError_t launch_prefill_prepare(const void* x, int64_t xs, const void* cw, const void* cb,
+                                  const void* a, int64_t as, const void* b, int64_t bs,
                                   const float* A_log, const float* dt_bias, const int32_t* cu,
                                   int n_seqs, int B, int T_len, int H, int Hk, int K, float scale,
                                   int l2norm, void* ws, hipStream_t stream)
 {
     if (!cu) n_seqs = 0;
     if (K == 128)
-        return launch_prefill_prepare_t<128>((const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias,
+        return launch_prefill_prepare_t<128>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
+                                             (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias,
                                              cu, n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
-    return launch_prefill_prepare_t<64>((const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias, cu,
+    return launch_prefill_prepare_t<64>((const bf16*)x, xs, (const bf16*)cw, (const bf16*)cb,
+                                        (const bf16*)a, as, (const bf16*)b, bs, A_log, dt_bias, cu,
                                         n_seqs, B, T_len, H, Hk, scale, l2norm, ws, stream);
 }
 

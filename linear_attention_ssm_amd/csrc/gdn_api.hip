@@ -25,10 +25,8 @@ hipError_t launch_chunk_scan(const void* q, const void* k, int64_t qks, const vo
                              int B, int T_len, int H, int Hk, int K, int V, bool use_bf16,
                              const void* ws, hipStream_t stream);
 size_t prefill_workspace_bytes(int B, int T_len, int H, int Hk, int K, int n_seqs, bool packed);
-hipError_t launch_prefill_conv(const void* x, int64_t xs, const void* cw, const void* cb,
-                               const int32_t* cu, int n_seqs, int B, int T_len, int H, int Hk,
-                               int K, void* ws, hipStream_t stream);
-hipError_t launch_prefill_prepare(const void* a, int64_t as, const void* b, int64_t bs,
+hipError_t launch_prefill_prepare(const void* x, int64_t xs, const void* cw, const void* cb,
+                                  const void* a, int64_t as, const void* b, int64_t bs,
                                   const float* A_log, const float* dt_bias, const int32_t* cu,
                                   int n_seqs, int B, int T_len, int H, int Hk, int K, float scale,
                                   int l2norm, void* ws, hipStream_t stream);
@@ -224,7 +222,7 @@ size_t gdn_prefill_workspace_size(int B, int T, int H, int Hk, int K, int V, int
     return gdn::prefill_workspace_bytes(B, T, H, Hk, K, packed ? n_seqs : 0, packed);
 }
 
-// Checks shared by the whole-prefill entry points (the three phases and all
+// Checks shared by the whole-prefill entry points (the two phases and both
 // of them); need_x: x and conv_w are read, need_gates: a, b and the gate
 // parameters, need_out: o and the states.
 static int check_prefill(bool need_x, const void* x, int64_t x_stride_t, const void* conv_w,
@@ -266,32 +264,22 @@ static int check_prefill(bool need_x, const void* x, int64_t x_stride_t, const v
     return GDN_OK;
 }
 
-int gdn_prefill_conv(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
-                     const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K,
-                     int V, int dtype, void* workspace, size_t workspace_bytes, void* stream)
+int gdn_prefill_prepare(const void* x, int64_t x_stride_t, const void* conv_w,
+                        const void* conv_bias, const void* a, int64_t a_stride_row, const void* b,
+                        int64_t b_stride_row, const float* A_log, const float* dt_bias,
+                        const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk, int K,
+                        int V, float scale, int qk_l2norm, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream)
 {
-    const int st = check_prefill(true, x, x_stride_t, conv_w, conv_bias, false, nullptr, 0, nullptr,
-                                 0, nullptr, nullptr, false, nullptr, nullptr, nullptr, cu_seqlens,
-                                 n_seqs, B, T, H, Hk, K, V, 0, dtype, workspace, workspace_bytes);
-    if (st != GDN_OK) return st;
-    return status_from(gdn::launch_prefill_conv(x, x_stride_t, conv_w, conv_bias, cu_seqlens, n_seqs,
-                                                B, T, H, Hk, K, workspace, (hipStream_t)stream));
-}
-
-int gdn_prefill_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t b_stride_row,
-                        const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
-                        int n_seqs, int B, int T, int H, int Hk, int K, int V, float scale,
-                        int qk_l2norm, int dtype, void* workspace, size_t workspace_bytes,
-                        void* stream)
-{
-    const int st = check_prefill(false, nullptr, 0, nullptr, nullptr, true, a, a_stride_row, b,
+    const int st = check_prefill(true, x, x_stride_t, conv_w, conv_bias, true, a, a_stride_row, b,
                                  b_stride_row, A_log, dt_bias, false, nullptr, nullptr, nullptr,
                                  cu_seqlens, n_seqs, B, T, H, Hk, K, V, qk_l2norm, dtype, workspace,
                                  workspace_bytes);
     if (st != GDN_OK) return st;
-    return status_from(gdn::launch_prefill_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias,
-                                                   cu_seqlens, n_seqs, B, T, H, Hk, K, scale,
-                                                   qk_l2norm, workspace, (hipStream_t)stream));
+    return status_from(gdn::launch_prefill_prepare(x, x_stride_t, conv_w, conv_bias, a, a_stride_row,
+                                                   b, b_stride_row, A_log, dt_bias, cu_seqlens,
+                                                   n_seqs, B, T, H, Hk, K, scale, qk_l2norm,
+                                                   workspace, (hipStream_t)stream));
 }
 
 int gdn_prefill_scan(const void* x, int64_t x_stride_t, const void* conv_w, const void* conv_bias,
@@ -322,12 +310,10 @@ int gdn_prefill(const void* x, int64_t x_stride_t, const void* conv_w, const voi
                            workspace_bytes);
     if (st != GDN_OK) return st;
     if (T > 0 && (o == a || o == b)) return GDN_EINVAL;
-    hipError_t e = gdn::launch_prefill_conv(x, x_stride_t, conv_w, conv_bias, cu_seqlens, n_seqs, B,
-                                            T, H, Hk, K, workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return GDN_ELAUNCH;
-    e = gdn::launch_prefill_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias, cu_seqlens,
-                                    n_seqs, B, T, H, Hk, K, scale, qk_l2norm, workspace,
-                                    (hipStream_t)stream);
+    hipError_t e = gdn::launch_prefill_prepare(x, x_stride_t, conv_w, conv_bias, a, a_stride_row, b,
+                                               b_stride_row, A_log, dt_bias, cu_seqlens, n_seqs, B,
+                                               T, H, Hk, K, scale, qk_l2norm, workspace,
+                                               (hipStream_t)stream);
     if (e != hipSuccess) return GDN_ELAUNCH;
     return status_from(gdn::launch_prefill_scan(x, x_stride_t, conv_w, conv_bias, initial_state,
                                                 final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K,

@@ -55,8 +55,8 @@ def lib():
     L.gdn_prefill_workspace_size.restype = sz
     L.gdn_prefill.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32]
                               + [i32] * 6 + [f32, i32, i32, vp, sz, vp])
-    L.gdn_prefill_conv.argtypes = [vp, i64, vp, vp, vp, i32] + [i32] * 6 + [i32, vp, sz, vp]
-    L.gdn_prefill_prepare.argtypes = [vp, i64, vp, i64, vp, vp, vp, i32] + [i32] * 6 + [f32, i32, i32, vp, sz, vp]
+    L.gdn_prefill_prepare.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, i32] + [i32] * 6
+                                      + [f32, i32, i32, vp, sz, vp])
     L.gdn_prefill_scan.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6 + [i32, vp, sz, vp]
     return L
 
@@ -232,22 +232,20 @@ def test_prefill_validation(lib):
 
 def test_prefill_phase_validation(lib):
     need = lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
-    conv = lambda **kw: lib.gdn_prefill_conv(
-        kw.get("x", P), kw.get("xs", 6144), kw.get("w", P2), None, None, 0, 4, 4096, 16, 16,
-        kw.get("K", 128), 128, kw.get("dtype", BF16), kw.get("ws", WS), kw.get("wsb", need), None)
     prep = lambda **kw: lib.gdn_prefill_prepare(
-        kw.get("a", P3), kw.get("as_", 16), kw.get("b", P3 + 64), 16, kw.get("A_log", P4), P4 + 64,
-        None, 0, 4, 4096, 16, kw.get("Hk", 16), kw.get("K", 128), 128, 1.0, kw.get("l2", 1),
-        kw.get("dtype", BF16), kw.get("ws", WS), kw.get("wsb", need), None)
+        kw.get("x", P), kw.get("xs", 6144), kw.get("w", P2), None, kw.get("a", P3), kw.get("as_", 16),
+        kw.get("b", P3 + 64), 16, kw.get("A_log", P4), P4 + 64, None, 0, 4, 4096, 16, kw.get("Hk", 16),
+        kw.get("K", 128), 128, 1.0, kw.get("l2", 1), kw.get("dtype", BF16), kw.get("ws", WS),
+        kw.get("wsb", need), None)
     scan = lambda **kw: lib.gdn_prefill_scan(
         kw.get("x", P), kw.get("xs", 6144), kw.get("w", P2), None, None, kw.get("Sf", P5),
         kw.get("o", P6), None, 0, 4, 4096, 16, 16, 128, kw.get("V", 128), kw.get("dtype", BF16),
         kw.get("ws", WS), kw.get("wsb", need), None)
-    assert conv(x=None) == EINVAL and conv(w=None) == EINVAL and conv(xs=100) == EINVAL
-    assert conv(x=P + 2) == EUNSUP and conv(dtype=FP32) == EUNSUP and conv(wsb=need - 1) == EWS
+    assert prep(x=None) == EINVAL and prep(w=None) == EINVAL and prep(xs=100) == EINVAL
     assert prep(a=None) == EINVAL and prep(A_log=None) == EINVAL and prep(ws=None) == EINVAL
     assert prep(Hk=5) == EINVAL and prep(K=32) == EUNSUP and prep(dtype=FP32) == EUNSUP
-    assert prep(wsb=need - 1) == EWS and prep(as_=8) == EINVAL and prep(l2=2) == EINVAL
+    assert prep(x=P + 2) == EUNSUP and prep(wsb=need - 1) == EWS
+    assert prep(as_=8) == EINVAL and prep(l2=2) == EINVAL
     assert scan(o=None) == EINVAL and scan(o=P) == EINVAL and scan(Sf=P6) == EINVAL
     assert scan(V=96) == EUNSUP and scan(wsb=need - 1) == EWS and scan(w=None) == EINVAL
 

@@ -1,7 +1,8 @@
-"""gdn_prefill (HIP, three launches) against the four-step chain and the oracle.
+"""gdn_prefill (HIP, two launches) against the four-step chain and the oracle.
 
-gdn_prefill folds the gates and the value rows' short convolution into the
-chunked forward and convolves only the q and k channels on their own. Its contract is that it equals conv1d + SiLU -> gates -> chunk_fwd on
+gdn_prefill folds the short convolution and the gates into the chunked
+forward: the per-chunk solve convolves the q and k rows and forms the gates,
+the scan convolves the value rows. Its contract is that it equals conv1d + SiLU -> gates -> chunk_fwd on
 the same inputs bit for bit, so every case compares o and the final state
 with torch.equal against that chain (whose kernels have their own parity
 tests against the fp64 oracle); the small cases, which also carry a conv bias,
@@ -157,8 +158,8 @@ def test_prefill_phases_equal_whole(gpu):
     Hk, K, H, V = d["Hk"], d["K"], d["H"], d["V"]
     ws = torch.empty(gpu.gdn_prefill_workspace_size(1, d["T"], H, Hk, K, V, 0), dtype=torch.uint8,
                      device=DEV)
-    gpu.gdn_prefill_conv(t["x"], t["w"], ws, Hk=Hk, K=K, H=H, V=V)
-    gpu.gdn_prefill_prepare(t["a"], t["b"], t["A_log"], t["dt_bias"], ws, Hk=Hk, K=K, H=H, V=V)
+    gpu.gdn_prefill_prepare(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"], ws, Hk=Hk,
+                            K=K, H=H, V=V)
     o, sf = gpu.gdn_prefill_scan(t["x"], t["w"], ws, Hk=Hk, K=K, H=H, V=V, initial_state=S0)
     torch.cuda.synchronize()
     _equal((o, sf), _fused(gpu, d), "phases")
