@@ -289,27 +289,29 @@ __device__ __forceinline__ bf16x8 conv_rows(const unsigned char* sl, const unsig
     typedef PrepStage<128> PS;   // (the row layout does not depend on KD)
     const int r = 16 * i + c;
     auto row = [&](int s) {   // segment g of slot s
-        return __builtin_convertvector(
-            *reinterpret_cast<const bf16x8*>(sl + s * PS::kRowB + 16 * stage_seg(s, g)), f32x8);
+        return *reinterpret_cast<const u32x4*>(sl + s * PS::kRowB + 16 * stage_seg(s, g));
     };
-    const f32x8 x0 = row(r + 3);
-    const f32x8 x1 = row(r + 2);
-    const f32x8 x2 = row(r + 1);
-    const f32x8 x3 = row(r);
+    const u32x4 x0 = row(r + 3);   // rows r, r - 1, r - 2, r - 3: two columns to a word
+    const u32x4 x1 = row(r + 2);
+    const u32x4 x2 = row(r + 1);
+    const u32x4 x3 = row(r);
     const f32x8 bf = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(bp + 16 * g), f32x8);
-    bf16x8 taps[4];
+    uint32_t wp[16];   // column e: (w0, w1) in word 2 e, (w2, w3) in word 2 e + 1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) taps[j] = *reinterpret_cast<const bf16x8*>(tp + 64 * g + 16 * j);
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(tp + 64 * g + 16 * j);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) wp[4 * j + d] = u[d];
+    }
     f32x8 out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        // taps of column e: flat entries 4 e .. 4 e + 3 of the 32
-        const float w0 = (float)taps[(4 * e + 0) / 8][(4 * e + 0) % 8];
-        const float w1 = (float)taps[(4 * e + 1) / 8][(4 * e + 1) % 8];
-        const float w2 = (float)taps[(4 * e + 2) / 8][(4 * e + 2) % 8];
-        const float w3 = (float)taps[(4 * e + 3) / 8][(4 * e + 3) % 8];
-        const float y = conv_silu(conv_taps4(w0, w1, w2, w3, bf[e], x3[e], x2[e], x1[e], x0[e]));
-        out[e] = r < L ? y : 0.f;
+    for (int d = 0; d < 4; ++d) {
+        const float a0 = conv_taps4_bf16(wp[4 * d], wp[4 * d + 1], bf[2 * d],
+                                         pair_lo(x3[d], x2[d]), pair_lo(x1[d], x0[d]));
+        const float a1 = conv_taps4_bf16(wp[4 * d + 2], wp[4 * d + 3], bf[2 * d + 1],
+                                         pair_hi(x3[d], x2[d]), pair_hi(x1[d], x0[d]));
+        out[2 * d] = r < L ? conv_silu(a0) : 0.f;
+        out[2 * d + 1] = r < L ? conv_silu(a1) : 0.f;
     }
     return __builtin_convertvector(out, bf16x8);
 }
@@ -1487,7 +1489,8 @@ struct ChainOps {
 // the whole-prefill form, where the staged values are the raw rows before the
 // convolution.
 struct ColTaps {
-    float w0, w1, w2, w3, b;
+    uint32_t w01, w23;   // (w0, w1), (w2, w3) as bf16 pairs
+    float b;
 };
 
 template <int KD, int NT, bool CONV>
@@ -1517,14 +1520,17 @@ __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
             const unsigned char* pa = head ? (prev ? prev->v[t] + ln.vtr + 60 * SB::VRB : buf->v[t] + ln.vtr)
                                            : buf->v[t] + ln.vtr + (16 * i - 4) * SB::VRB;
             const s16x4 pr = lds_read_tr16(pa);
-            const f32x4 x = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
-            f32x4 p = __builtin_convertvector(__builtin_bit_cast(bf16x4, pr), f32x4);
-            if (head && !prev) p = zero4();
+            // rows in time order, two to a word: p = (p0, p1), (p2, p3); x = (x0, x1), (x2, x3)
+            const u32x2 x = __builtin_bit_cast(u32x2, raw);
+            u32x2 p = __builtin_bit_cast(u32x2, pr);
+            if (head && !prev) p = u32x2{0u, 0u};
+            const uint32_t p12 = pair_mid(p[0], p[1]), p3x0 = pair_mid(p[1], x[0]);
+            const uint32_t x12 = pair_mid(x[0], x[1]);
             f32x4 y;
-            y[0] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[1], p[2], p[3], x[0]));
-            y[1] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[2], p[3], x[0], x[1]));
-            y[2] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, p[3], x[0], x[1], x[2]));
-            y[3] = conv_silu(conv_taps4(cv.w0, cv.w1, cv.w2, cv.w3, cv.b, x[0], x[1], x[2], x[3]));
+            y[0] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p12, p3x0));
+            y[1] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p[1], x[0]));
+            y[2] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p3x0, x12));
+            y[3] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, x[0], x[1]));
             // the values the scan sees are the bf16 convolution outputs
             op.vv[i] = __builtin_convertvector(__builtin_convertvector(y, bf16x4), f32x4);
         } else {
@@ -1816,10 +1822,9 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
         ColTaps cv{};
         if constexpr (CONV) {
             const int64_t chn = (int64_t)h * V + vc;
-            cv.w0 = (float)wv[chn * 4 + 0];
-            cv.w1 = (float)wv[chn * 4 + 1];
-            cv.w2 = (float)wv[chn * 4 + 2];
-            cv.w3 = (float)wv[chn * 4 + 3];
+            const u32x2 tw = *reinterpret_cast<const u32x2*>(wv + chn * 4);
+            cv.w01 = tw[0];
+            cv.w23 = tw[1];
             cv.b = bv ? (float)bv[chn] : 0.f;
         }
         lds_barrier();

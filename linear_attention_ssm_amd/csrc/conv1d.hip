@@ -47,15 +47,24 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     const int c0 = cg * VN;
 
     // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e]; the group's VN x W taps
-    // are contiguous, read as W 16-byte vectors
+    // are contiguous, read as W 16-byte vectors (bf16: kept as they lie, two
+    // taps to a word: word 2 e holds (w0, w1) of channel e, word 2 e + 1 (w2, w3))
     float wt[kConvW][VN];
+    uint32_t wp[2 * VN];
 #pragma unroll
     for (int i = 0; i < kConvW; ++i) {
-        const typename V::ftype f = V::to_float(*reinterpret_cast<const typename V::type*>(w + (int64_t)c0 * kConvW + i * VN));
+        const typename V::type raw_w = *reinterpret_cast<const typename V::type*>(w + (int64_t)c0 * kConvW + i * VN);
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 u = __builtin_bit_cast(u32x4, raw_w);
 #pragma unroll
-        for (int u = 0; u < VN; ++u) {
-            const int flat = i * VN + u;            // = e * W + j
-            wt[flat % kConvW][flat / kConvW] = f[u];
+            for (int d = 0; d < 4; ++d) wp[4 * i + d] = u[d];
+        } else {
+            const typename V::ftype f = V::to_float(raw_w);
+#pragma unroll
+            for (int u = 0; u < VN; ++u) {
+                const int flat = i * VN + u;            // = e * W + j
+                wt[flat % kConvW][flat / kConvW] = f[u];
+            }
         }
     }
     float bs[VN];
@@ -90,41 +99,78 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
         if (t < 0 || t >= T_len) raw[i] = typename V::type{};
     }
 
-    float win[kConvW - 1][VN];   // x[t-3], x[t-2], x[t-1]
+    if constexpr (sizeof(T) == 2) {
+        // the window as raw words (two channels each): x[t-3], x[t-2], x[t-1]
+        u32x4 win[kConvW - 1];
 #pragma unroll
-    for (int i = 0; i < kConvW - 1; ++i) {
-        int t = t0 - (kConvW - 1) + i;
-        typename V::ftype f = V::to_float(raw[i]);
-        bool live = (t >= seq_start);
+        for (int i = 0; i < kConvW - 1; ++i) {
+            const int t = t0 - (kConvW - 1) + i;
+            win[i] = t >= seq_start ? __builtin_bit_cast(u32x4, raw[i]) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-        for (int e = 0; e < VN; ++e) win[i][e] = live ? f[e] : 0.f;
-    }
+        for (int i = 0; i < RUN; ++i) {
+            const int t = t0 + i;
+            if (t >= T_len) break;
+            if (cu && t >= seq_end) {
+                // crossed into a later sequence: its taps start from zero
+                while (t >= seq_end) { ++si; seq_start = cu[si]; seq_end = cu[si + 1]; }
+#pragma unroll
+                for (int a = 0; a < kConvW - 1; ++a)
+                    if (t - (kConvW - 1) + a < seq_start) win[a] = u32x4{0u, 0u, 0u, 0u};
+            }
+            const u32x4 xw = __builtin_bit_cast(u32x4, raw[kConvW - 1 + i]);
+            typename V::ftype out;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const float a0 = conv_taps4_bf16(wp[4 * d], wp[4 * d + 1], bs[2 * d],
+                                                 pair_lo(win[0][d], win[1][d]), pair_lo(win[2][d], xw[d]));
+                const float a1 = conv_taps4_bf16(wp[4 * d + 2], wp[4 * d + 3], bs[2 * d + 1],
+                                                 pair_hi(win[0][d], win[1][d]), pair_hi(win[2][d], xw[d]));
+                out[2 * d] = silu ? conv_silu(a0) : a0;
+                out[2 * d + 1] = silu ? conv_silu(a1) : a1;
+            }
+            win[0] = win[1];
+            win[1] = win[2];
+            win[2] = xw;
+            *reinterpret_cast<typename V::type*>(yb + (int64_t)t * yst) = V::from_float(out);
+        }
+    } else {
+        float win[kConvW - 1][VN];   // x[t-3], x[t-2], x[t-1]
+#pragma unroll
+        for (int i = 0; i < kConvW - 1; ++i) {
+            int t = t0 - (kConvW - 1) + i;
+            typename V::ftype f = V::to_float(raw[i]);
+            bool live = (t >= seq_start);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) win[i][e] = live ? f[e] : 0.f;
+        }
 
 #pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-        const int t = t0 + i;
-        if (t >= T_len) break;
-        if (cu && t >= seq_end) {
-            // crossed into a later sequence: its taps start from zero
-            while (t >= seq_end) { ++si; seq_start = cu[si]; seq_end = cu[si + 1]; }
+        for (int i = 0; i < RUN; ++i) {
+            const int t = t0 + i;
+            if (t >= T_len) break;
+            if (cu && t >= seq_end) {
+                // crossed into a later sequence: its taps start from zero
+                while (t >= seq_end) { ++si; seq_start = cu[si]; seq_end = cu[si + 1]; }
 #pragma unroll
-            for (int a = 0; a < kConvW - 1; ++a)
+                for (int a = 0; a < kConvW - 1; ++a)
 #pragma unroll
-                for (int e = 0; e < VN; ++e)
-                    win[a][e] = (t - (kConvW - 1) + a >= seq_start) ? win[a][e] : 0.f;
+                    for (int e = 0; e < VN; ++e)
+                        win[a][e] = (t - (kConvW - 1) + a >= seq_start) ? win[a][e] : 0.f;
+            }
+            typename V::ftype xf = V::to_float(raw[kConvW - 1 + i]);
+            typename V::ftype out;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                const float acc = conv_taps4(wt[0][e], wt[1][e], wt[2][e], wt[3][e], bs[e],
+                                             win[0][e], win[1][e], win[2][e], xf[e]);
+                out[e] = silu ? conv_silu(acc) : acc;
+                win[0][e] = win[1][e];
+                win[1][e] = win[2][e];
+                win[2][e] = xf[e];
+            }
+            *reinterpret_cast<typename V::type*>(yb + (int64_t)t * yst) = V::from_float(out);
         }
-        typename V::ftype xf = V::to_float(raw[kConvW - 1 + i]);
-        typename V::ftype out;
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-            const float acc = conv_taps4(wt[0][e], wt[1][e], wt[2][e], wt[3][e], bs[e],
-                                         win[0][e], win[1][e], win[2][e], xf[e]);
-            out[e] = silu ? conv_silu(acc) : acc;
-            win[0][e] = win[1][e];
-            win[1][e] = win[2][e];
-            win[2][e] = xf[e];
-        }
-        *reinterpret_cast<typename V::type*>(yb + (int64_t)t * yst) = V::from_float(out);
     }
 }
 

@@ -185,6 +185,34 @@ __device__ __forceinline__ float conv_taps4(float w0, float w1, float w2, float 
 }
 __device__ __forceinline__ float conv_silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
+// bf16 inputs and taps: the four products summed onto the bias as two
+// two-term dot products (v_dot2_f32_bf16; a product of two bf16 values is
+// exact in fp32). x01 packs (x[t-3], x[t-2]) and x23 (x[t-1], x[t]) as bf16
+// pairs (low half first); w01 and w23 pack (w0, w1) and (w2, w3), which is how
+// a channel's four taps lie in memory. Every bf16 kernel that applies the
+// convolution uses this, so they agree bit for bit.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float conv_taps4_bf16(uint32_t w01, uint32_t w23, float bias,
+                                                 uint32_t x01, uint32_t x23) {
+    const float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x01),
+                                                      __builtin_bit_cast(bf16x2, w01), bias, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x23),
+                                           __builtin_bit_cast(bf16x2, w23), acc, false);
+}
+// (lo, hi) bf16 pair from the low (pair_lo) or high (pair_hi) halves of two
+// words, each holding two channels: the same channel at two times
+__device__ __forceinline__ uint32_t pair_lo(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+// (lo's high half, hi's low half): the pair straddling two words of a
+// sequence of bf16 values packed in time order
+__device__ __forceinline__ uint32_t pair_mid(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, 0x05040302u);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Index of the packed sequence containing token t: the largest i with

@@ -112,39 +112,61 @@ __global__ __launch_bounds__(kGdpThreads) void conv1d_update_kernel(
     }
     V* st = reinterpret_cast<V*>(state + (int64_t)s * (W - 1) * C + c0);
     const int64_t srow = C / VN;    // 16-byte vectors per state row
-    const typename VV::ftype xf = VV::to_float(*reinterpret_cast<const V*>(x + (int64_t)r * xs + c0));
-    typename VV::ftype win[W - 1];
+    const V xr = *reinterpret_cast<const V*>(x + (int64_t)r * xs + c0);
     V raw[W - 1];
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) {
-        raw[j] = st[j * srow];
-        win[j] = VV::to_float(raw[j]);
-    }
-    // taps: wt[j][e] multiplies x[t - (W-1) + j][c0 + e] (as in the prefill kernel)
-    float wt[W][VN];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-        const typename VV::ftype f = VV::to_float(*reinterpret_cast<const V*>(w + (int64_t)c0 * W + i * VN));
-#pragma unroll
-        for (int u = 0; u < VN; ++u) {
-            const int flat = i * VN + u;
-            wt[flat % W][flat / W] = f[u];
-        }
-    }
+    for (int j = 0; j < W - 1; ++j) raw[j] = st[j * srow];
     typename VV::ftype bs{};
     if (bias) bs = VV::to_float(*reinterpret_cast<const V*>(bias + c0));
     typename VV::ftype out;
+    // the same arithmetic as the prefill kernel: taps wt[j][e] multiply
+    // x[t - (W-1) + j][c0 + e] (bf16: as they lie, two to a word)
+    if constexpr (sizeof(T) == 2) {
+        uint32_t wp[2 * VN];
 #pragma unroll
-    for (int e = 0; e < VN; ++e) {
-        const float acc = conv_taps4(wt[0][e], wt[1][e], wt[2][e], wt[3][e], bias ? bs[e] : 0.f,
-                                     win[0][e], win[1][e], win[2][e], xf[e]);
-        out[e] = silu ? conv_silu(acc) : acc;
+        for (int i = 0; i < W; ++i) {
+            const u32x4 u = __builtin_bit_cast(u32x4, *reinterpret_cast<const V*>(w + (int64_t)c0 * W + i * VN));
+#pragma unroll
+            for (int d = 0; d < 4; ++d) wp[4 * i + d] = u[d];
+        }
+        const u32x4 w0 = __builtin_bit_cast(u32x4, raw[0]), w1 = __builtin_bit_cast(u32x4, raw[1]);
+        const u32x4 w2 = __builtin_bit_cast(u32x4, raw[2]), xw = __builtin_bit_cast(u32x4, xr);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float a0 = conv_taps4_bf16(wp[4 * d], wp[4 * d + 1], bias ? bs[2 * d] : 0.f,
+                                             pair_lo(w0[d], w1[d]), pair_lo(w2[d], xw[d]));
+            const float a1 = conv_taps4_bf16(wp[4 * d + 2], wp[4 * d + 3], bias ? bs[2 * d + 1] : 0.f,
+                                             pair_hi(w0[d], w1[d]), pair_hi(w2[d], xw[d]));
+            out[2 * d] = silu ? conv_silu(a0) : a0;
+            out[2 * d + 1] = silu ? conv_silu(a1) : a1;
+        }
+    } else {
+        const typename VV::ftype xf = VV::to_float(xr);
+        typename VV::ftype win[W - 1];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) win[j] = VV::to_float(raw[j]);
+        float wt[W][VN];
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            const typename VV::ftype f = VV::to_float(*reinterpret_cast<const V*>(w + (int64_t)c0 * W + i * VN));
+#pragma unroll
+            for (int u = 0; u < VN; ++u) {
+                const int flat = i * VN + u;
+                wt[flat % W][flat / W] = f[u];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+            const float acc = conv_taps4(wt[0][e], wt[1][e], wt[2][e], wt[3][e], bias ? bs[e] : 0.f,
+                                         win[0][e], win[1][e], win[2][e], xf[e]);
+            out[e] = silu ? conv_silu(acc) : acc;
+        }
     }
     *yr = VV::from_float(out);
     // the window moves one token on
     st[0] = raw[1];
     st[srow] = raw[2];
-    st[2 * srow] = *reinterpret_cast<const V*>(x + (int64_t)r * xs + c0);
+    st[2 * srow] = xr;
 }
 
 // One block per (token row, copy m) of a prefill: output row p = row * M + m.
