@@ -251,13 +251,16 @@ def test_prefill_phase_validation(lib):
 
 
 def test_prefill_workspace_size(lib):
-    # the chunked forward's workspace, then the convolved q and k rows (bf16)
+    # the chunked forward's workspace, then per (chunk, key head) a block of the
+    # convolved q and k rows: 2 x 64 rows x K bf16
     chunk = lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
-    qk = 4 * 4096 * 2 * 16 * 128 * 2
-    assert lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16) == chunk + qk
+    blocks = 4 * 64 * 16 * (2 * 64 * 128 * 2)
+    assert lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16) == chunk + blocks
+    # packed: the same upper bound on the chunk count as the records
     packed_chunk = lib.gdn_chunk_fwd_workspace_size(1, 1000, 4, 2, 64, 64, 10, BF16)
     packed = lib.gdn_prefill_workspace_size(1, 1000, 4, 2, 64, 64, 10, BF16)
-    assert packed == (packed_chunk + 255) // 256 * 256 + (1000 * 2 * 2 * 64 * 2 + 255) // 256 * 256
+    tiles_ub = (1000 + 63 * 10) // 64
+    assert packed == (packed_chunk + 255) // 256 * 256 + tiles_ub * 2 * (2 * 64 * 64 * 2)
     assert lib.gdn_prefill_workspace_size(4, 4096, 16, 16, 128, 128, 0, FP32) == 0
     assert lib.gdn_prefill_workspace_size(0, 10, 4, 4, 64, 64, 0, BF16) == 0
 
