@@ -8,8 +8,10 @@ run as the library's whole-prefill entry in its two phases: the per-chunk
 solve (convolving the q and k rows and forming the gates itself) and the scan
 (convolving the value rows as it reads them). Inputs are resident in HBM
 before timing starts. `value` is tokens/s of the whole step (16,384 tokens
-per step). With --chain the same computation is also timed as the four
-per-step calls (conv1d, gates, chunk_prepare, chunk_scan). The one-token Gated
+per step). The same computation is also timed as the four per-step calls
+(conv1d, gates, chunk_prepare, chunk_scan; `chain`), whose chunk_prepare +
+chunk_scan is the chunked forward on resident q, k, v, g, beta
+(`chain.chunk_fwd`: tokens/s and fractions of the MFMA and HBM peaks). The one-token Gated
 DeltaProduct decode (n=256 requests, M=2, H=32, G=16, P=N=128, 1000 steps,
 fp32 state updated in place) and the steps around it are reported beside it.
 
@@ -20,7 +22,7 @@ time per step; `traffic` comes from committed rocprofv3 counter summaries
 (profiles/traffic.json) and is null when absent or when the kernel's source
 has changed since they were taken.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--chain]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-chain]
 """
 from __future__ import annotations
 
@@ -59,8 +61,8 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration runs)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
-    p.add_argument("--chain", action="store_true",
-                   help="also time the four-call chain (conv1d, gates, chunk_prepare, chunk_scan)")
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the four-call chain (conv1d, gates, chunk_prepare, chunk_scan)")
     p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
                    help="turn a rocprofv3 --stats kernel_stats.csv into a profiles/ summary")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -578,7 +580,7 @@ def main():
                                "achieved_GBs": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9,
                                "hbm_frac": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9 / HBM_PEAK_GBS}
                           for op in op_ms}
-    if args.chain and args.only != "decode":
+    if not args.no_chain and args.only != "decode":
         out["chain"] = run_chain(args, gdn, wl, torch, dev, stream)
         ch = out["chain"]["ops_us"]
         out["chain"]["chunk_fwd"] = chunk_fwd_report(acc, tokens, (ch["chunk_prepare"] + ch["chunk_scan"]) / 1e3)
