@@ -56,6 +56,34 @@ typedef enum gdn_dtype {
 const char* gdn_status_string(int status);
 
 /* ------------------------------------------------------------------------
+ * gdn_tune_set / gdn_tune_get -- launch-configuration knobs, for the offline
+ * sweep that stands in for the pages' autotuning ([ZZ] item 1: the conv's
+ * block sizes and grouping are autotuned; item 4: one configuration serves
+ * every shape). A knob changes only how the work is scheduled, never the
+ * arithmetic: every setting gives the same results, bit for bit. 0 =
+ * automatic (the default). The knobs are process-wide host state read when
+ * an entry point launches; set them between calls, from one thread.
+ *   GDN_TUNE_SCAN_TILES    column tiles of 16 value columns per workgroup of
+ *                          the state scan (gdn_chunk_fwd, gdn_chunk_scan,
+ *                          gdn_prefill, gdn_prefill_scan): 1 or 2 for bf16, 1
+ *                          or 4 for fp32; a value that does not fit the
+ *                          call's dtype or V means automatic.
+ *   GDN_TUNE_CONV_RUN      tokens per thread of gdn_conv1d_causal: 8, 16 or
+ *                          32.
+ *   GDN_TUNE_CONV_THREADS  threads per workgroup of gdn_conv1d_causal: 64,
+ *                          128 or 256.
+ * gdn_tune_set returns GDN_EINVAL for an unknown knob or value (nothing
+ * changes); gdn_tune_get returns the knob's value, or -1 for an unknown knob.
+ * ---------------------------------------------------------------------- */
+enum {
+    GDN_TUNE_SCAN_TILES = 0,
+    GDN_TUNE_CONV_RUN = 1,
+    GDN_TUNE_CONV_THREADS = 2
+};
+int gdn_tune_set(int knob, int value);
+int gdn_tune_get(int knob);
+
+/* ------------------------------------------------------------------------
  * gdn_conv1d_causal -- [ZZ] item 1 "Causal Conv1d".
  * Depthwise causal convolution of width W (only W == 4 is implemented; the
  * width is fixed at compile time so the tap loop unrolls), each channel with

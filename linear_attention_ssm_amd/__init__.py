@@ -21,6 +21,8 @@ __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
     "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
+    "gdn_tune_set", "gdn_tune_get", "GDN_TUNE_SCAN_TILES", "GDN_TUNE_CONV_RUN",
+    "GDN_TUNE_CONV_THREADS",
     "gdn_recurrent_decode", "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
     "gdp_prefill", "prefill_chain", "split_qkv",
 ]
@@ -51,6 +53,10 @@ _lib.gdn_chunk_fwd_workspace_size.restype = _sz
 _lib.gdn_chunk_fwd.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
                                + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_chunk_fwd.restype = _i32
+_lib.gdn_tune_set.argtypes = [_i32, _i32]
+_lib.gdn_tune_set.restype = _i32
+_lib.gdn_tune_get.argtypes = [_i32]
+_lib.gdn_tune_get.restype = _i32
 _lib.gdn_prefill_workspace_size.argtypes = [_i32] * 8
 _lib.gdn_prefill_workspace_size.restype = _sz
 _lib.gdn_prefill.argtypes = ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
@@ -243,6 +249,22 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                             _stream(q.device))
     _check(rc, "gdn_chunk_fwd")
     return o, final_state
+
+
+# launch-configuration knobs (C constants of the same names)
+GDN_TUNE_SCAN_TILES, GDN_TUNE_CONV_RUN, GDN_TUNE_CONV_THREADS = 0, 1, 2
+
+
+def gdn_tune_set(knob: int, value: int) -> None:
+    """Set a launch-configuration knob (0 = automatic); results do not change."""
+    _check(_lib.gdn_tune_set(int(knob), int(value)), "gdn_tune_set")
+
+
+def gdn_tune_get(knob: int) -> int:
+    v = int(_lib.gdn_tune_get(int(knob)))
+    if v < 0:
+        raise ValueError(f"unknown knob {knob}")
+    return v
 
 
 def gdn_prefill_workspace_size(B: int, T: int, H: int, Hk: int, K: int, V: int,

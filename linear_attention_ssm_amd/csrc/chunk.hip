@@ -2043,6 +2043,21 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
     return hipSuccess;
 }
 
+// Column tiles (of 16 value columns) per scan workgroup. bf16 (role-split
+// kernel): two where that still gives a workgroup per CU, else one; fp32: four
+// (shared staging) when there is parallelism to spare, else one (a 2-tile
+// instance does not get through the gfx950 backend). The tuning knob
+// overrides the choice with any value valid for the dtype.
+static inline int scan_tiles(int64_t units, int slabs, bool bf16_ops) {
+    const int k = tune_knob[kTuneScanTiles];
+    if (bf16_ops) {
+        if (k == 1 || k == 2) return k;
+        return units * (slabs / 2) >= 256 ? 2 : 1;
+    }
+    if (k == 1 || (k == 4 && slabs % 4 == 0)) return k;
+    return units * (slabs / 4) >= 512 && slabs % 4 == 0 ? 4 : 1;
+}
+
 template <typename T, int KD>
 static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const void* v,
                                 int64_t vs, const float* S0, float* Sf, void* o, const int32_t* cu,
@@ -2053,18 +2068,15 @@ static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const
     const ChunkWs w = carve(const_cast<void*>(ws), n_seqs);
     const int units = N * H;
     const int slabs = V / 16;
+    const int tiles = scan_tiles(units, slabs, sizeof(T) == 2);
     if constexpr (sizeof(T) == 2) {
-        // bf16 operands: the split-role step, two column tiles per workgroup
-        // where that still gives a workgroup per CU (the same choice as the
-        // whole-prefill entry, so the two agree bit for bit)
-        if ((int64_t)units * (slabs / 2) >= 256)
+        // bf16 operands: the split-role step
+        if (tiles == 2)
             return launch_scan_roles<KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
         return launch_scan_roles<KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
     } else {
-        // fp32 operands (the small parity workloads): four column tiles per
-        // workgroup (shared staging) when there is parallelism to spare, else
-        // one (the 2-wave instance does not get through the gfx950 backend)
-        if (units * (slabs / 4) >= 512 && slabs % 4 == 0)
+        // fp32 operands (the small parity workloads)
+        if (tiles == 4)
             return launch_scan<T, KD, 4>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
         return launch_scan<T, KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
     }
@@ -2136,8 +2148,7 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
     const int slabs = V / 16;
     const bf16* wv = cw + 2 * qkc * 4;
     const bf16* bv = cb ? cb + 2 * qkc : nullptr;
-    // two column tiles per workgroup where that still gives a workgroup per CU
-    if ((int64_t)N * H * (slabs / 2) >= 256)
+    if (scan_tiles((int64_t)N * H, slabs, true) == 2)
         return launch_scan_roles<KD, 2, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu, w.offsets,
                                               w.rec, T_len, H, Hk, V, N, stream, wv, bv);
     return launch_scan_roles<KD, 1, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu, w.offsets,

@@ -14,16 +14,18 @@
 // so every access is a fully coalesced 1 KiB segment. Taps before the start
 // of a token's sequence read zero; with packed sequences the run tracks the
 // next boundary and clears its window there.
+#include <climits>
+
 #include "gdn_common.hpp"
 
 namespace gdn {
 
 constexpr int kConvW = 4;
-constexpr int kConvRun = 16;       // tokens per thread
-constexpr int kConvThreads = 256;
+constexpr int kConvRun = 16;       // tokens per thread (default)
+constexpr int kConvThreads = 256;  // threads per workgroup (default)
 
-template <typename T, int RUN>
-__global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
+template <typename T, int RUN, int NTH>
+__global__ __launch_bounds__(NTH) void conv1d_causal_kernel(
     const T* __restrict__ x, int64_t xsb, int64_t xst,
     const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, int64_t ysb, int64_t yst,
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     const int j = blockIdx.x >> 3;
     const int cgb = j / per_xcd;
     const int run = (blockIdx.x & 7) * per_xcd + (j - cgb * per_xcd);
-    const int cg = cgb * kConvThreads + threadIdx.x;
+    const int cg = cgb * NTH + threadIdx.x;
     if (cg >= ncg || run >= runs_total) return;
     const int b = run / runs_per_row;
     const int t0 = (run % runs_per_row) * RUN;
@@ -174,22 +176,54 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_causal_kernel(
     }
 }
 
+template <typename T, int RUN, int NTH>
+static hipError_t launch_conv1d_cfg(const void* x, int64_t xsb, int64_t xst, const void* w,
+                                    const void* bias, void* y, int64_t ysb, int64_t yst,
+                                    const int32_t* cu, int n_seqs, int B, int T_len, int C,
+                                    int silu, hipStream_t stream)
+{
+    const int ncg = C / V16<T>::n;
+    const int runs = (T_len + RUN - 1) / RUN;
+    const int total = runs * B;
+    const int pad = (total + 7) / 8 * 8;
+    const int cgb = (ncg + NTH - 1) / NTH;
+    hipLaunchKernelGGL((conv1d_causal_kernel<T, RUN, NTH>), dim3((unsigned)(pad * cgb)), dim3(NTH),
+                       0, stream, (const T*)x, xsb, xst, (const T*)w, (const T*)bias, (T*)y, ysb,
+                       yst, cu, n_seqs, T_len, C, runs, total, pad, silu);
+    return hipGetLastError();
+}
+
+template <typename T, int RUN>
+static hipError_t launch_conv1d_run(int nth, const void* x, int64_t xsb, int64_t xst,
+                                    const void* w, const void* bias, void* y, int64_t ysb,
+                                    int64_t yst, const int32_t* cu, int n_seqs, int B, int T_len,
+                                    int C, int silu, hipStream_t stream)
+{
+    if (nth == 64)
+        return launch_conv1d_cfg<T, RUN, 64>(x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
+    if (nth == 128)
+        return launch_conv1d_cfg<T, RUN, 128>(x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
+    return launch_conv1d_cfg<T, RUN, 256>(x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
+}
+
 template <typename T>
 hipError_t launch_conv1d_t(const void* x, int64_t xsb, int64_t xst, const void* w,
                            const void* bias, void* y, int64_t ysb, int64_t yst,
                            const int32_t* cu, int n_seqs, int B, int T_len, int C, int silu,
                            hipStream_t stream)
 {
-    const int ncg = C / V16<T>::n;
-    const int runs = (T_len + kConvRun - 1) / kConvRun;
-    const int total = runs * B;
-    const int pad = (total + 7) / 8 * 8;
-    const int cgb = (ncg + kConvThreads - 1) / kConvThreads;
-    hipLaunchKernelGGL((conv1d_causal_kernel<T, kConvRun>), dim3((unsigned)(pad * cgb)),
-                       dim3(kConvThreads), 0, stream, (const T*)x, xsb, xst, (const T*)w,
-                       (const T*)bias, (T*)y, ysb, yst, cu, n_seqs, T_len, C, runs, total, pad,
-                       silu);
-    return hipGetLastError();
+    // the tuned configuration, unless its grid would not fit (the default's is
+    // checked by the entry point)
+    int run = tune_knob[kTuneConvRun] ? tune_knob[kTuneConvRun] : kConvRun;
+    int nth = tune_knob[kTuneConvThreads] ? tune_knob[kTuneConvThreads] : kConvThreads;
+    const int64_t grid = ((int64_t)(T_len + run - 1) / run * B + 7) / 8 * 8 *
+                         ((C / V16<T>::n + nth - 1) / nth);
+    if (grid > INT_MAX) { run = kConvRun; nth = kConvThreads; }
+    if (run == 8)
+        return launch_conv1d_run<T, 8>(nth, x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
+    if (run == 32)
+        return launch_conv1d_run<T, 32>(nth, x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
+    return launch_conv1d_run<T, 16>(nth, x, xsb, xst, w, bias, y, ysb, yst, cu, n_seqs, B, T_len, C, silu, stream);
 }
 
 hipError_t launch_conv1d(const void* x, int64_t xsb, int64_t xst, const void* w,

@@ -52,6 +52,10 @@ hipError_t launch_gdp_prefill_prepare(const void* x, int64_t xs, const void* ba,
                                       int P, int N, bool bf16_io, hipStream_t stream);
 }  // namespace gdn
 
+namespace gdn {
+int tune_knob[kTuneKnobs] = {0, 0, 0};
+}  // namespace gdn
+
 namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -120,6 +124,31 @@ int gdn_gate_prepare(const void* a, int64_t a_stride_row, const void* b, int64_t
     return status_from(gdn::launch_gate_prepare(a, a_stride_row, b, b_stride_row, A_log, dt_bias,
                                                 g, beta, R, H, in_dtype == GDN_BF16,
                                                 (hipStream_t)stream));
+}
+
+int gdn_tune_set(int knob, int value)
+{
+    switch (knob) {
+    case GDN_TUNE_SCAN_TILES:
+        if (value != 0 && value != 1 && value != 2 && value != 4) return GDN_EINVAL;
+        break;
+    case GDN_TUNE_CONV_RUN:
+        if (value != 0 && value != 8 && value != 16 && value != 32) return GDN_EINVAL;
+        break;
+    case GDN_TUNE_CONV_THREADS:
+        if (value != 0 && value != 64 && value != 128 && value != 256) return GDN_EINVAL;
+        break;
+    default:
+        return GDN_EINVAL;
+    }
+    gdn::tune_knob[knob] = value;
+    return GDN_OK;
+}
+
+int gdn_tune_get(int knob)
+{
+    if (knob < 0 || knob >= gdn::kTuneKnobs) return -1;
+    return gdn::tune_knob[knob];
 }
 
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int Hk, int K, int V, int n_seqs, int dtype)

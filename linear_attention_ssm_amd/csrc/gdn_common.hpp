@@ -262,4 +262,10 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Launch-configuration knobs (gdn_tune_set): 0 = automatic. They change how
+// work is scheduled, never the arithmetic, so every setting gives the same
+// bits. Read by the launchers on the host.
+enum TuneKnob { kTuneScanTiles = 0, kTuneConvRun = 1, kTuneConvThreads = 2, kTuneKnobs = 3 };
+extern int tune_knob[kTuneKnobs];
+
 }  // namespace gdn

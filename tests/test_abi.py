@@ -51,6 +51,8 @@ def lib():
     L.gdn_conv1d_update.argtypes = [vp, i64, vp, vp, vp, vp, vp, i64] + [i32] * 6 + [vp]
     L.gdn_gdp_prefill_prepare.argtypes = ([vp, i64, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
                                           + [i32] * 8 + [vp])
+    L.gdn_tune_set.argtypes = [i32, i32]
+    L.gdn_tune_get.argtypes = [i32]
     L.gdn_prefill_workspace_size.argtypes = [i32] * 8
     L.gdn_prefill_workspace_size.restype = sz
     L.gdn_prefill.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32]
@@ -248,6 +250,23 @@ def test_prefill_phase_validation(lib):
     assert prep(as_=8) == EINVAL and prep(l2=2) == EINVAL
     assert scan(o=None) == EINVAL and scan(o=P) == EINVAL and scan(Sf=P6) == EINVAL
     assert scan(V=96) == EUNSUP and scan(wsb=need - 1) == EWS and scan(w=None) == EINVAL
+
+
+def test_tune_knobs(lib):
+    SCAN, RUN, THREADS = 0, 1, 2
+    try:
+        for knob, good, bad in ((SCAN, (1, 2, 4, 0), (3, -1, 8)), (RUN, (8, 16, 32, 0), (4, 64)),
+                                (THREADS, (64, 128, 256, 0), (32, 512))):
+            for v in good:
+                assert lib.gdn_tune_set(knob, v) == OK and lib.gdn_tune_get(knob) == v
+            lib.gdn_tune_set(knob, good[0])
+            for v in bad:   # rejected values change nothing
+                assert lib.gdn_tune_set(knob, v) == EINVAL and lib.gdn_tune_get(knob) == good[0]
+        assert lib.gdn_tune_set(3, 0) == EINVAL and lib.gdn_tune_get(3) == -1
+        assert lib.gdn_tune_get(-1) == -1
+    finally:
+        for knob in (SCAN, RUN, THREADS):
+            lib.gdn_tune_set(knob, 0)
 
 
 def test_prefill_workspace_size(lib):
