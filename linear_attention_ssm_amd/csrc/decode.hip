@@ -38,11 +38,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
     static_assert(RPT * RG == NK && CG * RG == kDecodeThreads, "tile shape");
 
     __shared__ float kv[kDecodeMaxM][NK];
-    __shared__ float qv[NK];
+    __shared__ float qv[kDecodeThreads > NK ? kDecodeThreads : NK];   // (staged past NK, unread)
     __shared__ float vv[kDecodeMaxM][PV];
     __shared__ __align__(16) float red[2][RG][PV];
-    __shared__ float beta_s[kDecodeMaxM];
-    __shared__ float alpha_s;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -55,24 +53,39 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
     const int64_t k_base = (int64_t)M * H * PV;
     const int64_t q_base = k_base + (int64_t)M * G * NK;
 
-    // --- split: this head's value slices, its group's keys and query
-    for (int e = tid; e < M * PV; e += kDecodeThreads) {
-        int m = e / PV, p = e - m * PV;
-        vv[m][p] = to_f32(xr[((int64_t)m * H + h) * PV + p]);
+    // --- the token's inputs, all requested at once (one memory round trip):
+    // this head's value slices, its group's keys and query, b per copy and a
+    constexpr int VPT = (kDecodeMaxM * PV + kDecodeThreads - 1) / kDecodeThreads;
+    constexpr int KPT = (kDecodeMaxM * NK + kDecodeThreads - 1) / kDecodeThreads;
+    constexpr int QPT = (NK + kDecodeThreads - 1) / kDecodeThreads;
+    // (unpredicated loads of clamped indices, masked when staged: a predicated
+    // load would get a wait of its own)
+    T vin[VPT], kin[KPT], qin[QPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int e0 = tid + i * kDecodeThreads, e = e0 < M * PV ? e0 : 0;
+        const int m = e / PV, p = e - m * PV;
+        vin[i] = xr[((int64_t)m * H + h) * PV + p];
     }
-    for (int e = tid; e < M * NK; e += kDecodeThreads) {
-        int m = e / NK, i = e - m * NK;
-        kv[m][i] = to_f32(xr[k_base + ((int64_t)m * G + grp) * NK + i]);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int e0 = tid + i * kDecodeThreads, e = e0 < M * NK ? e0 : 0;
+        const int m = e / NK, c = e - m * NK;
+        kin[i] = xr[k_base + ((int64_t)m * G + grp) * NK + c];
     }
-    for (int i = tid; i < NK; i += kDecodeThreads) qv[i] = to_f32(xr[q_base + (int64_t)grp * NK + i]);
-    // --- gates: beta per copy, the decay on copy 0 only
-    if (tid < M) beta_s[tid] = gate_beta(to_f32(br[(int64_t)tid * H + h]));
-    if (tid == kWave) {
-        float a = to_f32(br[(int64_t)M * H + h]);
-        alpha_s = expf(gate_g(a, A_log[h], dt_bias[h]));
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int c0 = tid + i * kDecodeThreads, c = c0 < NK ? c0 : 0;
+        qin[i] = xr[q_base + (int64_t)grp * NK + c];
     }
+    // gate inputs, read by every thread (uniform addresses: one request each)
+    T bin[kDecodeMaxM];
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m) bin[m] = br[(int64_t)(m < M ? m : 0) * H + h];
+    const T ain = br[(int64_t)M * H + h];
 
-    // --- issue the state loads early: they are the bulk of the traffic
+    // --- then the state: the bulk of the traffic, in flight while the inputs
+    // are staged and normalised
     const int cg = tid % CG;
     const int rg = tid / CG;
     float* st = state + ((int64_t)r * H + h) * NK * PV;
@@ -80,6 +93,23 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
         S[j] = *reinterpret_cast<const f32x4*>(st + (int64_t)(rg + RG * j) * PV + 4 * cg);
+
+    // (staged unconditionally: slots of copies >= M and query slots >= NK take
+    // stand-in values nothing reads, and no load waits behind a branch)
+    static_assert(VPT * kDecodeThreads <= kDecodeMaxM * PV && KPT * kDecodeThreads <= kDecodeMaxM * NK,
+                  "staging stays inside the arrays");
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) (&vv[0][0])[tid + i * kDecodeThreads] = to_f32(vin[i]);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) (&kv[0][0])[tid + i * kDecodeThreads] = to_f32(kin[i]);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) qv[tid + i * kDecodeThreads] = to_f32(qin[i]);
+    // --- gates: beta per copy, the decay on copy 0 only (formed in every
+    // thread's registers)
+    float beta_r[kDecodeMaxM];
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m) beta_r[m] = gate_beta(to_f32(bin[m]));
+    const float alpha = expf(gate_g(to_f32(ain), A_log[h], dt_bias[h]));
     __syncthreads();
 
     // --- L2 normalisation of k_0..k_{M-1} and q, one wave per vector
@@ -95,12 +125,13 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
         __syncthreads();
     }
 
-    const float alpha = alpha_s;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) S[j] *= alpha;
 
     // --- M sub-steps: u = beta (v - h^T k); h += k u^T
-    for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m) {
+        if (m >= M) break;
         f32x4 part = zero4();
 #pragma unroll
         for (int j = 0; j < RPT; ++j) part += S[j] * kv[m][rg + RG * j];
@@ -110,7 +141,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gdp_decode_kernel(
 #pragma unroll
         for (int a = 0; a < RG; ++a) hk += *reinterpret_cast<const f32x4*>(&red[m & 1][a][4 * cg]);
         const f32x4 vm = *reinterpret_cast<const f32x4*>(&vv[m][4 * cg]);
-        const f32x4 u = beta_s[m] * (vm - hk);
+        const f32x4 u = beta_r[m] * (vm - hk);
 #pragma unroll
         for (int j = 0; j < RPT; ++j) S[j] += kv[m][rg + RG * j] * u;
     }
