@@ -107,7 +107,9 @@ def prefill_accounting(B, T, H, Hk, K, V):
         # the whole chunked forward, single-pass: q, k, v, g, beta in; o, final state out;
         # flops per token and head 6 d^2 + 5 C d + 2/3 C^2 (triangular count)
         "chunk_fwd": {"bytes": qk + v + gb + o + state,
-                      "flops": tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3)},
+                      "flops": tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3),
+                      # dense count: the intra-chunk products as full C x C blocks
+                      "flops_dense": tok * H * (6 * d * d + 10 * Cc * d + (2 * Cc * Cc) / 3)},
     }
 
 
@@ -117,6 +119,7 @@ def chunk_fwd_report(acc, tokens, ms):
     s = ms / 1e3
     return {"tokens_per_s": tokens / s, "us": s * 1e6,
             "mfma_frac": acc["chunk_fwd"]["flops"] / s / (BF16_PEAK_TFLOPS * 1e12),
+            "mfma_frac_dense": acc["chunk_fwd"]["flops_dense"] / s / (BF16_PEAK_TFLOPS * 1e12),
             "hbm_frac": acc["chunk_fwd"]["bytes"] / s / (HBM_PEAK_GBS * 1e9),
             "algorithmic_flops": acc["chunk_fwd"]["flops"],
             "algorithmic_bytes": acc["chunk_fwd"]["bytes"]}
@@ -192,6 +195,47 @@ def _timed_steps(args, torch, stream, step, n_ev):
     return evs, (time.perf_counter() - t0) * 1e3 / args.steps
 
 
+class Flush:
+    """Writes a 512 MB scratch buffer: evicts the 256 MB Infinity Cache (and the
+    L2s) between timed iterations, outside the timed region."""
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xff)
+
+
+def iter_stats(fn, torch, stream, iters, flush=None):
+    """Median, p10 and p90 (us) of `iters` single calls timed with HIP events on
+    `stream`, each preceded (outside its events) by `flush` when given."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+    def pct(q):
+        return us[min(len(us) - 1, int(round(q * (len(us) - 1))))]
+    return {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9), "iters": iters}
+
+
+def copy_peak(torch, dev, stream):
+    """GB/s of a plain 1 GiB device-to-device copy (read + write bytes)."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = iter_stats(lambda: dst.copy_(src), torch, stream, 5)
+    return 2 * (1 << 30) / (st["median_us"] / 1e6) / 1e9
+
+
 def run_prefill(args, gdn, wl, torch, dev, stream):
     """The whole prefill through its three phase entry points (each one kernel),
     with events between them."""
@@ -220,7 +264,11 @@ def run_prefill(args, gdn, wl, torch, dev, stream):
     evs, step_ms = _timed_steps(args, torch, stream, step, 3)
     op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
              for j, op in enumerate(ops)}
-    return w, op_ms, step_ms
+    # per-iteration statistics: back to back, and with the caches flushed
+    # between iterations (outside the timed region)
+    stats = {"back_to_back": iter_stats(step, torch, stream, args.steps),
+             "flushed": iter_stats(step, torch, stream, args.steps, Flush(torch, dev))}
+    return w, op_ms, step_ms, stats
 
 
 def run_chain(args, gdn, wl, torch, dev, stream):
@@ -261,7 +309,16 @@ def run_chain(args, gdn, wl, torch, dev, stream):
     op_us = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps * 1e3
              for j, op in enumerate(ops)}
     tokens = w.B * w.T
-    return {"us": step_ms * 1e3, "tokens_per_s": tokens / (step_ms / 1e3), "ops_us": op_us}
+
+    # the chunked forward alone on the resident q, k, v, g, beta (the
+    # headline metric's unit): per-iteration statistics, flushed and not
+    def chunk():
+        gdn.gdn_chunk_prepare(q, k, g, beta, ws)
+        gdn.gdn_chunk_scan(q, k, v, o, ws, final_state=fs)
+    chunk_stats = {"back_to_back": iter_stats(chunk, torch, stream, args.steps),
+                   "flushed": iter_stats(chunk, torch, stream, args.steps, Flush(torch, dev))}
+    return {"us": step_ms * 1e3, "tokens_per_s": tokens / (step_ms / 1e3), "ops_us": op_us,
+            "chunk_fwd_iters": chunk_stats}
 
 
 def run_decode(args, gdn, wl, torch, dev, stream):
@@ -555,7 +612,7 @@ def main():
                       "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"}}
 
     if args.only != "decode":
-        w, op_ms, step_ms = run_prefill(args, gdn, wl, torch, dev, stream)
+        w, op_ms, step_ms, step_stats = run_prefill(args, gdn, wl, torch, dev, stream)
         acc = prefill_accounting(w.B, w.T, w.H, w.Hk, w.K, w.V)
         tokens = w.B * w.T
         out["value"] = tokens / (step_ms / 1e3)
@@ -572,7 +629,8 @@ def main():
             out["roofline"]["mfma_frac"] = acc[dom]["flops"] / sec / (BF16_PEAK_TFLOPS * 1e12)
         step_s = step_ms / 1e3
         out["step"] = {"algorithmic_bytes": acc["prefill"]["bytes"],
-                       "hbm_frac": acc["prefill"]["bytes"] / step_s / (HBM_PEAK_GBS * 1e9)}
+                       "hbm_frac": acc["prefill"]["bytes"] / step_s / (HBM_PEAK_GBS * 1e9),
+                       "iters": step_stats}
         # the chunked forward: the prepare and scan phases (which here also form
         # the gates and convolve the value rows)
         out["chunk_fwd"] = chunk_fwd_report(acc, tokens, op_ms["prefill_prepare"] + op_ms["prefill_scan"])
@@ -584,9 +642,23 @@ def main():
         out["chain"] = run_chain(args, gdn, wl, torch, dev, stream)
         ch = out["chain"]["ops_us"]
         out["chain"]["chunk_fwd"] = chunk_fwd_report(acc, tokens, (ch["chunk_prepare"] + ch["chunk_scan"]) / 1e3)
+        for kind, st in out["chain"].pop("chunk_fwd_iters").items():
+            out["chain"]["chunk_fwd"][kind] = dict(
+                st, tokens_per_s_median=tokens / (st["median_us"] / 1e6),
+                mfma_frac_median=acc["chunk_fwd"]["flops"] / (st["median_us"] / 1e6) / (BF16_PEAK_TFLOPS * 1e12))
     if args.only != "prefill" and not args.no_decode:
         out["decode"] = run_decode(args, gdn, wl, torch, dev, stream)
         out["gdp_steps"] = run_gdp_steps(gdn, wl, torch, dev, stream)
+    # the copy-kernel peak, the practical HBM ceiling the fractions are also read
+    # against (read + write bytes of a plain device copy)
+    cp = copy_peak(torch, dev, stream)
+    out["copy_peak_GBs"] = cp
+    for kk in out.get("kernels", {}).values():
+        kk["copy_frac"] = kk["achieved_GBs"] / cp
+    if "roofline" in out:
+        out["roofline"]["copy_frac"] = out["roofline"]["achieved"] / cp
+    if "decode" in out:
+        out["decode"]["roofline"]["copy_frac"] = out["decode"]["roofline"]["achieved"] / cp
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
