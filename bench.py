@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (made with "
                         "--copy-probe) into profiles/traffic.json")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
+                   help="write the MFMA-busy summary of a --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                        "SQ_INSTS_MFMA GRBM_GUI_ACTIVE run")
     p.add_argument("--command", default="", help="the command that produced the CSVs")
     return p.parse_args()
 
@@ -579,8 +582,44 @@ def summarize_traffic(fetch_csv, write_csv, command):
     return res
 
 
+def summarize_mfma(csv_path, out_md, command, cus=256, simds=4, xcds=8):
+    """Per kernel and bench part: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
+    (active cycles x CUs x SIMDs), the active cycles being GRBM_GUI_ACTIVE per
+    XCD (the counter is summed over the XCDs); and MFMA instructions per launch."""
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = (phase(r), r["Kernel_Name"])
+    groups = collections.OrderedDict()
+    for d in sorted(per):
+        groups.setdefault(names[d], []).append(per[d])
+    lines = ["# MFMA busy (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             f"busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs x {simds} SIMDs),",
+             "averaged over the launches of each kernel in each part of the bench.", "",
+             "| part | kernel | launches | MFMA busy | MFMA instructions / launch |",
+             "|---|---|---|---|---|"]
+    for (ph, name), cs in groups.items():
+        act = sum(c.get("GRBM_GUI_ACTIVE", 0) for c in cs) / xcds
+        busy = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for c in cs)
+        insts = sum(c.get("SQ_INSTS_MFMA", 0) for c in cs) / len(cs)
+        if insts == 0:
+            continue
+        frac = busy / (act * cus * simds) if act else 0.0
+        lines.append(f"| {ph} | `{_kernel_stem(name)}` | {len(cs)} | {frac:.3f} | {insts:.4g} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma[0], args.summarize_mfma[1], args.command)
+        return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command)
         return
