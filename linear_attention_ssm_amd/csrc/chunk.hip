@@ -439,6 +439,22 @@ void chunk_prep_kernel(
         stage_slice(1, 1);
         gate_in(hk * per, gh, bh);
     }
+    // bf16 rows read from q and k: every fragment of the item is requested
+    // before the first product, so the loads overlap one another instead of
+    // waiting slice by slice (fp32 rows would not fit in registers)
+    constexpr bool kAhead = !CONV && sizeof(T) == 2;
+    Frag kall[kAhead ? KD / 32 : 1][4], qall[kAhead ? KD / 32 : 1][4];
+    if constexpr (kAhead) {
+#pragma unroll
+        for (int kb = 0; kb < KD / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = (uint32_t)(16 * i + c) * row_bytes + (32 * kb + 8 * gq) * ES;
+                kall[kb][i] = RowFrag<T>::load(rsk, off);
+                qall[kb][i] = RowFrag<T>::load(rsq, off);
+            }
+        __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the products
+    }
 #pragma unroll
     for (int kb = 0; kb < KD / 32; ++kb) {
         Frag kf[4], qf[4];
@@ -470,6 +486,12 @@ void chunk_prep_kernel(
                 const uint32_t off = (uint32_t)(kChunk * 64 * kb + 64 * (16 * i + c) + 16 * gq);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, kf[i]), rok, off, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, qf[i]), roq, off, 0, 0);
+            }
+        } else if constexpr (kAhead) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kf[i] = kall[kb][i];
+                qf[i] = qall[kb][i];
             }
         } else {
 #pragma unroll
