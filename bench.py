@@ -628,8 +628,8 @@ def main():
                                            args.command), indent=1))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; runs on several GPUs "
-                                   "are not part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the kernels are "
+                                   "single-GPU and no multi-GPU path exists", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
