@@ -52,7 +52,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # (the GPU needs some tens of milliseconds of work to reach its sustained
+    # clock: 10 warm-up steps time 10% slow, 200 (about 35 ms) do not)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
@@ -184,18 +186,25 @@ def cpu_baseline(w, batch):
 
 
 def _timed_steps(args, torch, stream, step, n_ev):
-    """W untimed steps, then K timed ones with n_ev events each; returns the
-    events and the wall time per step (ms)."""
+    """W untimed steps, then K timed steps with nothing else on the stream (the
+    wall time per step, ms, between two synchronisations), then K more with
+    n_ev HIP events each on `stream`, bracketing each kernel (its duration).
+    The two passes are separate because an event recorded between two
+    kernels leaves a gap of several microseconds between them."""
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    return evs, (time.perf_counter() - t0) * 1e3 / args.steps
+    return evs, step_ms
 
 
 class Flush:

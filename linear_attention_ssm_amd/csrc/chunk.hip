@@ -1475,7 +1475,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // ------------------------------------------------------------ chunk_scan, role-split waves (bf16)
 //
 // One workgroup per (sequence, value head, 16 NT value columns) with NT + 2
-// waves, one per SIMD:
+// waves, one per SIMD (NT + 3 in the whole-prefill form, see below):
 //   chain t owns the fp32 state of column tile t (16 columns) and runs the
 //           dependent part of a chunk: X = K h, U = T (V - a o X), h' =
 //           gamma_L h + K^T (c o U);
@@ -1493,6 +1493,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // wave through LDS. A chain wave reads a chunk's operands one step ahead,
 // right after the mid-step barrier by which the copy wave has seen it land;
 // the output wave reads its own at the start of the step.
+// In the whole-prefill form the values are staged raw and a conv wave
+// convolves each chunk's value slabs in place during the step before the
+// chains read them, half before and half after the mid-step barrier (with one
+// column tile it has a SIMD of its own; with two it shares the copy wave's).
+// Measured on MI355X: with one tile (the GQA workload) this is 9% faster than
+// convolving in the chain waves; with two, the same within noise.
 template <int KD, int NT>
 struct RoleHand {
     bf16x8 h[KD / 32][NT][kWave];   // h of the step's chunk: B operand per contraction block and tile
@@ -1507,21 +1513,31 @@ struct ChainOps {
     f32x4 fa[4], fc[4];         // row factors a and c
     float gL;                   // gamma_L
 };
-// Short-convolution taps (w0..w3, bias) of a chain lane's value column, for
-// the whole-prefill form, where the staged values are the raw rows before the
+// Short-convolution taps (w0..w3, bias) of one value column, for the
+// whole-prefill form, where the values are staged as raw rows before the
 // convolution.
 struct ColTaps {
     uint32_t w01, w23;   // (w0, w1), (w2, w3) as bf16 pairs
     float b;
 };
 
+// Whole-prefill form: the conv wave rewrites a chunk's staged value slab of
+// tile t in place, from raw rows (row r at byte 32 r) to the convolved values
+// in the chain wave's operand order: row tile i of chain lane l is 4 bf16 at
+// byte 8 (64 i + l), i.e. where raw rows 16 i .. 16 i + 15 were.
+__device__ __forceinline__ const unsigned char* conv_slot(const unsigned char* slab, int i, int lane) {
+    return slab + (i * kWave + lane) * 8;
+}
+__device__ __forceinline__ unsigned char* conv_slot(unsigned char* slab, int i, int lane) {
+    return slab + (i * kWave + lane) * 8;
+}
+
 template <int KD, int NT, bool CONV>
 __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
                                                 const ScanBuf<bf16, KD, NT>* __restrict__ buf,
-                                                const ScanBuf<bf16, KD, NT>* __restrict__ prev,
-                                                const ScanLane<bf16, KD, NT>& ln, int t, int grp, int lane,
-                                                const ColTaps& cv)
+                                                const ScanLane<bf16, KD, NT>& ln, int t, int lane)
 {
+    const int grp = lane >> 4;
     typedef ScanBuf<bf16, KD, NT> SB;
     typedef Rec<bf16> RC;
 #pragma unroll
@@ -1532,30 +1548,10 @@ __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
     for (int f = 0; f < kTriFrags; ++f) op.tf[f] = ld<bf16x8>(buf->rec + RC::tfrag + (f * kWave + lane) * RC::frag_bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const s16x4 raw = lds_read_tr16(buf->v[t] + ln.vtr + i * 16 * SB::VRB);
         if constexpr (CONV) {
-            // rows 16 i + 4 g + e need rows back to 16 i + 4 g - 3: the four
-            // before them are 4 rows up in the slab, or, for lane group 0 of
-            // the first row tile, rows 60..63 of the previous chunk (still
-            // staged), or zero at the start of the sequence (prev null)
-            const bool head = i == 0 && grp == 0;
-            const unsigned char* pa = head ? (prev ? prev->v[t] + ln.vtr + 60 * SB::VRB : buf->v[t] + ln.vtr)
-                                           : buf->v[t] + ln.vtr + (16 * i - 4) * SB::VRB;
-            const s16x4 pr = lds_read_tr16(pa);
-            // rows in time order, two to a word: p = (p0, p1), (p2, p3); x = (x0, x1), (x2, x3)
-            const u32x2 x = __builtin_bit_cast(u32x2, raw);
-            u32x2 p = __builtin_bit_cast(u32x2, pr);
-            if (head && !prev) p = u32x2{0u, 0u};
-            const uint32_t p12 = pair_mid(p[0], p[1]), p3x0 = pair_mid(p[1], x[0]);
-            const uint32_t x12 = pair_mid(x[0], x[1]);
-            f32x4 y;
-            y[0] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p12, p3x0));
-            y[1] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p[1], x[0]));
-            y[2] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p3x0, x12));
-            y[3] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, x[0], x[1]));
-            // the values the scan sees are the bf16 convolution outputs
-            op.vv[i] = __builtin_convertvector(__builtin_convertvector(y, bf16x4), f32x4);
+            op.vv[i] = __builtin_convertvector(ld<bf16x4>(conv_slot(buf->v[t], i, lane)), f32x4);
         } else {
+            const s16x4 raw = lds_read_tr16(buf->v[t] + ln.vtr + i * 16 * SB::VRB);
             op.vv[i] = __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
         }
     }
@@ -1565,6 +1561,40 @@ __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
         op.fc[i] = ld<f32x4>(buf->rec + RC::fac + (2 * kChunk + 16 * i + 4 * grp) * 4);
     }
     op.gL = ld<float>(buf->rec + RC::fac + 3 * kChunk * 4);
+}
+
+// Conv wave, whole-prefill form: convolve row tile i of value tile t of a
+// staged chunk in place (see conv_slot), the raw rows read before the slot is
+// overwritten. Lane (g, col) takes rows 16 i + 4 g .. + 3 of column col, the
+// chain lane's rows. Rows 16 i + 4 g - 3 .. - 1 come 4 rows up in the slab,
+// or, for lane group 0 of row tile 0, from `halo` (the raw rows 60..63 of the
+// previous chunk, zero at the sequence start). Row tile 3 saves this chunk's
+// rows 60..63 in `next`. Tiles are taken from i = 3 down to 0, so no raw row
+// a later tile still needs has been overwritten.
+template <int KD, int NT>
+__device__ __forceinline__ void conv_tile(ScanBuf<bf16, KD, NT>* __restrict__ buf,
+                                               const ScanLane<bf16, KD, NT>& ln, int t, int i, int grp,
+                                               int lane, const ColTaps& cv, const u32x2& halo, u32x2& next)
+{
+    typedef ScanBuf<bf16, KD, NT> SB;
+    const bool head = i == 0 && grp == 0;
+    const unsigned char* xa = buf->v[t] + ln.vtr + i * 16 * SB::VRB;
+    // (group 0 of row tile 0 reads a valid address; its result is replaced)
+    const s16x4 raw = lds_read_tr16(xa);
+    const s16x4 pr = lds_read_tr16(head ? xa : xa - 4 * SB::VRB);
+    // rows in time order, two to a word: p = (p0, p1), (p2, p3); x = (x0, x1), (x2, x3)
+    const u32x2 x = __builtin_bit_cast(u32x2, raw);
+    const u32x2 p = head ? halo : __builtin_bit_cast(u32x2, pr);
+    if (i == 3) next = x;
+    const uint32_t p12 = pair_mid(p[0], p[1]), p3x0 = pair_mid(p[1], x[0]);
+    const uint32_t x12 = pair_mid(x[0], x[1]);
+    f32x4 y;
+    y[0] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p12, p3x0));
+    y[1] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p[1], x[0]));
+    y[2] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, p3x0, x12));
+    y[3] = conv_silu(conv_taps4_bf16(cv.w01, cv.w23, cv.b, x[0], x[1]));
+    // the values the scan sees are the bf16 convolution outputs
+    *reinterpret_cast<bf16x4*>(conv_slot(buf->v[t], i, lane)) = __builtin_convertvector(y, bf16x4);
 }
 
 template <int KD>
@@ -1599,7 +1629,7 @@ __device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restri
                                            RoleHand<KD, NT>* __restrict__ hand,
                                            const ScanLane<bf16, KD, NT>& ln, int t, int grp, int col,
                                            f32x4 (&hs)[KD / 16], bf16x8 (&hf)[KD / 32],
-                                           ChainOps<KD>& op, const ColTaps& cv)
+                                           ChainOps<KD>& op)
 {
     typedef Mma<bf16> MT;
     typedef bf16x8 Frag;
@@ -1650,7 +1680,7 @@ __device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restri
     lds_barrier();   // U is visible to the output wave; the next chunk has landed
 
     // ---- the next chunk's operands, then h' = gamma_L h + K^T (c o U)
-    chain_load<KD, NT, CONV>(op, ahead, cur, ln, t, grp, lane, cv);
+    chain_load<KD, NT, CONV>(op, ahead, ln, t, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) U[rt] *= fc[rt];
     const Frag df0 = MT::acc_frag(U[0], U[1]);
@@ -1724,9 +1754,18 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
 
 // CONV (whole-prefill form): vp points at the raw value rows before the
 // short convolution, whose taps and bias for value channel 0 of head 0 are at
-// wv and bv (bv may be null); the chain waves convolve them as they read them.
+// wv and bv (bv may be null). A fifth wave, the conv wave, convolves each
+// chunk's staged values in place (conv_tile) in the step before the chain
+// waves read them; the copy wave stages values one chunk further ahead than
+// the rest, so they have landed a step before that. The conv wave shares a
+// SIMD with the copy wave, which issues little besides its copies.
+template <int NT, bool CONV>
+constexpr int roles_waves() { return NT + 2 + (CONV ? 1 : 0); }
+
 template <int KD, int NT, int NBUF, bool CONV>
-__global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_roles_kernel(
+__global__ __launch_bounds__((NT + 2 + (CONV ? 1 : 0)) * kWave)
+__attribute__((amdgpu_waves_per_eu((NT + 5 + (CONV ? 1 : 0)) / 4, (NT + 5 + (CONV ? 1 : 0)) / 4)))
+void chunk_scan_roles_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
     const bf16* __restrict__ vp, int64_t v_stride,
     const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
@@ -1762,8 +1801,13 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
     const int h = u - seq * H;
 
     const int lane = threadIdx.x & (kWave - 1);
-    // waves 0 .. NT - 1: chain of column tile `role`; NT: output; NT + 1: copy
-    const int role = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    // roles: 0 .. NT - 1 chain of column tile `role`; NT output; NT + 1 copy;
+    // NT + 2 conv (whole-prefill form). Waves in that order, except that with a
+    // conv wave the copy wave comes first, so that the two share SIMD 0.
+    constexpr int kRoleCopy = NT + 1, kRoleConv = NT + 2;
+    constexpr int nwaves = roles_waves<NT, CONV>();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int role = !CONV ? wave : wave == 0 ? kRoleCopy : wave <= NT + 1 ? wave - 1 : kRoleConv;
     const int grp = lane >> 4;
     const int col = lane & 15;
 
@@ -1815,7 +1859,7 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
     // them at zero so they hold finite values (their factors are zero).
     if ((a.tok_end - a.tok_begin) % kChunk != 0) {
         const f32x4 z = zero4();
-        for (int i = threadIdx.x * 16; i < NBUF * (int)sizeof(SB); i += (NT + 2) * kWave * 16)
+        for (int i = threadIdx.x * 16; i < NBUF * (int)sizeof(SB); i += nwaves * kWave * 16)
             *reinterpret_cast<f32x4*>(smem_raw + i) = z;
         lds_barrier();
     }
@@ -1841,21 +1885,14 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
             hf[kb] = state_frag<T>(hs[2 * kb], hs[2 * kb + 1], grp);
             hand->h[kb][t][lane] = hf[kb];
         }
-        ColTaps cv{};
-        if constexpr (CONV) {
-            const int64_t chn = (int64_t)h * V + vc;
-            const u32x2 tw = *reinterpret_cast<const u32x2*>(wv + chn * 4);
-            cv.w01 = tw[0];
-            cv.w23 = tw[1];
-            cv.b = bv ? (float)bv[chn] : 0.f;
-        }
         lds_barrier();
+        if constexpr (CONV) lds_barrier();   // chunk 0's values are convolved
         ChainOps<KD> op;
-        chain_load<KD, NT, CONV>(op, &bufs[0], nullptr, ln, t, grp, lane, cv);
+        chain_load<KD, NT, CONV>(op, &bufs[0], ln, t, lane);
         int b = 0;
         for (int c = 0; c < nchunks; ++c) {
             const int bn = b == NBUF - 1 ? 0 : b + 1;
-            role_chain<KD, NT, CONV>(&bufs[b], &bufs[bn], hand, ln, t, grp, col, hs, hf, op, cv);
+            role_chain<KD, NT, CONV>(&bufs[b], &bufs[bn], hand, ln, t, grp, col, hs, hf, op);
             lds_barrier();
             b = bn;
         }
@@ -1870,6 +1907,7 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
         const int64_t HV = (int64_t)H * V;
         const uint32_t o_row = (uint32_t)(HV * ES);
         lds_barrier();
+        if constexpr (CONV) lds_barrier();
         OutOps<KD> op;
         int b = 0;
         for (int c = 0; c < nchunks; ++c) {
@@ -1881,7 +1919,7 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
             lds_barrier();
             b = bn;
         }
-    } else {
+    } else if (role == kRoleCopy) {
         // ---------------- copy
         uint32_t tsrc[TP];
 #pragma unroll
@@ -1901,18 +1939,25 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
         // A chunk's copies go out in two parts, one on each side of the
         // mid-step barrier, so that the copy engine works through the whole
         // step: part A (the K tile, the values and the prefetch of chunk cp)
-        // and part B (the Q tile and the record).
-        constexpr int partA = TP + NT * SB::v_pieces + kPrefetchSlots;
-        auto issue_a = [&](int cs, int cp, SB* __restrict__ dst) {
+        // and part B (the Q tile and the record). In the whole-prefill form the
+        // values go out on their own, after the mid-step barrier of the step
+        // two chunks earlier (issue_v).
+        constexpr int nv = NT * SB::v_pieces;
+        constexpr int partA = TP + (CONV ? 0 : nv) + kPrefetchSlots;
+        auto issue_v = [&](int cs, SB* __restrict__ dst) {
             const ChunkSpan sp = chunk_span<T, KD, NT>(cs, a, a.c0);
-            const rsrc_t rk = make_rsrc((const void*)sp.k, sp.kq_bytes);
             const rsrc_t rv = make_rsrc((const void*)sp.v, sp.v_bytes);
-#pragma unroll
-            for (int j = 0; j < TP; ++j) dma16(rk, dst->k + j * 1024, tsrc[j], 0);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int p = 0; p < SB::v_pieces; ++p) dma16(rv, dst->v[t] + p * 1024, vsrc[p], t * 16 * ES);
+        };
+        auto issue_a = [&](int cs, int cp, SB* __restrict__ dst) {
+            const ChunkSpan sp = chunk_span<T, KD, NT>(cs, a, a.c0);
+            const rsrc_t rk = make_rsrc((const void*)sp.k, sp.kq_bytes);
+#pragma unroll
+            for (int j = 0; j < TP; ++j) dma16(rk, dst->k + j * 1024, tsrc[j], 0);
+            if constexpr (!CONV) issue_v(cs, dst);
             const bool pvalid = cp < nchunks;
             const int pc = pvalid ? cp : 0;
             const uint32_t pL = pvalid ? (uint32_t)min(kChunk, a.tok_end - (a.tok_begin + cp * kChunk)) : 0u;
@@ -1933,23 +1978,90 @@ __global__ __launch_bounds__((NT + 2) * kWave) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int j = 0; j < RP; ++j) dma16(rr, dst->rec + j * 1024, lane * 16, j * 1024);
         };
-        issue_a(0, NBUF - 1, &bufs[0]);
-        issue_b(0, &bufs[0]);
-        issue_a(1, NBUF, &bufs[1]);
-        issue_b(1, &bufs[1]);
-        wait_vmcnt<loads + kPrefetchSlots>();   // chunk 0 has landed (younger: chunk 1's copies)
-        lds_barrier();
+        if constexpr (CONV) {
+            // chunk 0 and chunk 1's values must land before the loop (the conv
+            // wave takes them in the prologue), chunk 2's by the first mid-step
+            issue_v(0, &bufs[0]);
+            issue_a(0, NBUF - 1, &bufs[0]);
+            issue_b(0, &bufs[0]);
+            issue_v(1, &bufs[1]);
+            issue_a(1, NBUF, &bufs[1]);
+            issue_b(1, &bufs[1]);
+            issue_v(2, &bufs[2]);
+            wait_vmcnt<partA + TP + RP + nv>();   // younger: chunk 1's other copies, chunk 2's values
+            lds_barrier();
+            lds_barrier();   // chunk 0's values (and half of chunk 1's) are convolved
+        } else {
+            issue_a(0, NBUF - 1, &bufs[0]);
+            issue_b(0, &bufs[0]);
+            issue_a(1, NBUF, &bufs[1]);
+            issue_b(1, &bufs[1]);
+            wait_vmcnt<loads + kPrefetchSlots>();   // chunk 0 has landed (younger: chunk 1's copies)
+            lds_barrier();
+        }
         int b = 0;
         for (int c = 0; c < nchunks; ++c) {
             const int bp = b == 0 ? NBUF - 1 : b - 1;
             issue_a(c + NBUF - 1, c + NBUF - 1 + kPrefetchAhead, &bufs[bp]);
-            wait_vmcnt<partA>();   // chunk c + 1 has landed (younger: this step's part A)
+            // chunk c + 1 has landed (younger: this step's part A); with CONV
+            // also chunk c + 2's values, issued a step ago
+            wait_vmcnt<partA>();
             lds_barrier();         // mid-step
+            // (CONV: chunk c's values were read by the chains a step ago)
+            if constexpr (CONV) issue_v(c + NBUF, &bufs[b]);
             issue_b(c + NBUF - 1, &bufs[bp]);
             lds_barrier();         // end of step
             b = b == NBUF - 1 ? 0 : b + 1;
         }
         wait_vmcnt<0>();   // no copy into LDS may outlive the workgroup
+    } else if constexpr (CONV) {
+        // ---------------- conv (whole-prefill form)
+        // A chunk's value slabs are convolved in two halves: items 0 .. 2 NT - 1
+        // and 2 NT .. 4 NT - 1, item k being row tile 3 - k % 4 of tile k / 4.
+        // Chunk c + 2's first half is done after the mid-step barrier of step
+        // c, its second half before the mid-step barrier of step c + 1, by
+        // which the chain waves read it.
+        ColTaps cv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int64_t chn = (int64_t)h * V + a.c0 + 16 * t + col;
+            const u32x2 tw = *reinterpret_cast<const u32x2*>(wv + chn * 4);
+            cv[t].w01 = tw[0];
+            cv[t].w23 = tw[1];
+            cv[t].b = bv ? (float)bv[chn] : 0.f;
+        }
+        // per tile: raw rows 60..63 of the chunk before (cur; zero before the
+        // first) and of this chunk (nxt), as held by lane group 3
+        u32x2 cur[NT], nxt[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) cur[t] = nxt[t] = u32x2{0u, 0u};
+        const int from = (48 + col) * 4;   // byte index of lane (3, col)
+        auto convert = [&](int cc, int half) {
+            if (cc >= nchunks) return;
+            SB* __restrict__ buf = &bufs[cc % NBUF];
+#pragma unroll
+            for (int k = half * 2 * NT; k < (half + 1) * 2 * NT; ++k) {
+                const int t = k / 4, i = 3 - k % 4;
+                u32x2 halo = u32x2{0u, 0u};
+                if (i == 0) {
+                    halo[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[t][0]);
+                    halo[1] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[t][1]);
+                }
+                conv_tile<KD, NT>(buf, ln, t, i, grp, lane, cv[t], halo, nxt[t]);
+                if (i == 0) cur[t] = nxt[t];
+            }
+        };
+        lds_barrier();
+        convert(0, 0);
+        convert(0, 1);
+        convert(1, 0);
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            convert(c + 1, 1);
+            lds_barrier();   // mid-step
+            convert(c + 2, 0);
+            lds_barrier();   // end of step
+        }
     }
 }
 
@@ -2017,7 +2129,7 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
     auto kern = chunk_scan_roles_kernel<KD, NT, NBUF, CONV>;
     hipError_t err = set_smem(kern, smem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3((NT + 2) * kWave), smem, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(upad * groups)), dim3(roles_waves<NT, CONV>() * kWave), smem, stream,
                        (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf, (bf16*)o,
                        cu, offsets, wsrec, T_len, H, Hk, V, units, groups, (const bf16*)wv,
                        (const bf16*)bv);
