@@ -63,6 +63,10 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration runs)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--no-flush", action="store_true",
+                   help="skip the per-iteration timings with the caches flushed between "
+                        "iterations (profiling runs: every traced launch then runs warm, as in "
+                        "the timed steps)")
     p.add_argument("--no-chain", action="store_true",
                    help="skip the four-call chain (conv1d, gates, chunk_prepare, chunk_scan)")
     p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
@@ -74,6 +78,9 @@ def parse():
                    help="write the MFMA-busy summary of a --pmc SQ_VALU_MFMA_BUSY_CYCLES "
                         "SQ_INSTS_MFMA GRBM_GUI_ACTIVE run")
     p.add_argument("--command", default="", help="the command that produced the CSVs")
+    p.add_argument("--bench-log", default=None,
+                   help="with --summarize-stats: the profiled run's output, whose bench line "
+                        "gives the same run's kernel times measured with HIP events")
     return p.parse_args()
 
 
@@ -278,8 +285,9 @@ def run_prefill(args, gdn, wl, torch, dev, stream):
              for j, op in enumerate(ops)}
     # per-iteration statistics: back to back, and with the caches flushed
     # between iterations (outside the timed region)
-    stats = {"back_to_back": iter_stats(step, torch, stream, args.steps),
-             "flushed": iter_stats(step, torch, stream, args.steps, Flush(torch, dev))}
+    stats = {"back_to_back": iter_stats(step, torch, stream, args.steps)}
+    if not args.no_flush:
+        stats["flushed"] = iter_stats(step, torch, stream, args.steps, Flush(torch, dev))
     return w, op_ms, step_ms, stats
 
 
@@ -327,8 +335,9 @@ def run_chain(args, gdn, wl, torch, dev, stream):
     def chunk():
         gdn.gdn_chunk_prepare(q, k, g, beta, ws)
         gdn.gdn_chunk_scan(q, k, v, o, ws, final_state=fs)
-    chunk_stats = {"back_to_back": iter_stats(chunk, torch, stream, args.steps),
-                   "flushed": iter_stats(chunk, torch, stream, args.steps, Flush(torch, dev))}
+    chunk_stats = {"back_to_back": iter_stats(chunk, torch, stream, args.steps)}
+    if not args.no_flush:
+        chunk_stats["flushed"] = iter_stats(chunk, torch, stream, args.steps, Flush(torch, dev))
     return {"us": step_ms * 1e3, "tokens_per_s": tokens / (step_ms / 1e3), "ops_us": op_us,
             "chunk_fwd_iters": chunk_stats}
 
@@ -503,7 +512,7 @@ def _phases(rows, id_key, name_key):
     return phase
 
 
-def summarize_stats(csv_path, out_md, command):
+def summarize_stats(csv_path, out_md, command, bench_log=None):
     """Kernel time table from rocprofv3's kernel trace (one row per dispatch),
     one line per (benchmark part, kernel, grid, workgroup)."""
     import collections
@@ -529,6 +538,15 @@ def summarize_stats(csv_path, out_md, command):
         lines.append(f"| {ph} | `{_kernel_stem(name)}` | {grid} | {wg} | {len(d)} | "
                      f"{sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
                      f"{100 * sum(d) / total:.1f}% |")
+    if bench_log:
+        js = [ln for ln in open(bench_log) if ln.startswith("{")]
+        b = json.loads(js[-1])
+        lines += ["", "The same run's bench line (HIP events on the launch stream, averaged over",
+                  "the timed steps), for comparison with the trace averages above:", ""]
+        for op, us in b.get("ops_us", {}).items():
+            lines.append(f"- {op} (`{KERNELS[op][0]}`): {us:.2f} us")
+        if "decode" in b:
+            lines.append(f"- decode step (`{b['decode']['kernel']}`): {b['decode']['us_per_step']:.2f} us")
     lines += ["", "Full symbols:", ""]
     seen = set()
     for (_, name, _, _), _ in items:
@@ -630,7 +648,8 @@ def main():
         summarize_mfma(args.summarize_mfma[0], args.summarize_mfma[1], args.command)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command)
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command,
+                        args.bench_log)
         return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
