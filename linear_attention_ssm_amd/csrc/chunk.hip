@@ -1475,7 +1475,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // ------------------------------------------------------------ chunk_scan, role-split waves (bf16)
 //
 // One workgroup per (sequence, value head, 16 NT value columns) with NT + 2
-// waves, one per SIMD (NT + 3 in the whole-prefill form, see below):
+// waves, one per SIMD (2 NT + 2 in the whole-prefill form, see below):
 //   chain t owns the fp32 state of column tile t (16 columns) and runs the
 //           dependent part of a chunk: X = K h, U = T (V - a o X), h' =
 //           gamma_L h + K^T (c o U);
@@ -1493,12 +1493,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // wave through LDS. A chain wave reads a chunk's operands one step ahead,
 // right after the mid-step barrier by which the copy wave has seen it land;
 // the output wave reads its own at the start of the step.
-// In the whole-prefill form the values are staged raw and a conv wave
-// convolves each chunk's value slabs in place during the step before the
-// chains read them, half before and half after the mid-step barrier (with one
-// column tile it has a SIMD of its own; with two it shares the copy wave's).
-// Measured on MI355X: with one tile (the GQA workload) this is 9% faster than
-// convolving in the chain waves; with two, the same within noise.
+// In the whole-prefill form the values are staged raw and one conv wave per
+// column tile convolves its slab of each chunk in place during the step
+// before the chains read them, half before and half after the mid-step
+// barrier. Measured on MI355X (per-wave cycle stamps): this takes the
+// convolution off the chains' dependent path; a chunk's step went from
+// about 3,300 cycles (convolving in the chain waves) to 2,900.
 template <int KD, int NT>
 struct RoleHand {
     bf16x8 h[KD / 32][NT][kWave];   // h of the step's chunk: B operand per contraction block and tile
@@ -1563,29 +1563,30 @@ __device__ __forceinline__ void chain_load(ChainOps<KD>& op,
     op.gL = ld<float>(buf->rec + RC::fac + 3 * kChunk * 4);
 }
 
-// Conv wave, whole-prefill form: convolve row tile i of value tile t of a
-// staged chunk in place (see conv_slot), the raw rows read before the slot is
-// overwritten. Lane (g, col) takes rows 16 i + 4 g .. + 3 of column col, the
-// chain lane's rows. Rows 16 i + 4 g - 3 .. - 1 come 4 rows up in the slab,
-// or, for lane group 0 of row tile 0, from `halo` (the raw rows 60..63 of the
-// previous chunk, zero at the sequence start). Row tile 3 saves this chunk's
-// rows 60..63 in `next`. Tiles are taken from i = 3 down to 0, so no raw row
-// a later tile still needs has been overwritten.
+// Conv wave, whole-prefill form: row tile i of value tile t of a staged chunk
+// is convolved in place (see conv_slot). Lane (g, col) takes rows
+// 16 i + 4 g .. + 3 of column col, the chain lane's rows: conv_rows reads them
+// raw (x) with the four rows before them (p: 4 rows up in the slab; for lane
+// group 0 of row tile 0 a valid address whose result the caller replaces by
+// the raw rows 60..63 of the previous chunk, zero at the sequence start), and
+// conv_put convolves and writes them over the slot. A tile's raw rows
+// 16 i - 4 .. 16 i + 15 lie in its own slot and the one before, so a set of
+// tiles all read before any of them is written may be converted in any order.
 template <int KD, int NT>
-__device__ __forceinline__ void conv_tile(ScanBuf<bf16, KD, NT>* __restrict__ buf,
+__device__ __forceinline__ void conv_rows(const ScanBuf<bf16, KD, NT>* __restrict__ buf,
                                                const ScanLane<bf16, KD, NT>& ln, int t, int i, int grp,
-                                               int lane, const ColTaps& cv, const u32x2& halo, u32x2& next)
+                                               u32x2& x, u32x2& p)
 {
     typedef ScanBuf<bf16, KD, NT> SB;
-    const bool head = i == 0 && grp == 0;
     const unsigned char* xa = buf->v[t] + ln.vtr + i * 16 * SB::VRB;
-    // (group 0 of row tile 0 reads a valid address; its result is replaced)
-    const s16x4 raw = lds_read_tr16(xa);
-    const s16x4 pr = lds_read_tr16(head ? xa : xa - 4 * SB::VRB);
+    x = __builtin_bit_cast(u32x2, lds_read_tr16(xa));
+    p = __builtin_bit_cast(u32x2, lds_read_tr16(i == 0 && grp == 0 ? xa : xa - 4 * SB::VRB));
+}
+template <int KD, int NT>
+__device__ __forceinline__ void conv_put(ScanBuf<bf16, KD, NT>* __restrict__ buf, int t, int i, int lane,
+                                              const ColTaps& cv, const u32x2& x, const u32x2& p)
+{
     // rows in time order, two to a word: p = (p0, p1), (p2, p3); x = (x0, x1), (x2, x3)
-    const u32x2 x = __builtin_bit_cast(u32x2, raw);
-    const u32x2 p = head ? halo : __builtin_bit_cast(u32x2, pr);
-    if (i == 3) next = x;
     const uint32_t p12 = pair_mid(p[0], p[1]), p3x0 = pair_mid(p[1], x[0]);
     const uint32_t x12 = pair_mid(x[0], x[1]);
     f32x4 y;
@@ -1754,17 +1755,19 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
 
 // CONV (whole-prefill form): vp points at the raw value rows before the
 // short convolution, whose taps and bias for value channel 0 of head 0 are at
-// wv and bv (bv may be null). A fifth wave, the conv wave, convolves each
-// chunk's staged values in place (conv_tile) in the step before the chain
-// waves read them; the copy wave stages values one chunk further ahead than
-// the rest, so they have landed a step before that. The conv wave shares a
-// SIMD with the copy wave, which issues little besides its copies.
+// wv and bv (bv may be null). NT more waves, the conv waves (one per column
+// tile), convolve each chunk's staged values in place (conv_rows, conv_put)
+// in the step before the chain waves read them; the copy wave stages values
+// one chunk further ahead than the rest, so they have landed a step before
+// that. Waves go copy, output, chains, conv: with two tiles the conv waves
+// share SIMDs with the copy and output waves, which leave the VALU mostly
+// idle; with one, every wave has a SIMD of its own.
 template <int NT, bool CONV>
-constexpr int roles_waves() { return NT + 2 + (CONV ? 1 : 0); }
+constexpr int roles_waves() { return NT + 2 + (CONV ? NT : 0); }
 
 template <int KD, int NT, int NBUF, bool CONV>
-__global__ __launch_bounds__((NT + 2 + (CONV ? 1 : 0)) * kWave)
-__attribute__((amdgpu_waves_per_eu((NT + 5 + (CONV ? 1 : 0)) / 4, (NT + 5 + (CONV ? 1 : 0)) / 4)))
+__global__ __launch_bounds__((NT + 2 + (CONV ? NT : 0)) * kWave)
+__attribute__((amdgpu_waves_per_eu((NT + 5 + (CONV ? NT : 0)) / 4, (NT + 5 + (CONV ? NT : 0)) / 4)))
 void chunk_scan_roles_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
     const bf16* __restrict__ vp, int64_t v_stride,
@@ -1802,12 +1805,13 @@ void chunk_scan_roles_kernel(
 
     const int lane = threadIdx.x & (kWave - 1);
     // roles: 0 .. NT - 1 chain of column tile `role`; NT output; NT + 1 copy;
-    // NT + 2 conv (whole-prefill form). Waves in that order, except that with a
-    // conv wave the copy wave comes first, so that the two share SIMD 0.
+    // NT + 2 + t conv of tile t (whole-prefill form). Waves in that order,
+    // except that with conv waves they go copy, output, chains, conv (a
+    // workgroup's wave w runs on SIMD (s + w) mod 4 for some s)
     constexpr int kRoleCopy = NT + 1, kRoleConv = NT + 2;
     constexpr int nwaves = roles_waves<NT, CONV>();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int role = !CONV ? wave : wave == 0 ? kRoleCopy : wave <= NT + 1 ? wave - 1 : kRoleConv;
+    const int role = !CONV ? wave : wave == 0 ? kRoleCopy : wave == 1 ? NT : wave <= NT + 1 ? wave - 2 : wave;
     const int grp = lane >> 4;
     const int col = lane & 15;
 
@@ -2015,41 +2019,44 @@ void chunk_scan_roles_kernel(
         }
         wait_vmcnt<0>();   // no copy into LDS may outlive the workgroup
     } else if constexpr (CONV) {
-        // ---------------- conv (whole-prefill form)
-        // A chunk's value slabs are convolved in two halves: items 0 .. 2 NT - 1
-        // and 2 NT .. 4 NT - 1, item k being row tile 3 - k % 4 of tile k / 4.
-        // Chunk c + 2's first half is done after the mid-step barrier of step
-        // c, its second half before the mid-step barrier of step c + 1, by
-        // which the chain waves read it.
-        ColTaps cv[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        // ---------------- conv of column tile t (whole-prefill form)
+        // A chunk's value slab of tile t is convolved in two halves, row tiles
+        // 3 and 2, then 1 and 0: chunk c + 2's first half after the mid-step
+        // barrier of step c, its second half before the mid-step barrier of
+        // step c + 1, by which the chain waves read it.
+        const int t = role - kRoleConv;
+        ColTaps cv;
+        {
             const int64_t chn = (int64_t)h * V + a.c0 + 16 * t + col;
             const u32x2 tw = *reinterpret_cast<const u32x2*>(wv + chn * 4);
-            cv[t].w01 = tw[0];
-            cv[t].w23 = tw[1];
-            cv[t].b = bv ? (float)bv[chn] : 0.f;
+            cv.w01 = tw[0];
+            cv.w23 = tw[1];
+            cv.b = bv ? (float)bv[chn] : 0.f;
         }
-        // per tile: raw rows 60..63 of the chunk before (cur; zero before the
-        // first) and of this chunk (nxt), as held by lane group 3
-        u32x2 cur[NT], nxt[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) cur[t] = nxt[t] = u32x2{0u, 0u};
+        // raw rows 60..63 of the chunk before (cur; zero before the first) and
+        // of this chunk (nxt), as held by lane group 3
+        u32x2 cur = u32x2{0u, 0u}, nxt = u32x2{0u, 0u};
         const int from = (48 + col) * 4;   // byte index of lane (3, col)
+        // a half's two row tiles are both read, then both convolved and
+        // written (their dependent arithmetic interleaves); the second half's
+        // row tiles lie above the first's
         auto convert = [&](int cc, int half) {
             if (cc >= nchunks) return;
             SB* __restrict__ buf = &bufs[cc % NBUF];
+            u32x2 xs[2], ps[2];
 #pragma unroll
-            for (int k = half * 2 * NT; k < (half + 1) * 2 * NT; ++k) {
-                const int t = k / 4, i = 3 - k % 4;
-                u32x2 halo = u32x2{0u, 0u};
-                if (i == 0) {
-                    halo[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[t][0]);
-                    halo[1] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[t][1]);
-                }
-                conv_tile<KD, NT>(buf, ln, t, i, grp, lane, cv[t], halo, nxt[t]);
-                if (i == 0) cur[t] = nxt[t];
+            for (int n = 0; n < 2; ++n) conv_rows<KD, NT>(buf, ln, t, 3 - 2 * half - n, grp, xs[n], ps[n]);
+            if (half == 0) {
+                nxt = xs[0];
+            } else {
+                u32x2 halo;
+                halo[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[0]);
+                halo[1] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)cur[1]);
+                if (grp == 0) ps[1] = halo;
+                cur = nxt;
             }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) conv_put<KD, NT>(buf, t, 3 - 2 * half - n, lane, cv, xs[n], ps[n]);
         };
         lds_barrier();
         convert(0, 0);
