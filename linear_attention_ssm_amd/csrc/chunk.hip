@@ -1742,15 +1742,37 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
         uf[t][1] = hand->u[1][t][lane];
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             O[t][rt] = MT::mma(uf[t][0], op.pf[tri_frag(rt, 0)], O[t][rt]);
             if (rt >= 2) O[t][rt] = MT::mma(uf[t][1], op.pf[tri_frag(rt, 1)], O[t][rt]);
-            const bf16x4 ob = __builtin_convertvector(O[t][rt], bf16x4);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
-                                                  (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
         }
+        if constexpr (NT == 2) {
+            // one 16-byte store per lane: lane (g, c) holds columns 4 g .. + 3
+            // of each tile in row c; two lane swaps (32 lanes apart, then 16)
+            // give lane (g, c) the workgroup's columns 8 g .. + 7 instead, so a
+            // row's 64 bytes go out as one piece (half the store requests)
+            const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(O[0][rt], bf16x4));
+            const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(O[1][rt], bf16x4));
+            u32x4 s;
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto w32 = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+                const auto w16 = __builtin_amdgcn_permlane16_swap(w32[0], w32[1], false, false);
+                s[d] = w16[0];
+                s[2 + d] = w16[1];
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(s, ro, (uint32_t)(16 * rt + col) * o_row + 16 * grp, 0, 0);
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bf16x4 ob = __builtin_convertvector(O[t][rt], bf16x4);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
+                                                      (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
+            }
+        }
+    }
 }
 
 // CONV (whole-prefill form): vp points at the raw value rows before the
