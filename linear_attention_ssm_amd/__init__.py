@@ -4,7 +4,7 @@ The functions below carry the names of the C entry points in include/gdn.h and
 only marshal arguments: tensor -> device pointer, strides, dtype code, the
 current HIP stream. Every step of the computation runs in the library's HIP
 kernels; there is no fallback. Importing this package fails if libgdn.so has
-not been built (``python -m linear_attention_ssm_amd.build``), and every call
+not been built (``python linear_attention_ssm_amd/build.py``), and every call
 fails on tensors that are not on a GPU.
 
 PyTorch is used for device memory (allocating outputs and workspaces) and for
@@ -35,7 +35,7 @@ _DTYPE_CODE = {torch.float32: GDN_FP32, torch.bfloat16: GDN_BF16}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m linear_attention_ssm_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python linear_attention_ssm_amd/build.py` "
         "(the HIP library is the only implementation; there is no fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,8 @@
 """Build libgdn.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
 
-    python -m linear_attention_ssm_amd.build        # or build_library() from Python
+    python linear_attention_ssm_amd/build.py        # or build_library() from Python
+
+(run as a file: importing the package needs the library already built)
 
 Each .hip source is compiled to an object in parallel, then linked into
 linear_attention_ssm_amd/libgdn.so. All device code is built for gfx950 only,

@@ -33,7 +33,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libgdn.so is not built (run `python -m linear_attention_ssm_amd.build`)")
+        pytest.fail("libgdn.so is not built (run `python linear_attention_ssm_amd/build.py`)")
     L = ctypes.CDLL(LIB)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.gdn_status_string.argtypes = [i32]
