@@ -123,6 +123,24 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _tstride(t: torch.Tensor, row: int) -> int:
+    """Token stride of a [B, T, ...] tensor as the library takes it (batch b,
+    token t at (b T + t) * stride). A length-1 dimension may carry any stride:
+    with one token per batch row the batch stride is the token stride, and a
+    lone row gets any stride at least a row long."""
+    B, T = t.shape[:2]
+    if T == 1 and B > 1:
+        return t.stride(0)
+    if T <= 1:
+        return max(t.stride(1), row)
+    return t.stride(1)
+
+
+def _even_batches(t: torch.Tensor) -> bool:
+    B, T = t.shape[:2]
+    return B <= 1 or T <= 1 or t.stride(0) == T * t.stride(1)
+
+
 # --------------------------------------------------------------------- conv1d
 
 def gdn_conv1d_causal(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
@@ -143,8 +161,11 @@ def gdn_conv1d_causal(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None =
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    rc = _lib.gdn_conv1d_causal(_dev(x, "x"), x.stride(0), x.stride(1), _dev(w, "w"),
-                                _opt(bias, "bias"), _dev(y, "y"), y.stride(0), y.stride(1),
+    # (one token per row: its token stride is never used, and a length-1
+    # dimension may carry any stride)
+    xt, yt = (x.stride(1), y.stride(1)) if T > 1 else (C, C)
+    rc = _lib.gdn_conv1d_causal(_dev(x, "x"), x.stride(0), xt, _dev(w, "w"),
+                                _opt(bias, "bias"), _dev(y, "y"), y.stride(0), yt,
                                 _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, C, w.shape[1],
                                 int(bool(silu)), _code(x.dtype), _stream(x.device))
     _check(rc, "gdn_conv1d_causal")
@@ -195,11 +216,9 @@ def _token_rows(t: torch.Tensor, name: str, heads: int, d: int):
     """[B, T, heads, d] with contiguous (heads, d) and batch stride T * token stride."""
     if t.dim() != 4 or t.shape[2] != heads or t.shape[3] != d:
         raise ValueError(f"{name} must be [B, T, {heads}, {d}]")
-    B, T = t.shape[:2]
-    st = t.stride(1)
-    if t.stride(3) != 1 or t.stride(2) != d or (B > 1 and T > 0 and t.stride(0) != T * st):
+    if t.stride(3) != 1 or (heads > 1 and t.stride(2) != d) or not _even_batches(t):
         raise ValueError(f"{name}: heads and head dim must be contiguous and batches evenly strided")
-    return st
+    return _tstride(t, heads * d)
 
 
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -278,7 +297,7 @@ def _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens):
     B, T, C = x.shape
     if C != 2 * Hk * K + H * V:
         raise ValueError(f"x has {C} channels, expected 2*Hk*K + H*V = {2 * Hk * K + H * V}")
-    if B > 1 and T > 0 and x.stride(0) != T * x.stride(1):
+    if not _even_batches(x):
         raise ValueError("x: batch rows must be evenly strided (stride(0) == T * stride(1))")
     if w.shape != (C, 4) or not w.is_contiguous() or w.dtype != x.dtype:
         raise ValueError("w must be a contiguous [C, 4] tensor of x's dtype")
@@ -287,8 +306,7 @@ def _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens):
     for t, n in ((a, "a"), (b, "b")):
         if t is None:
             continue
-        if t.shape != (B, T, H) or t.dtype != x.dtype or t.stride(2) != 1 or \
-                (B > 1 and T > 0 and t.stride(0) != T * t.stride(1)):
+        if t.shape != (B, T, H) or t.dtype != x.dtype or t.stride(2) != 1 or not _even_batches(t):
             raise ValueError(f"{n} must be [B, T, H] of x's dtype, head dim contiguous, "
                              "batch rows evenly strided")
     for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
@@ -339,8 +357,8 @@ def gdn_prefill(x: torch.Tensor, w: torch.Tensor, a: torch.Tensor, b: torch.Tens
     o, final_state = _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state,
                                       output_final_state, o, final_state)
     workspace = _prefill_ws(workspace, x, B, T, H, Hk, K, V, n_seqs)
-    rc = _lib.gdn_prefill(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
-                          _dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
+    rc = _lib.gdn_prefill(_dev(x, "x"), _tstride(x, x.shape[2]), _dev(w, "w"), _opt(bias, "bias"),
+                          _dev(a, "a"), _tstride(a, H), _dev(b, "b"), _tstride(b, H),
                           _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
                           _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
                           _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
@@ -355,8 +373,9 @@ def gdn_prefill_prepare(x, w, a, b, A_log, dt_bias, workspace, *, Hk, K, H, V, b
                         cu_seqlens=None, scale=1.0, qk_l2norm=True):
     """Phase 1 of gdn_prefill (q/k convolution, gates, per-chunk solve) into `workspace`."""
     B, T, n_seqs = _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens)
-    rc = _lib.gdn_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
-                                  _dev(a, "a"), a.stride(1), _dev(b, "b"), b.stride(1),
+    rc = _lib.gdn_prefill_prepare(_dev(x, "x"), _tstride(x, x.shape[2]), _dev(w, "w"),
+                                  _opt(bias, "bias"), _dev(a, "a"), _tstride(a, H), _dev(b, "b"),
+                                  _tstride(b, H),
                                   _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
                                   _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
                                   float(scale), int(bool(qk_l2norm)), _code(x.dtype),
@@ -371,7 +390,7 @@ def gdn_prefill_scan(x, w, workspace, *, Hk, K, H, V, bias=None, initial_state=N
     B, T, n_seqs = _prefill_args(x, w, None, None, None, None, Hk, K, H, V, bias, cu_seqlens)
     o, final_state = _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state,
                                       output_final_state, o, final_state)
-    rc = _lib.gdn_prefill_scan(_dev(x, "x"), x.stride(1), _dev(w, "w"), _opt(bias, "bias"),
+    rc = _lib.gdn_prefill_scan(_dev(x, "x"), _tstride(x, x.shape[2]), _dev(w, "w"), _opt(bias, "bias"),
                                _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
                                _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk,
                                K, V, _code(x.dtype), _dev(workspace, "workspace"),
@@ -512,7 +531,7 @@ def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tens
     if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[:2] != (B, T) or ba.dtype != x.dtype:
         raise ValueError("x and ba must be [B, T, row] with contiguous rows of one dtype")
     for t, name in ((x, "x"), (ba, "ba")):
-        if B > 1 and T > 0 and t.stride(0) != T * t.stride(1):
+        if not _even_batches(t):
             raise ValueError(f"{name}: batches must be evenly strided")
     dev = x.device
     if out is None:
@@ -530,7 +549,8 @@ def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tens
                 raise ValueError(f"output tensors must be contiguous {shp} {dt}")
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     cu_out = None if cu_seqlens is None else torch.empty_like(cu_seqlens)
-    rc = _lib.gdn_gdp_prefill_prepare(_dev(x, "x"), x.stride(1), _dev(ba, "ba"), ba.stride(1),
+    rc = _lib.gdn_gdp_prefill_prepare(_dev(x, "x"), _tstride(x, row), _dev(ba, "ba"),
+                                      _tstride(ba, ba.shape[2]),
                                       _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
                                       _opt(cu_seqlens, "cu_seqlens"), n_seqs, _opt(cu_out, "cu_out"),
                                       _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),

@@ -411,3 +411,22 @@ def test_gdp_prefill_prepare_validation(lib):
     assert gprep(lib, x=P + 4) == EUNSUP
     assert gprep(lib, T=0, x=None, ba=None, q=None, k=None, v=None, g=None, beta=None) == OK
     assert gprep(lib, B=1, cu=0xA0000, n_seqs=2, cu_out=0xB0000, T=0) == OK
+
+
+def test_token_strides_of_length_one_dims(lib):
+    """A length-1 dimension may carry any stride (a view of [B, 1, ...] can
+    report a token stride shorter than a row): the binding takes the token
+    stride from the batch stride when each batch row has one token."""
+    import torch
+
+    import linear_attention_ssm_amd as gdn
+    y = torch.zeros(3, 1, 6144, dtype=torch.bfloat16)
+    q = y[:, :, :64].view(3, 1, 1, 64)             # strides (6144, 64, 64, 1)
+    assert gdn._even_batches(q)
+    assert gdn._tstride(q, 64) == 6144             # = batch stride
+    x = torch.zeros(2, 5, 8)
+    assert gdn._tstride(x, 8) == 8 and gdn._even_batches(x)
+    lone = torch.zeros(1, 1, 1, 64).as_strided((1, 1, 1, 64), (64, 1, 64, 1))
+    assert gdn._tstride(lone, 64) == 64            # at least a row
+    uneven = torch.zeros(2, 10, 8)[:, :5]          # batch stride 80, token stride 8, T = 5
+    assert not gdn._even_batches(uneven)
