@@ -1492,7 +1492,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // The chain waves hand h (at the end of a step) and U (mid-step) to the output
 // wave through LDS. A chain wave reads a chunk's operands one step ahead,
 // right after the mid-step barrier by which the copy wave has seen it land;
-// the output wave reads its own at the start of the step.
+// the output wave reads its Q rows, P fragments and factors for the next
+// chunk at the end of the step, likewise after that barrier.
 // In the whole-prefill form the values are staged raw and one conv wave per
 // column tile convolves its slab of each chunk in place during the step
 // before the chains read them, half before and half after the mid-step
@@ -1698,9 +1699,11 @@ __device__ __forceinline__ void role_chain(const ScanBuf<bf16, KD, NT>* __restri
 }
 
 // One chunk of the output wave: O^T tiles (lane: chunk row 16 rt + c, value
-// columns 16 t + 4 g .. + 3) stored straight to global memory.
+// columns 16 t + 4 g .. + 3) stored straight to global memory. `op` holds the
+// chunk's operands (read a step ahead) and turns over to the next chunk's,
+// read from `ahead`.
 template <int KD, int NT>
-__device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restrict__ cur,
+__device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restrict__ ahead,
                                             const RoleHand<KD, NT>* __restrict__ hand,
                                             const ScanLane<bf16, KD, NT>& ln, int grp, int col,
                                             OutOps<KD>& op, rsrc_t ro, uint32_t o_row)
@@ -1715,7 +1718,6 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int t = 0; t < NT; ++t) hf[t][kb] = hand->h[kb][t][lane];
-    out_load<KD, NT>(op, cur, ln, col, lane);
     // ---- h^T Q^T, scaled by b per chunk row
     f32x4 O[NT][4];
 #pragma unroll
@@ -1773,6 +1775,7 @@ __device__ __forceinline__ void role_output(const ScanBuf<bf16, KD, NT>* __restr
             }
         }
     }
+    out_load<KD, NT>(op, ahead, ln, col, lane);   // the next chunk's (landed by the mid-step barrier)
 }
 
 // CONV (whole-prefill form): vp points at the raw value rows before the
@@ -1935,13 +1938,14 @@ void chunk_scan_roles_kernel(
         lds_barrier();
         if constexpr (CONV) lds_barrier();
         OutOps<KD> op;
+        out_load<KD, NT>(op, &bufs[0], ln, col, lane);
         int b = 0;
         for (int c = 0; c < nchunks; ++c) {
             const int bn = b == NBUF - 1 ? 0 : b + 1;
             const int tok0 = a.tok_begin + c * kChunk;
             const int L = min(kChunk, a.tok_end - tok0);
             const rsrc_t ro = make_rsrc(o + (int64_t)tok0 * HV + (int64_t)h * V + a.c0, (uint32_t)L * o_row);
-            role_output<KD, NT>(&bufs[b], hand, ln, grp, col, op, ro, o_row);
+            role_output<KD, NT>(&bufs[bn], hand, ln, grp, col, op, ro, o_row);
             lds_barrier();
             b = bn;
         }
