@@ -2064,8 +2064,10 @@ void chunk_scan_roles_kernel(
         u32x2 cur = u32x2{0u, 0u}, nxt = u32x2{0u, 0u};
         const int from = (48 + col) * 4;   // byte index of lane (3, col)
         // a half's two row tiles are both read, then both convolved and
-        // written (their dependent arithmetic interleaves); the second half's
-        // row tiles lie above the first's
+        // written (their dependent arithmetic interleaves). Row tile i reads
+        // the last four raw rows of row tile i - 1, so the halves go from the
+        // last rows to the first: tiles 3 and 2 (which read rows 28 .. 63)
+        // before tiles 1 and 0 overwrite rows 0 .. 31
         auto convert = [&](int cc, int half) {
             if (cc >= nchunks) return;
             SB* __restrict__ buf = &bufs[cc % NBUF];
