@@ -113,6 +113,31 @@ def _opt(t, name):
     return None if t is None else _dev(t, name)
 
 
+def _need(t, name: str, shape, dtype: torch.dtype, contiguous: bool = True) -> None:
+    """Shape, dtype and layout of a tensor the caller supplies (checked before
+    any pointer reaches the library: the kernels assume exactly this layout)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_params(H: int, **params) -> None:
+    """Per-head fp32 gate parameters (A_log, dt_bias): contiguous [H]."""
+    for name, t in params.items():
+        _need(t, name, (H,), torch.float32)
+
+
+def _same_device(*tensors) -> None:
+    devs = {t.device for t in tensors if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
 def _code(dt: torch.dtype) -> int:
     if dt not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dt} (float32 or bfloat16)")
@@ -152,14 +177,19 @@ def gdn_conv1d_causal(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None =
     if x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("x must be [B, T, C] with a contiguous channel dim")
     B, T, C = x.shape
+    if w.dim() != 2 or w.shape[0] != C:
+        raise ValueError(f"w must be [C, W] with C = {C}")
+    _need(w, "w", (C, w.shape[1]), x.dtype)
+    if bias is not None:
+        _need(bias, "bias", (C,), x.dtype)
     if y is None:
         y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
-    if w.dim() != 2 or not w.is_contiguous() or w.dtype != x.dtype or y.dtype != x.dtype:
-        raise ValueError("w must be a contiguous [C, W] tensor of x's dtype; y of x's dtype")
-    if bias is not None and (bias.dtype != x.dtype or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous [C] tensor of x's dtype")
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
+    _need(y, "y", (B, T, C), x.dtype, contiguous=False)
+    if y.stride(2) != 1:
+        raise ValueError("y must have a contiguous channel dim")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+    _same_device(x, w, y, bias, cu_seqlens)
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     # (one token per row: its token stride is never used, and a length-1
     # dimension may carry any stride)
@@ -195,9 +225,8 @@ def gdn_gate_prepare(a: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor,
     for t, n in ((g, "g"), (beta, "beta")):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != R * H:
             raise ValueError(f"{n} must be a contiguous fp32 tensor with {R * H} elements")
-    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != H:
-            raise ValueError(f"{n} must be a contiguous fp32 [H] tensor")
+    _need_params(H, A_log=A_log, dt_bias=dt_bias)
+    _same_device(a, b, A_log, dt_bias, g, beta)
     rc = _lib.gdn_gate_prepare(_dev(a2, "a"), a2.stride(0), _dev(b2, "b"), b2.stride(0),
                                _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"), _dev(g, "g"),
                                _dev(beta, "beta"), R, H, _code(a.dtype), _stream(a.device))
@@ -219,6 +248,24 @@ def _token_rows(t: torch.Tensor, name: str, heads: int, d: int):
     if t.stride(3) != 1 or (heads > 1 and t.stride(2) != d) or not _even_batches(t):
         raise ValueError(f"{name}: heads and head dim must be contiguous and batches evenly strided")
     return _tstride(t, heads * d)
+
+
+def _chunk_outputs(like, B, T, N, H, K, V, initial_state, output_final_state, o, final_state):
+    """The initial state (if any), and the output and final state, allocated
+    when not given and checked when given: o contiguous [B, T, H, V] in the
+    activation dtype, states contiguous fp32 [N, H, K, V]."""
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, K, V), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=like.dtype, device=like.device)
+    _need(o, "o", (B, T, H, V), like.dtype)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=like.device)
+    if not output_final_state:
+        final_state = None
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, K, V), torch.float32)
+    return o, final_state
 
 
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -246,19 +293,12 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     N = n_seqs if cu_seqlens is not None else B
-    if initial_state is not None and (initial_state.dtype != torch.float32 or
-                                      not initial_state.is_contiguous() or
-                                      initial_state.shape != (N, H, K, V)):
-        raise ValueError(f"initial_state must be a contiguous fp32 [{N}, {H}, {K}, {V}] tensor")
-    if o is None:
-        o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-    if not output_final_state:
-        final_state = None
+    o, final_state = _chunk_outputs(q, B, T, N, H, K, V, initial_state, output_final_state,
+                                    o, final_state)
     ws_bytes = gdn_chunk_fwd_workspace_size(B, T, H, Hk, K, V, n_seqs, q.dtype)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _same_device(q, k, v, g, beta, initial_state, final_state, o, cu_seqlens, workspace)
     rc = _lib.gdn_chunk_fwd(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(v, "v"), st_v, _dev(g, "g"),
                             _dev(beta, "beta"), _opt(initial_state, "initial_state"),
                             _opt(final_state, "final_state"), _dev(o, "o"),
@@ -310,28 +350,19 @@ def _prefill_args(x, w, a, b, A_log, dt_bias, Hk, K, H, V, bias, cu_seqlens):
             raise ValueError(f"{n} must be [B, T, H] of x's dtype, head dim contiguous, "
                              "batch rows evenly strided")
     for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias")):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != H):
-            raise ValueError(f"{n} must be a contiguous fp32 [H] tensor")
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
+        if t is not None:
+            _need(t, n, (H,), torch.float32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _same_device(x, w, a, b, A_log, dt_bias, bias, cu_seqlens)
     return B, T, n_seqs
 
 
 def _prefill_outputs(x, B, T, n_seqs, cu_seqlens, H, K, V, initial_state, output_final_state,
                      o, final_state):
     N = n_seqs if cu_seqlens is not None else B
-    if initial_state is not None and (initial_state.dtype != torch.float32 or
-                                      not initial_state.is_contiguous() or
-                                      initial_state.shape != (N, H, K, V)):
-        raise ValueError(f"initial_state must be a contiguous fp32 [{N}, {H}, {K}, {V}] tensor")
-    if o is None:
-        o = torch.empty((B, T, H, V), dtype=x.dtype, device=x.device)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=x.device)
-    if not output_final_state:
-        final_state = None
-    return o, final_state
+    return _chunk_outputs(x, B, T, N, H, K, V, initial_state, output_final_state, o, final_state)
 
 
 def _prefill_ws(workspace, x, B, T, H, Hk, K, V, n_seqs):
@@ -405,9 +436,14 @@ def gdn_chunk_prepare(q, k, g, beta, workspace, cu_seqlens=None, scale=1.0, qk_l
     B, T, Hk, K = q.shape
     H = g.shape[2] if H is None else H
     st_qk = _token_rows(q, "q", Hk, K)
-    if _token_rows(k, "k", Hk, K) != st_qk:
-        raise ValueError("q and k must share strides")
+    if _token_rows(k, "k", Hk, K) != st_qk or k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape, strides and dtype")
+    _need(g, "g", (B, T, H), torch.float32)
+    _need(beta, "beta", (B, T, H), torch.float32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _same_device(q, k, g, beta, cu_seqlens, workspace)
     rc = _lib.gdn_chunk_prepare(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(g, "g"), _dev(beta, "beta"),
                                 _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K,
                                 float(scale), int(bool(qk_l2norm)), _code(q.dtype),
@@ -421,8 +457,17 @@ def gdn_chunk_scan(q, k, v, o, workspace, initial_state=None, final_state=None, 
     B, T, Hk, K = q.shape
     H, V = v.shape[2], v.shape[3]
     st_qk = _token_rows(q, "q", Hk, K)
+    if _token_rows(k, "k", Hk, K) != st_qk or k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape, strides and dtype")
     st_v = _token_rows(v, "v", H, V)
+    if v.shape[:2] != (B, T) or v.dtype != q.dtype:
+        raise ValueError("v must agree with q in batch, length and dtype")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = n_seqs if cu_seqlens is not None else B
+    _chunk_outputs(q, B, T, N, H, K, V, initial_state, final_state is not None, o, final_state)
+    _same_device(q, k, v, o, initial_state, final_state, cu_seqlens, workspace)
     rc = _lib.gdn_chunk_scan(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(v, "v"), st_v,
                              _opt(initial_state, "initial_state"), _opt(final_state, "final_state"),
                              _dev(o, "o"), _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
@@ -433,6 +478,21 @@ def gdn_chunk_scan(q, k, v, o, workspace, initial_state=None, final_state=None, 
 
 
 # -------------------------------------------------------------------- decode
+
+def _decode_rows(x, ba, M, H, G, P, N) -> None:
+    """x [n, >= M*H*P + M*G*N + G*N] and ba [n, >= M*H + H] rows of one dtype,
+    the last dim contiguous (rows may be strided)."""
+    n = x.shape[0]
+    if x.dim() != 2 or ba.dim() != 2 or ba.shape[0] != n:
+        raise ValueError("x and ba must be [n, row]")
+    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.dtype != x.dtype:
+        raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
+    if x.shape[1] < M * H * P + M * G * N + G * N:
+        raise ValueError(f"x rows must hold M*H*P + M*G*N + G*N = {M * H * P + M * G * N + G * N} "
+                         f"elements, got {x.shape[1]}")
+    if ba.shape[1] < M * H + H:
+        raise ValueError(f"ba rows must hold M*H + H = {M * H + H} elements, got {ba.shape[1]}")
+
 
 def gdn_recurrent_decode(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
                          dt_bias: torch.Tensor, state: torch.Tensor, M: int, H: int, G: int,
@@ -446,12 +506,13 @@ def gdn_recurrent_decode(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
     if ba.dim() == 3:
         ba = ba.reshape(ba.shape[0], ba.shape[-1])
     n = x.shape[0]
-    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[0] != n or ba.dtype != x.dtype:
-        raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
-    if state.dtype != torch.float32 or not state.is_contiguous() or state.shape != (n, H, N, P):
-        raise ValueError(f"state must be a contiguous fp32 [{n}, {H}, {N}, {P}] tensor")
+    _decode_rows(x, ba, M, H, G, P, N)
+    _need(state, "state", (n, H, N, P), torch.float32)
+    _need_params(H, A_log=A_log, dt_bias=dt_bias)
     if o is None:
         o = torch.empty((n, H, P), dtype=x.dtype, device=x.device)
+    _need(o, "o", (n, H, P), x.dtype)
+    _same_device(x, ba, A_log, dt_bias, state, o)
     rc = _lib.gdn_recurrent_decode(_dev(x, "x"), x.stride(0), _dev(ba, "ba"), ba.stride(0),
                                    _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),
                                    _dev(state, "state"), _dev(o, "o"), n, M, H, G, P, N,
@@ -472,8 +533,8 @@ def gdn_decode_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
     if ba.dim() == 3:
         ba = ba.reshape(ba.shape[0], ba.shape[-1])
     n = x.shape[0]
-    if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[0] != n or ba.dtype != x.dtype:
-        raise ValueError("x and ba must be [n, row] with contiguous rows of one dtype")
+    _decode_rows(x, ba, M, H, G, P, N)
+    _need_params(H, A_log=A_log, dt_bias=dt_bias)
     dev = x.device
     if out is None:
         q = torch.empty((n, M, H, N), dtype=x.dtype, device=dev)
@@ -488,6 +549,7 @@ def gdn_decode_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tensor,
                            (g, (n, M, H), torch.float32)):
             if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
                 raise ValueError(f"output tensors must be contiguous {shp} {dt}")
+    _same_device(x, ba, A_log, dt_bias, q, k, v, beta, g)
     rc = _lib.gdn_decode_prepare(_dev(x, "x"), x.stride(0), _dev(ba, "ba"), ba.stride(0),
                                  _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"), _dev(q, "q"),
                                  _dev(k, "k"), _dev(v, "v"), _dev(beta, "beta"), _dev(g, "g"),
@@ -508,10 +570,15 @@ def gdn_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, slot: torch.Ten
         raise ValueError("conv_state must be a contiguous [S, W-1, C] tensor of x's dtype")
     if slot.dtype != torch.int32 or slot.numel() != n:
         raise ValueError("slot must be int32 [n]")
-    if w.shape != (C, Wm1 + 1) or not w.is_contiguous():
-        raise ValueError("w must be a contiguous [C, W] tensor")
+    _need(w, "w", (C, Wm1 + 1), x.dtype)
+    if bias is not None:
+        _need(bias, "bias", (C,), x.dtype)
     if y is None:
         y = torch.empty((n, C), dtype=x.dtype, device=x.device)
+    _need(y, "y", (n, C), x.dtype, contiguous=False)
+    if y.stride(-1) != 1:
+        raise ValueError("y must be [n, C] with contiguous rows")
+    _same_device(x, conv_state, slot, w, bias, y)
     rc = _lib.gdn_conv1d_update(_dev(x, "x"), x.stride(0), _dev(conv_state, "conv_state"),
                                 _dev(slot, "slot"), _dev(w, "w"), _opt(bias, "bias"), _dev(y, "y"),
                                 y.stride(0), n, S, C, Wm1 + 1, int(bool(silu)), _code(x.dtype),
@@ -530,6 +597,11 @@ def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tens
     B, T, row = x.shape
     if x.stride(-1) != 1 or ba.stride(-1) != 1 or ba.shape[:2] != (B, T) or ba.dtype != x.dtype:
         raise ValueError("x and ba must be [B, T, row] with contiguous rows of one dtype")
+    if row < M * H * P + M * G * N + G * N or ba.shape[2] < M * H + H:
+        raise ValueError("x rows must hold M*H*P + M*G*N + G*N elements and ba rows M*H + H")
+    _need_params(H, A_log=A_log, dt_bias=dt_bias)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
     for t, name in ((x, "x"), (ba, "ba")):
         if not _even_batches(t):
             raise ValueError(f"{name}: batches must be evenly strided")
@@ -549,6 +621,7 @@ def gdn_gdp_prefill_prepare(x: torch.Tensor, ba: torch.Tensor, A_log: torch.Tens
                 raise ValueError(f"output tensors must be contiguous {shp} {dt}")
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     cu_out = None if cu_seqlens is None else torch.empty_like(cu_seqlens)
+    _same_device(x, ba, A_log, dt_bias, cu_seqlens, q, k, v, g, beta)
     rc = _lib.gdn_gdp_prefill_prepare(_dev(x, "x"), _tstride(x, row), _dev(ba, "ba"),
                                       _tstride(ba, ba.shape[2]),
                                       _dev(A_log, "A_log"), _dev(dt_bias, "dt_bias"),

@@ -430,3 +430,98 @@ def test_token_strides_of_length_one_dims(lib):
     assert gdn._tstride(lone, 64) == 64            # at least a row
     uneven = torch.zeros(2, 10, 8)[:, :5]          # batch stride 80, token stride 8, T = 5
     assert not gdn._even_batches(uneven)
+
+
+def _raises(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_checks_every_supplied_tensor():
+    """Every tensor the caller supplies, outputs included, is checked for
+    shape, dtype and layout before any pointer reaches the library (a wrong
+    output shape would otherwise send the kernels out of bounds). CPU
+    tensors: the checks run before the device check."""
+    import torch
+
+    import linear_attention_ssm_amd as gdn
+    bf, f32 = torch.bfloat16, torch.float32
+    B, T, Hk, K, H, V = 2, 70, 2, 64, 4, 64
+    C = 2 * Hk * K + H * V
+    z = torch.zeros
+    # conv1d: y shape and layout, taps per channel, bias length
+    x = z(B, T, C, dtype=bf)
+    w = z(C, 4, dtype=bf)
+    _raises(lambda: gdn.gdn_conv1d_causal(x, w, y=z(B, T, C - 8, dtype=bf)), "y must have shape")
+    _raises(lambda: gdn.gdn_conv1d_causal(x, w, y=z(B, T, C, dtype=f32)), "y must be")
+    _raises(lambda: gdn.gdn_conv1d_causal(x, w, y=z(B, C, T, dtype=bf).transpose(1, 2)),
+            "contiguous channel")
+    _raises(lambda: gdn.gdn_conv1d_causal(x, z(C - 8, 4, dtype=bf), y=z(B, T, C, dtype=bf)), "w must be")
+    _raises(lambda: gdn.gdn_conv1d_causal(x, w, y=z(B, T, C, dtype=bf), bias=z(C + 8, dtype=bf)),
+            "bias must have shape")
+    # gates: per-head parameters
+    a = z(B, T, H, dtype=bf)
+    _raises(lambda: gdn.gdn_gate_prepare(a, a, z(H + 1), z(H)), "A_log must have shape")
+    _raises(lambda: gdn.gdn_gate_prepare(a, a, z(H), z(H, dtype=torch.float64)), "dt_bias must be")
+    # chunked forward: o and the states
+    q = z(B, T, Hk, K, dtype=bf)
+    v = z(B, T, H, V, dtype=bf)
+    g = z(B, T, H)
+    ok_o = z(B, T, H, V, dtype=bf)
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=z(B, T, H, V + 64, dtype=bf)), "o must have shape")
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=z(B, T, H, V, dtype=f32)), "o must be")
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=z(B, T, V, H, dtype=bf).transpose(2, 3)),
+            "o must be contiguous")
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=ok_o, final_state=z(B, H, V, V + 64)),
+            "final_state must have shape")
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=ok_o, final_state=z(B, H, K, V, dtype=bf)),
+            "final_state must be")
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=ok_o, initial_state=z(B + 1, H, K, V)),
+            "initial_state must have shape")
+    # the phases: the scan's o and k; the prepare's gates
+    _raises(lambda: gdn.gdn_chunk_scan(q, q, v, z(B, T, H, V - 8, dtype=bf), z(16, dtype=torch.uint8)),
+            "o must have shape")
+    _raises(lambda: gdn.gdn_chunk_scan(q, z(B, T, Hk, K + 64, dtype=bf), v, ok_o, z(16, dtype=torch.uint8)),
+            "k must be")
+    _raises(lambda: gdn.gdn_chunk_scan(q, z(B, T, Hk, K), v, ok_o, z(16, dtype=torch.uint8)),
+            "q and k")
+    _raises(lambda: gdn.gdn_chunk_prepare(q, q, g, z(B, T, H + 1), z(16, dtype=torch.uint8)),
+            "beta must have shape")
+    # whole prefill: o and the final state
+    xp = z(B, T, C, dtype=bf)
+    AL = z(H)
+    _raises(lambda: gdn.gdn_prefill(xp, w, a, a, AL, AL, Hk=Hk, K=K, H=H, V=V,
+                                    o=z(B, T, H, V, dtype=f32)), "o must be")
+    _raises(lambda: gdn.gdn_prefill(xp, w, a, a, AL, AL, Hk=Hk, K=K, H=H, V=V, o=ok_o,
+                                    final_state=z(B, H, K, 2 * V)), "final_state must have shape")
+    _raises(lambda: gdn.gdn_prefill(xp, w, a, a, z(H + 2), AL, Hk=Hk, K=K, H=H, V=V), "A_log must have shape")
+    # decode: o, the state, the parameters and the row lengths
+    M, G, P, N, n = 2, 2, 64, 64, 3
+    row = M * H * P + M * G * N + G * N
+    xd = z(n, row, dtype=bf)
+    ba = z(n, M * H + H, dtype=bf)
+    st = z(n, H, N, P)
+    _raises(lambda: gdn.gdn_recurrent_decode(xd, ba, AL, AL, st, M, H, G, P, N, o=z(n, H, P + 8, dtype=bf)),
+            "o must have shape")
+    _raises(lambda: gdn.gdn_recurrent_decode(xd, ba, z(H - 1), AL, st, M, H, G, P, N), "A_log must have shape")
+    _raises(lambda: gdn.gdn_recurrent_decode(xd, ba, AL, AL, z(n, H, P, N + 64), M, H, G, P, N),
+            "state must have shape")
+    _raises(lambda: gdn.gdn_recurrent_decode(xd[:, :row - 8], ba, AL, AL, st, M, H, G, P, N), "x rows")
+    _raises(lambda: gdn.gdn_recurrent_decode(xd, ba[:, :-1], AL, AL, st, M, H, G, P, N), "ba rows")
+    _raises(lambda: gdn.gdn_decode_prepare(xd, ba, AL, z(H + 1), M, H, G, P, N), "dt_bias must have shape")
+    # decode conv update: y, taps, bias
+    Cu = 128
+    cst = z(4, 3, Cu, dtype=bf)
+    slot = z(n, dtype=torch.int32)
+    xu = z(n, Cu, dtype=bf)
+    wu = z(Cu, 4, dtype=bf)
+    _raises(lambda: gdn.gdn_conv1d_update(xu, cst, slot, wu, y=z(n, Cu - 8, dtype=bf)), "y must have shape")
+    _raises(lambda: gdn.gdn_conv1d_update(xu, cst, slot, z(Cu, 4)), "w must be")
+    _raises(lambda: gdn.gdn_conv1d_update(xu, cst, slot, wu, bias=z(Cu - 8, dtype=bf)), "bias must have shape")
+    # GDP interleave: row lengths, parameters
+    xg = z(1, 5, row, dtype=bf)
+    bg = z(1, 5, M * H + H, dtype=bf)
+    _raises(lambda: gdn.gdn_gdp_prefill_prepare(xg[:, :, :row - 8], bg, AL, AL, M, H, G, P, N), "x rows")
+    _raises(lambda: gdn.gdn_gdp_prefill_prepare(xg, bg, z(H, dtype=bf), AL, M, H, G, P, N), "A_log must be")
+    # correct shapes on the CPU: the device check still refuses them
+    _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=ok_o), "GPU")

@@ -535,3 +535,13 @@ def test_gdp_prefill_packed_sequences_reset_state():
         o1, sf1 = oracle.gdp_prefill(x[:, a:b], ba[:, a:b], A_log, dt_bias, M, H, G, P, N)
         np.testing.assert_allclose(o[:, a:b], o1, rtol=1e-13, atol=1e-15)
         np.testing.assert_allclose(sf[s], sf1[0], rtol=1e-13, atol=1e-15)
+
+
+def test_softplus_golden_file_is_reproducible():
+    # the fixture is written by a committed script (120-digit decimal
+    # arithmetic, no floating-point library); re-running it gives the same bytes
+    import subprocess
+    import sys
+    script = os.path.join(GOLDEN, "make_softplus_threshold.py")
+    r = subprocess.run([sys.executable, script, "--check"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
