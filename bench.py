@@ -8,21 +8,31 @@ run as the library's whole-prefill entry in its two phases: the per-chunk
 solve (convolving the q and k rows and forming the gates itself) and the scan
 (convolving the value rows as it reads them). Inputs are resident in HBM
 before timing starts. `value` is tokens/s of the whole step (16,384 tokens
-per step). The same computation is also timed as the four per-step calls
-(conv1d, gates, chunk_prepare, chunk_scan; `chain`), whose chunk_prepare +
-chunk_scan is the chunked forward on resident q, k, v, g, beta
-(`chain.chunk_fwd`: tokens/s and fractions of the MFMA and HBM peaks). The one-token Gated
-DeltaProduct decode (n=256 requests, M=2, H=32, G=16, P=N=128, 1000 steps,
-fp32 state updated in place) and the steps around it are reported beside it.
+per step) over K back-to-back steps; `value_flushed` is the same step timed
+per iteration with the caches flushed between iterations (a 512 MB write
+outside the timed region), the median of K.
+
+The other workloads are measured beside it, each in its own block of
+`configs`: the tiny fp32 workload (c1), the prefill workload's four per-step
+calls and the chunked forward alone on resident q, k, v, g, beta (c2), the
+GQA long prefill (c3, one sequence of 65,536 tokens, 32 value heads over 16
+q/k heads, initial state), the packed varlen prefill (c4, 64 sequences of
+1..2048 tokens) and the Gated DeltaProduct decode (c5, n=256, M=2, H=32,
+G=16, P=N=128, 1000 steps, fp32 state in place). c3 and c4 draw their inputs
+on the GPU with a seeded generator; every other input is the seeded CPU draw
+of workloads.py.
 
 Per-kernel durations come from HIP events recorded between the launches on
 the stream the kernels run on (torch's current stream, which the binding
-passes to the library). `roofline` describes the kernel that takes the most
-time per step; `traffic` comes from committed rocprofv3 counter summaries
-(profiles/traffic.json) and is null when absent or when the kernel's source
-has changed since they were taken.
+passes to the library). Each kernel is charged with its share of the
+method's single-pass bytes (each tensor of the step's inputs and outputs that
+the kernel reads or writes, counted once); workspace traffic (records,
+convolved rows) is not in that share and shows up in `traffic` (rocprofv3
+FETCH_SIZE + WRITE_SIZE per launch, from profiles/traffic.json, null when
+absent or when the kernel's source has changed since) and in
+`traffic_ratio` = traffic / share.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-chain]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1,c2,c3,c4,c5] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -38,14 +48,40 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix / vector, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "linear_attention_ssm_amd/csrc/"
-KERNELS = {   # bench op -> (kernel symbol stem, source file)
-    "prefill_prepare": ("chunk_prep_kernelIDF16bLi128ELb1ELb1E", CSRC + "chunk.hip"),
-    "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", CSRC + "chunk.hip"),
-    "decode": ("gdp_decode_kernel", CSRC + "decode.hip"),
+PARTS = ["c2", "c1", "c3", "c4", "c5"]
+PART_WORKLOAD = {"c1": "tiny", "c2": "prefill", "c3": "gqa", "c4": "varlen", "c5": "decode"}
+
+# bench op -> (kernel name as _kernel_stem() prints it, source file), per part;
+# a launch shape that differs between parts selects a different instance
+_PREP = "chunk_prep_kernel<bf16, 128, true, true>"
+_CPREP = "chunk_prep_kernel<bf16, 128, false, false>"
+_CHUNK = CSRC + "chunk.hip"
+KERNELS = {
+    "c1": {"conv1d": ("conv1d_causal_kernel<float, 16, 256>", CSRC + "conv1d.hip"),
+           "gate_prepare": ("gate_prepare_kernel<float>", CSRC + "gate.hip"),
+           "chunk_prepare": ("chunk_prep_kernel<float, 64, false, false>", _CHUNK),
+           "chunk_scan": ("chunk_scan_kernel<float, 64, 1, 3>", _CHUNK)},
+    "c2": {"prefill_prepare": (_PREP, _CHUNK),
+           "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
+           "conv1d": ("conv1d_causal_kernel<bf16, 16, 256>", CSRC + "conv1d.hip"),
+           "gate_prepare": ("gate_prepare_kernel<bf16>", CSRC + "gate.hip"),
+           "chunk_prepare": (_CPREP, _CHUNK),
+           "chunk_scan": ("chunk_scan_roles_kernel<128, 2, 3, false>", _CHUNK)},
+    "c3": {"prefill_prepare": (_PREP, _CHUNK),
+           "prefill_scan": ("chunk_scan_roles_kernel<128, 1, 3, true>", _CHUNK),
+           "chunk_prepare": (_CPREP, _CHUNK),
+           "chunk_scan": ("chunk_scan_roles_kernel<128, 1, 3, false>", _CHUNK)},
+    "c4": {"prefill_prepare": (_PREP, _CHUNK),
+           "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
+           "chunk_prepare": (_CPREP, _CHUNK),
+           "chunk_scan": ("chunk_scan_roles_kernel<128, 2, 3, false>", _CHUNK)},
+    "c5": {"decode": ("gdp_decode_kernel<bf16, 128, 128>", CSRC + "decode.hip"),
+           "conv1d_update": ("conv1d_update_kernel<bf16>", CSRC + "gdp.hip"),
+           "decode_prepare": ("gdp_decode_prepare_kernel<bf16>", CSRC + "gdp.hip")},
 }
-REC_BYTES_BF16 = 2 * 6 * 64 * 16 + 4 * 64 * 4   # per (chunk, value head) workspace record
 
 
 def parse():
@@ -56,27 +92,26 @@ def parse():
     # clock: 10 warm-up steps time 10% slow, 200 (about 35 ms) do not)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--decode-steps", type=int, default=1000)
-    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--only", default=",".join(PARTS),
+                   help="comma-separated parts to run (c1 tiny fp32, c2 prefill, c3 GQA long "
+                        "prefill, c4 varlen, c5 decode); the headline needs c2")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-batch", type=int, default=4,
                    help="sequences of the prefill workload the oracle baseline runs (4 = all)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration runs)")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--no-flush", action="store_true",
                    help="skip the per-iteration timings with the caches flushed between "
                         "iterations (profiling runs: every traced launch then runs warm, as in "
                         "the timed steps)")
-    p.add_argument("--no-chain", action="store_true",
-                   help="skip the four-call chain (conv1d, gates, chunk_prepare, chunk_scan)")
-    p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
-                   help="turn a rocprofv3 --stats kernel_stats.csv into a profiles/ summary")
+    p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_TRACE_CSV", "OUT_MD"),
+                   help="turn a rocprofv3 --kernel-trace csv into a profiles/ summary")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                   help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (made with "
-                        "--copy-probe) into profiles/traffic.json")
-    p.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
-                   help="write the MFMA-busy summary of a --pmc SQ_VALU_MFMA_BUSY_CYCLES "
-                        "SQ_INSTS_MFMA GRBM_GUI_ACTIVE run")
+                   help="merge rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of one part (made "
+                        "with --copy-probe) into profiles/traffic.json")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
+                   help="per-kernel table of a --pmc run's counters")
+    p.add_argument("--part", default=None, help="with --summarize-*: the part the run covered")
     p.add_argument("--command", default="", help="the command that produced the CSVs")
     p.add_argument("--bench-log", default=None,
                    help="with --summarize-stats: the profiled run's output, whose bench line "
@@ -84,57 +119,41 @@ def parse():
     return p.parse_args()
 
 
-def prefill_accounting(B, T, H, Hk, K, V):
-    """Algorithmic HBM bytes (and MFMA flops) per launch of each prefill kernel:
-    every input read once, every output written once."""
+# ------------------------------------------------------------------ accounting
+
+def accounting(tok, n_chunks, N, H, Hk, K, V, es=2):
+    """Algorithmic HBM bytes of the method's tensors (each read or written
+    once) and MFMA flops, for a prefill of `tok` tokens in `n_chunks` chunks
+    per head and N sequences; es = bytes per activation element."""
     C = 2 * Hk * K + H * V
-    tok = B * T
-    chunks = B * ((T + 63) // 64)
-    qk = 2 * tok * Hk * K * 2
-    v = tok * H * V * 2
-    o = tok * H * V * 2
-    gb = 2 * tok * H * 4
-    state = B * H * K * V * 4
-    rec = chunks * H * REC_BYTES_BF16
+    xqk = tok * 2 * Hk * K * es          # q|k channels (before or after the conv)
+    xv = tok * H * V * es                # value channels
+    o = tok * H * V * es
+    ab = 2 * tok * H * es                # gate inputs a, b
+    gb = 2 * tok * H * 4                 # g, beta (fp32)
+    state = N * H * K * V * 4
+    taps = C * 4 * es
     d, Cc = K, 64
-    ab = 2 * tok * H * 2
+    flops = tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3)
+    flops_dense = tok * H * (6 * d * d + 10 * Cc * d + (2 * Cc * Cc) / 3)
     return {
-        # the two launches of the whole prefill: per-chunk solve (x's q|k channels
-        # and a, b in; convolved q|k rows and records out), scan (q|k rows, x's
-        # value channels, records in; o and the final state out)
-        "prefill_prepare": {"bytes": 2 * qk + 2 * Hk * K * 4 * 2 + ab + rec,
-                            "flops": chunks * (Hk * 2 * 10 * 16 * 16 * K * 2 + H * 64 ** 3 / 3)},
-        "prefill_scan": {"bytes": qk + v + rec + o + state,
-                         "flops": chunks * H * (3 * 64 * K * V * 2 + 2 * 0.5 * 64 * 64 * V * 2)},
-        # the whole step, single-pass: x, a, b in; o and the final state out
-        "prefill": {"bytes": tok * C * 2 + ab + o + state},
-        "conv1d": {"bytes": 2 * tok * C * 2 + C * 4 * 2},
-        "gate_prepare": {"bytes": 2 * tok * H * 2 + gb},
-        "chunk_prepare": {"bytes": qk + gb + rec,
-                          # lower-triangular K K^T and Q K^T tiles plus the 64x64 solve
-                          "flops": chunks * (Hk * 2 * 10 * 16 * 16 * K * 2 + H * 64 ** 3 / 3)},
-        "chunk_scan": {"bytes": qk + v + rec + o + state,
-                       # K h, Q h, K^T U (dense) + T V', P U (lower-triangular), per chunk and head
-                       "flops": chunks * H * (3 * 64 * K * V * 2 + 2 * 0.5 * 64 * 64 * V * 2)},
-        # the whole chunked forward, single-pass: q, k, v, g, beta in; o, final state out;
-        # flops per token and head 6 d^2 + 5 C d + 2/3 C^2 (triangular count)
-        "chunk_fwd": {"bytes": qk + v + gb + o + state,
-                      "flops": tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3),
-                      # dense count: the intra-chunk products as full C x C blocks
-                      "flops_dense": tok * H * (6 * d * d + 10 * Cc * d + (2 * Cc * Cc) / 3)},
+        # whole prefill (x, a, b in; o and the final state out), split between
+        # its two launches by the tensors each touches
+        "prefill": {"bytes": xqk + xv + ab + o + state + taps},
+        "prefill_prepare": {"bytes": xqk + ab + 2 * Hk * K * 4 * es},
+        "prefill_scan": {"bytes": xv + o + state + H * V * 4 * es},
+        # per-step calls
+        "conv1d": {"bytes": 2 * tok * C * es + taps},
+        "gate_prepare": {"bytes": ab + gb},
+        "chunk_prepare": {"bytes": xqk + gb},
+        "chunk_scan": {"bytes": xqk + xv + o + state},
+        # the chunked forward alone (q, k, v, g, beta in; o, final state out);
+        # flops per token and head 6 d^2 + 5 C d + 2/3 C^2 (intra-chunk products
+        # as lower triangles), dense count beside it
+        "chunk_fwd": {"bytes": xqk + xv + gb + o + state, "flops": flops,
+                      "flops_dense": flops_dense},
+        "n_chunks": n_chunks,
     }
-
-
-def chunk_fwd_report(acc, tokens, ms):
-    """tokens/s of the chunked forward and its fractions of the bf16 MFMA peak
-    (triangular flop count) and of HBM (single-pass bytes)."""
-    s = ms / 1e3
-    return {"tokens_per_s": tokens / s, "us": s * 1e6,
-            "mfma_frac": acc["chunk_fwd"]["flops"] / s / (BF16_PEAK_TFLOPS * 1e12),
-            "mfma_frac_dense": acc["chunk_fwd"]["flops_dense"] / s / (BF16_PEAK_TFLOPS * 1e12),
-            "hbm_frac": acc["chunk_fwd"]["bytes"] / s / (HBM_PEAK_GBS * 1e9),
-            "algorithmic_flops": acc["chunk_fwd"]["flops"],
-            "algorithmic_bytes": acc["chunk_fwd"]["bytes"]}
 
 
 def decode_accounting(n, M, H, G, P, N):
@@ -148,71 +167,45 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(op):
+def load_traffic(part, op):
     """HBM bytes per launch (FETCH + WRITE, scaled by the copy-kernel factor)
-    from profiles/traffic.json, or None when absent or stale."""
+    of op's kernel in `part`, from profiles/traffic.json; None when absent or
+    stale (the kernel's source has changed since the counters were taken)."""
     path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or op not in KERNELS.get(part, {}):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get("kernels", {}).get(KERNELS[op][0])
-    if not ent or ent.get("source_sha") != source_hash(KERNELS[op][1]):
+    stem, src = KERNELS[part][op]
+    ent = data.get("parts", {}).get(part, {}).get(stem)
+    if not ent or ent.get("source_sha") != source_hash(src):
         return None
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(w, batch):
-    """The fp64 oracle chain (conv -> gates -> recurrence) on `batch` sequences
-    (all heads, full length) of the prefill workload; batch = 4 is one whole step."""
-    import numpy as np
-    import torch
-
-    import oracle
-    import workloads as wl
-    threads = len(os.sched_getaffinity(0))
-    oracle.set_threads(threads)
-    d = wl.prefill_inputs(w, B=batch)
-    tokens = batch * w.T
-    f64 = lambda t: t.to(torch.float32).numpy().astype(np.float64)
-    x, cw, a, b = f64(d["x"]), f64(d["w"]), f64(d["a"]), f64(d["b"])
-    A_log, dt_bias = f64(d["A_log"]), f64(d["dt_bias"])
-    t0 = time.perf_counter()
-    y = oracle.conv1d_causal(x, cw, silu=True)
-    nq = w.Hk * w.K
-    q = y[:, :, :nq].reshape(batch, w.T, w.Hk, w.K)
-    k = y[:, :, nq:2 * nq].reshape(batch, w.T, w.Hk, w.K)
-    v = y[:, :, 2 * nq:].reshape(batch, w.T, w.H, w.V)
-    g, beta = oracle.gate_prepare(a, b, A_log, dt_bias)
-    oracle.gated_delta_rule(q, k, v, g, beta)
-    dt = time.perf_counter() - t0
-    used = min(threads, batch * w.H)   # the recurrence runs (sequence, head) units in parallel
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{batch} x {w.T} tokens x {w.H} heads of the prefill workload (fp64 "
-                      f"conv1d + gates + timestep recurrence), {dt:.2f} s on {used} threads"}
+def kernel_report(part, op, us, share):
+    """One kernel's duration, its share of the single-pass bytes and the HBM
+    rate that share implies, beside the measured traffic."""
+    gbs = share / (us * 1e-6) / 1e9
+    tr = load_traffic(part, op)
+    return {"kernel": KERNELS.get(part, {}).get(op, (None,))[0], "us": us, "share_bytes": share,
+            "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "traffic": tr,
+            "traffic_ratio": None if tr is None else tr / share}
 
 
-def _timed_steps(args, torch, stream, step, n_ev):
-    """W untimed steps, then K timed steps with nothing else on the stream (the
-    wall time per step, ms, between two synchronisations), then K more with
-    n_ev HIP events each on `stream`, bracketing each kernel (its duration).
-    The two passes are separate because an event recorded between two
-    kernels leaves a gap of several microseconds between them."""
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    return evs, step_ms
+def chunk_fwd_report(acc, tokens, us, peak_tflops=BF16_PEAK_TFLOPS):
+    """tokens/s of the chunked forward and its fractions of the MFMA peak
+    (triangular flop count; dense beside it) and of HBM (single-pass bytes)."""
+    s = us * 1e-6
+    cf = acc["chunk_fwd"]
+    return {"tokens_per_s": tokens / s, "us": us,
+            "mfma_frac": cf["flops"] / s / (peak_tflops * 1e12),
+            "mfma_frac_dense": cf["flops_dense"] / s / (peak_tflops * 1e12),
+            "hbm_frac": cf["bytes"] / s / (HBM_PEAK_GBS * 1e9),
+            "algorithmic_flops": cf["flops"], "algorithmic_bytes": cf["bytes"]}
 
+
+# --------------------------------------------------------------------- timing
 
 class Flush:
     """Writes a 512 MB scratch buffer: evicts the 256 MB Infinity Cache (and the
@@ -245,6 +238,38 @@ def iter_stats(fn, torch, stream, iters, flush=None):
     return {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9), "iters": iters}
 
 
+def timed_ops(torch, stream, calls, steps, warmup):
+    """calls: list of (op, fn). `warmup` untimed passes, then `steps` timed
+    passes with nothing else on the stream (wall time per pass, us, between
+    two synchronisations), then `steps` more with HIP events between the
+    calls (each op's duration; an event between two kernels leaves a gap of a
+    few microseconds, so these passes are not the ones the pass time comes from)."""
+    def run(evs=None):
+        for j, (_, fn) in enumerate(calls):
+            if evs:
+                evs[j].record(stream)
+            fn()
+        if evs:
+            evs[-1].record(stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    pass_us = (time.perf_counter() - t0) * 1e6 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    op_us = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1e3
+             for j, (op, _) in enumerate(calls)}
+    return pass_us, op_us, run
+
+
 def copy_peak(torch, dev, stream):
     """GB/s of a plain 1 GiB device-to-device copy (read + write bytes)."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -255,91 +280,142 @@ def copy_peak(torch, dev, stream):
     return 2 * (1 << 30) / (st["median_us"] / 1e6) / 1e9
 
 
-def run_prefill(args, gdn, wl, torch, dev, stream):
-    """The whole prefill through its three phase entry points (each one kernel),
-    with events between them."""
-    w = wl.WORKLOADS["prefill"]
-    d = wl.prefill_inputs(w)
-    x, cw = d["x"].to(dev), d["w"].to(dev)
-    a, b = d["a"].to(dev), d["b"].to(dev)
-    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
-    o = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
-    fs = torch.empty((w.B, w.H, w.K, w.V), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.gdn_prefill_workspace_size(w.B, w.T, w.H, w.Hk, w.K, w.V, 0),
-                     dtype=torch.uint8, device=dev)
-    dims = dict(Hk=w.Hk, K=w.K, H=w.H, V=w.V)
-    ops = ["prefill_prepare", "prefill_scan"]
+# ------------------------------------------------------------------ workloads
 
-    def step(evs=None):
-        if evs:
-            evs[0].record(stream)
-        gdn.gdn_prefill_prepare(x, cw, a, b, A_log, dt_bias, ws, **dims)
-        if evs:
-            evs[1].record(stream)
-        gdn.gdn_prefill_scan(x, cw, ws, o=o, final_state=fs, **dims)
-        if evs:
-            evs[2].record(stream)
+def device_inputs(w, wl, torch, dev):
+    """The prefill inputs of workload w on the device. The prefill workload
+    and the tiny one use the seeded CPU draws of workloads.py; the GQA and
+    varlen workloads (1 GB and more) are drawn on the GPU with a seeded
+    generator, in the same distributions (varlen: the lengths are the CPU
+    draw, made first as in workloads.py)."""
+    if w.name in ("prefill", "tiny"):
+        d = wl.prefill_inputs(w)
+        t = {n: d[n].to(dev) for n in ("x", "w", "a", "b", "A_log", "dt_bias")}
+        t["S0"] = None if d["S0"] is None else d["S0"].to(dev)
+        t["cu"] = None if d["cu_seqlens"] is None else d["cu_seqlens"].to(dev)
+        return t, d["B"], d["T"], d["N"]
+    gen_cpu = torch.Generator().manual_seed(w.seed)
+    cu = None
+    B, T, N = w.B, w.T, w.B
+    if w.n_seqs:
+        lengths = wl.varlen_lengths(gen_cpu, w.n_seqs, w.max_len)
+        cu_h = wl.cu_from_lengths(lengths)
+        B, T, N = 1, int(lengths.sum()), int(lengths.numel())
+        cu = cu_h.to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    C = 2 * w.Hk * w.K + w.H * w.V
+    bf = w.dtype
+    t = {"x": torch.randn((B, T, C), generator=gen, device=dev, dtype=bf),
+         "w": (torch.randn((C, 4), generator=gen, device=dev) * 0.5).to(bf),
+         "a": torch.randn((B, T, w.H), generator=gen, device=dev, dtype=bf),
+         "b": torch.randn((B, T, w.H), generator=gen, device=dev, dtype=bf),
+         "A_log": torch.log(1 + 15 * torch.rand(w.H, generator=gen, device=dev)),
+         "dt_bias": torch.randn(w.H, generator=gen, device=dev) * 0.1}
+    t["S0"] = (torch.randn((N, w.H, w.K, w.V), generator=gen, device=dev) * w.s0_std
+               if w.s0_std > 0 else None)
+    t["cu"] = cu
+    return t, B, T, N
 
-    evs, step_ms = _timed_steps(args, torch, stream, step, 3)
-    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-             for j, op in enumerate(ops)}
-    # per-iteration statistics: back to back, and with the caches flushed
-    # between iterations (outside the timed region)
-    stats = {"back_to_back": iter_stats(step, torch, stream, args.steps)}
-    if not args.no_flush:
-        stats["flushed"] = iter_stats(step, torch, stream, args.steps, Flush(torch, dev))
-    return w, op_ms, step_ms, stats
 
+def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
+    """One prefill workload: the whole prefill (two launches, events between
+    them), per-iteration statistics back to back and flushed; the chunked
+    forward alone (prepare + scan) on resident q, k, v, g, beta; with
+    chain_ops, the four per-step calls timed one by one as well."""
+    w = wl.WORKLOADS[PART_WORKLOAD[part]]
+    t, B, T, N = device_inputs(w, wl, torch, dev)
+    Hk, K, H, V = w.Hk, w.K, w.H, w.V
+    dims = dict(Hk=Hk, K=K, H=H, V=V)
+    n_seqs = 0 if t["cu"] is None else N
+    cu = t["cu"]
+    if cu is None:
+        n_chunks = B * ((T + 63) // 64)
+    else:
+        lens = (cu[1:] - cu[:-1]).cpu()
+        n_chunks = int(((lens + 63) // 64).sum())
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    acc = accounting(B * T, n_chunks, N, H, Hk, K, V, es)
+    tokens = B * T
+    res = {"workload": _workload_name(w, B, T, N), "tokens": tokens}
+    o = torch.empty((B, T, H, V), dtype=w.dtype, device=dev)
+    fs = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else Flush(torch, dev)
+    kernels = {}
+    steps, warm = args.steps, args.warmup
 
-def run_chain(args, gdn, wl, torch, dev, stream):
-    """The same computation as four calls: conv1d over all of q|k|v, gates,
-    chunk_prepare, chunk_scan (the per-step entry points)."""
-    w = wl.WORKLOADS["prefill"]
-    d = wl.prefill_inputs(w)
-    x, cw = d["x"].to(dev), d["w"].to(dev)
-    a, b = d["a"].to(dev), d["b"].to(dev)
-    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
-    y = torch.empty_like(x)
-    g = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
+    if w.dtype == torch.bfloat16:
+        ws = torch.empty(max(1, gdn.gdn_prefill_workspace_size(B, T, H, Hk, K, V, n_seqs)),
+                         dtype=torch.uint8, device=dev)
+        calls = [("prefill_prepare",
+                  lambda: gdn.gdn_prefill_prepare(t["x"], t["w"], t["a"], t["b"], t["A_log"],
+                                                  t["dt_bias"], ws, cu_seqlens=cu, **dims)),
+                 ("prefill_scan",
+                  lambda: gdn.gdn_prefill_scan(t["x"], t["w"], ws, initial_state=t["S0"],
+                                               cu_seqlens=cu, o=o, final_state=fs, **dims))]
+        pass_us, op_us, run = timed_ops(torch, stream, calls, steps, warm)
+        st = {"back_to_back": iter_stats(run, torch, stream, steps)}
+        if flush:
+            st["flushed"] = iter_stats(run, torch, stream, steps, flush)
+        res["prefill"] = {"us": pass_us, "tokens_per_s": tokens / (pass_us * 1e-6),
+                          "hbm_frac": acc["prefill"]["bytes"] / (pass_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                          "algorithmic_bytes": acc["prefill"]["bytes"], "iters": st}
+        for kind, s in st.items():
+            s["tokens_per_s"] = tokens / (s["median_us"] * 1e-6)
+            s["hbm_frac"] = acc["prefill"]["bytes"] / (s["median_us"] * 1e-6) / (HBM_PEAK_GBS * 1e9)
+        res["prefill"]["chunk_fwd"] = chunk_fwd_report(acc, tokens, sum(op_us.values()))
+        for op, us in op_us.items():
+            kernels[op] = kernel_report(part, op, us, acc[op]["bytes"])
+        del ws
+
+    # the per-step path: conv1d + gates produce resident q, k, v, g, beta; the
+    # chunked forward alone (the headline metric's unit) is prepare + scan
+    y = torch.empty_like(t["x"])
+    g = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     beta = torch.empty_like(g)
-    o = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
-    fs = torch.empty((w.B, w.H, w.K, w.V), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(w.B, w.T, w.H, w.Hk, w.K, w.V, 0,
-                                                      torch.bfloat16), dtype=torch.uint8, device=dev)
-    q, k, v = gdn.split_qkv(y, w.Hk, w.K, w.H, w.V)
-    ops = ["conv1d", "gate_prepare", "chunk_prepare", "chunk_scan"]
+    q, k, v = gdn.split_qkv(y, Hk, K, H, V)
+    ws2 = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H, Hk, K, V, n_seqs, w.dtype),
+                      dtype=torch.uint8, device=dev)
+    conv = ("conv1d", lambda: gdn.gdn_conv1d_causal(t["x"], t["w"], y=y, cu_seqlens=cu, silu=True))
+    gate = ("gate_prepare", lambda: gdn.gdn_gate_prepare(t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                                         g=g, beta=beta))
+    prep = ("chunk_prepare", lambda: gdn.gdn_chunk_prepare(q, k, g, beta, ws2, cu_seqlens=cu))
+    scan = ("chunk_scan", lambda: gdn.gdn_chunk_scan(q, k, v, o, ws2, initial_state=t["S0"],
+                                                     final_state=fs, cu_seqlens=cu))
+    conv[1]()
+    gate[1]()
+    calls = [conv, gate, prep, scan] if chain_ops else [prep, scan]
+    pass_us, op_us, run = timed_ops(torch, stream, calls, steps, warm)
+    if chain_ops:
+        res["chain"] = {"us": pass_us, "tokens_per_s": tokens / (pass_us * 1e-6)}
 
-    def step(evs=None):
-        if evs:
-            evs[0].record(stream)
-        gdn.gdn_conv1d_causal(x, cw, y=y, silu=True)
-        if evs:
-            evs[1].record(stream)
-        gdn.gdn_gate_prepare(a, b, A_log, dt_bias, g=g, beta=beta)
-        if evs:
-            evs[2].record(stream)
-        gdn.gdn_chunk_prepare(q, k, g, beta, ws)
-        if evs:
-            evs[3].record(stream)
-        gdn.gdn_chunk_scan(q, k, v, o, ws, final_state=fs)
-        if evs:
-            evs[4].record(stream)
-
-    evs, step_ms = _timed_steps(args, torch, stream, step, 5)
-    op_us = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps * 1e3
-             for j, op in enumerate(ops)}
-    tokens = w.B * w.T
-
-    # the chunked forward alone on the resident q, k, v, g, beta (the
-    # headline metric's unit): per-iteration statistics, flushed and not
     def chunk():
-        gdn.gdn_chunk_prepare(q, k, g, beta, ws)
-        gdn.gdn_chunk_scan(q, k, v, o, ws, final_state=fs)
-    chunk_stats = {"back_to_back": iter_stats(chunk, torch, stream, args.steps)}
-    if not args.no_flush:
-        chunk_stats["flushed"] = iter_stats(chunk, torch, stream, args.steps, Flush(torch, dev))
-    return {"us": step_ms * 1e3, "tokens_per_s": tokens / (step_ms / 1e3), "ops_us": op_us,
-            "chunk_fwd_iters": chunk_stats}
+        prep[1]()
+        scan[1]()
+    res["chunk_fwd"] = chunk_fwd_report(acc, tokens, op_us["chunk_prepare"] + op_us["chunk_scan"],
+                                        BF16_PEAK_TFLOPS if es == 2 else FP32_PEAK_TFLOPS)
+    st = {"back_to_back": iter_stats(chunk, torch, stream, steps)}
+    if flush:
+        st["flushed"] = iter_stats(chunk, torch, stream, steps, flush)
+    for kind, s in st.items():
+        s.update({kk: vv for kk, vv in chunk_fwd_report(
+            acc, tokens, s["median_us"], BF16_PEAK_TFLOPS if es == 2 else FP32_PEAK_TFLOPS).items()
+            if kk in ("tokens_per_s", "mfma_frac", "hbm_frac")})
+    res["chunk_fwd"]["iters"] = st
+    for op, us in op_us.items():
+        kernels[op] = kernel_report(part, op, us, acc[op]["bytes"])
+    res["kernels"] = kernels
+    return res, acc
+
+
+def _workload_name(w, B, T, N):
+    dt = "bf16" if w.dtype.is_floating_point and w.dtype.itemsize == 2 else "fp32"
+    s = f"{w.name} {dt} B={B} T={T} H={w.H} Hk={w.Hk} K={w.K} V={w.V} chunk=64"
+    if w.n_seqs:
+        s += f" ({N} packed sequences, lengths 1..{w.max_len})"
+    if w.s0_std:
+        s += f", S0 ~N(0, {w.s0_std})"
+    return s + ", conv1d W=4 + SiLU over q|k|v, fp32 state"
 
 
 def run_decode(args, gdn, wl, torch, dev, stream):
@@ -371,18 +447,19 @@ def run_decode(args, gdn, wl, torch, dev, stream):
     ms = e0.elapsed_time(e1)
     per_s = ms / steps / 1e3
     nbytes = decode_accounting(wd.n, wd.M, wd.H, wd.G, wd.V, wd.K)
+    tr = load_traffic("c5", "decode")
     return {"req_per_s": wd.n * steps / (ms / 1e3), "us_per_step": per_s * 1e6,
-            "kernel": KERNELS["decode"][0],
+            "kernel": KERNELS["c5"]["decode"][0],
             "roofline": {"bound": "hbm", "achieved": nbytes / per_s / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": nbytes / per_s / 1e9 / HBM_PEAK_GBS,
-                         "traffic": load_traffic("decode")},
+                         "traffic": tr, "traffic_ratio": None if tr is None else tr / nbytes},
             "algorithmic_bytes_per_step": nbytes,
             "workload": f"decode bf16 n={wd.n} M={wd.M} H={wd.H} G={wd.G} P=N={wd.K}, "
                         f"fp32 state in place, {steps} steps"}
 
 
 def _time_launches(torch, stream, fn, reps):
-    """Average µs of fn() over reps launches, HIP events on the launch stream."""
+    """Average us of fn() over reps launches, HIP events on the launch stream."""
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
@@ -396,7 +473,7 @@ def _time_launches(torch, stream, fn, reps):
 
 
 def _time_graph(torch, fn, reps):
-    """Average µs per launch of fn() replayed from a captured HIP graph of reps
+    """Average us per launch of fn() replayed from a captured HIP graph of reps
     launches (no per-launch host overhead: what a decode loop captured in a
     graph sees)."""
     fn()
@@ -477,6 +554,38 @@ def run_gdp_steps(gdn, wl, torch, dev, stream):
     return out
 
 
+def cpu_baseline(w, batch):
+    """The fp64 oracle chain (conv -> gates -> recurrence) on `batch` sequences
+    (all heads, full length) of the prefill workload; batch = 4 is one whole step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    d = wl.prefill_inputs(w, B=batch)
+    tokens = batch * w.T
+    f64 = lambda t: t.to(torch.float32).numpy().astype(np.float64)
+    x, cw, a, b = f64(d["x"]), f64(d["w"]), f64(d["a"]), f64(d["b"])
+    A_log, dt_bias = f64(d["A_log"]), f64(d["dt_bias"])
+    t0 = time.perf_counter()
+    y = oracle.conv1d_causal(x, cw, silu=True)
+    nq = w.Hk * w.K
+    q = y[:, :, :nq].reshape(batch, w.T, w.Hk, w.K)
+    k = y[:, :, nq:2 * nq].reshape(batch, w.T, w.Hk, w.K)
+    v = y[:, :, 2 * nq:].reshape(batch, w.T, w.H, w.V)
+    g, beta = oracle.gate_prepare(a, b, A_log, dt_bias)
+    oracle.gated_delta_rule(q, k, v, g, beta)
+    dt = time.perf_counter() - t0
+    used = min(threads, batch * w.H)   # the recurrence runs (sequence, head) units in parallel
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{batch} x {w.T} tokens x {w.H} heads of the prefill workload (fp64 "
+                      f"conv1d + gates + timestep recurrence), {dt:.2f} s on {used} threads"}
+
+
+# ----------------------------------------------------------- profile summaries
+
 def _kernel_stem(name):
     """Readable name of a kernel symbol: our mangled template kernels become
     name<args> (bf16 template arguments are beyond the image's c++filt)."""
@@ -489,97 +598,74 @@ def _kernel_stem(name):
             parts.append("bf16" if s == "DF16b" else "float" if s == "f" else
                          tok.group(1) if tok.group(1) else ("true" if tok.group(2) == "1" else "false"))
         return f"{m.group(1)}<{', '.join(parts)}>"
-    m = re.match(r"_ZN3gdn\d+(\w+?)I", name)
-    if m:
-        return m.group(1)
     s = name.split("(")[0]
-    return (s[5:] if s.startswith("void ") else s)[:60]
+    s = s[5:] if s.startswith("void ") else s
+    s = s[5:] if s.startswith("gdn::") else s
+    return s.replace("__bf16", "bf16")[:80]
 
 
-def _phases(rows, id_key, name_key):
-    """The benchmark runs its parts in a fixed order: the prefill step, then the
-    decode step, then the Gated DeltaProduct steps. The decode kernel's
-    dispatches mark the boundaries, so a kernel used by two parts (the chunked
-    forward) is summarised per part instead of as a blended average."""
-    ids = [int(r[id_key]) for r in rows if KERNELS["decode"][0] in r[name_key]]
-    lo, hi = (min(ids), max(ids)) if ids else (None, None)
-
-    def phase(r):
-        d = int(r[id_key])
-        if lo is None or d < lo:
-            return "prefill"
-        return "decode" if d <= hi else "gdp steps"
-    return phase
-
-
-def summarize_stats(csv_path, out_md, command, bench_log=None):
-    """Kernel time table from rocprofv3's kernel trace (one row per dispatch),
-    one line per (benchmark part, kernel, grid, workgroup)."""
-    import collections
+def _read_csv(path):
     import csv
-    rows = list(csv.DictReader(open(csv_path)))
-    phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
+    return list(csv.DictReader(open(path)))
+
+
+def summarize_stats(csv_path, out_md, command, part, bench_log=None):
+    """Kernel time table from rocprofv3's kernel trace (one row per dispatch),
+    one line per (kernel, grid, workgroup)."""
+    import collections
+    rows = _read_csv(csv_path)
     groups = collections.OrderedDict()
     for r in rows:
-        key = (phase(r), r["Kernel_Name"],
+        key = (_kernel_stem(r["Kernel_Name"]),
                int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
                int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in groups.values())
-    order = {"prefill": 0, "decode": 1, "gdp steps": 2}
-    items = sorted(groups.items(), key=lambda kv: (order[kv[0][0]], -sum(kv[1])))
-    lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
+    items = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    w = PART_WORKLOAD.get(part, part)
+    lines = [f"# Kernel times, {w} workload ({part}) (rocprofv3 --kernel-trace --stats)", "",
              f"Command: `{command}`", "",
-             "One line per part of the benchmark (prefill step, decode step, Gated DeltaProduct",
-             "steps), kernel and launch shape (grid = work-items), from the kernel trace.", "",
-             "| part | kernel | grid | workgroup | calls | average (us) | min (us) | max (us) | share |",
-             "|---|---|---|---|---|---|---|---|---|"]
-    for (ph, name, grid, wg), d in items:
-        lines.append(f"| {ph} | `{_kernel_stem(name)}` | {grid} | {wg} | {len(d)} | "
-                     f"{sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
-                     f"{100 * sum(d) / total:.1f}% |")
+             "One line per kernel and launch shape (grid = work-items), from the kernel trace.", "",
+             "| kernel | grid | workgroup | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in items:
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f} | {100 * sum(d) / total:.1f}% |")
     if bench_log:
         js = [ln for ln in open(bench_log) if ln.startswith("{")]
         b = json.loads(js[-1])
-        lines += ["", "The same run's bench line (HIP events on the launch stream, averaged over",
-                  "the timed steps), for comparison with the trace averages above:", ""]
-        for op, us in b.get("ops_us", {}).items():
-            lines.append(f"- {op} (`{KERNELS[op][0]}`): {us:.2f} us")
-        if "decode" in b:
-            lines.append(f"- decode step (`{b['decode']['kernel']}`): {b['decode']['us_per_step']:.2f} us")
-    lines += ["", "Full symbols:", ""]
-    seen = set()
-    for (_, name, _, _), _ in items:
-        if name not in seen:
-            seen.add(name)
-            lines.append(f"- `{name[:200]}`")
+        cfg = b.get("configs", {}).get(part, {})
+        lines += ["", "The same run's bench figures (HIP events on the launch stream, averaged",
+                  "over the timed passes), for comparison with the trace averages above:", ""]
+        for op, k in cfg.get("kernels", {}).items():
+            lines.append(f"- {op} (`{k['kernel']}`): {k['us']:.2f} us")
+        if "decode" in cfg:
+            lines.append(f"- decode step (`{cfg['decode']['kernel']}`): {cfg['decode']['us_per_step']:.2f} us")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def summarize_traffic(fetch_csv, write_csv, command):
-    """Per-kernel HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each scaled by the factor that makes the plain 1 GiB device copy
-    (the runtime's buffer-copy kernel, --copy-probe) read and write 1 GiB."""
+def summarize_traffic(fetch_csv, write_csv, command, part):
+    """Per-kernel HBM bytes per launch in one part's run: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
+    plain 1 GiB device copy (the runtime's buffer-copy kernel, --copy-probe)
+    read and write 1 GiB. Merged into profiles/traffic.json under the part."""
     import collections
-    import csv
 
     def per_dispatch(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
+        rows = [r for r in _read_csv(path) if r["Counter_Name"] == counter]
         acc = collections.defaultdict(float)
-        names, phases = {}, {}
+        names = {}
         for r in rows:
             d = int(r["Dispatch_Id"])
             acc[d] += float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
             names[d] = r["Kernel_Name"]
-            phases[d] = phase(r)
-        return acc, names, phases
+        return acc, names
 
-    fetch, fnames, fphase = per_dispatch(fetch_csv, "FETCH_SIZE")
-    write, wnames, wphase = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch, fnames = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, wnames = per_dispatch(write_csv, "WRITE_SIZE")
     gib = float(1 << 30)
-    # the probe copies are the buffer-copy dispatches that move 1 GiB: the last three
-    # of that kernel in each run (earlier ones are uploads and the state reset)
+
+    # the probe copies are the last three buffer-copy dispatches of each run
     def probe(table, names):
         ids = sorted(d for d, n in names.items() if "copybuffer" in n.lower())[-3:]
         vals = [table[d] for d in ids]
@@ -587,73 +673,87 @@ def summarize_traffic(fetch_csv, write_csv, command):
     pf, pw = probe(fetch, fnames), probe(write, wnames)
     ff = gib / pf if pf else None
     fw = gib / pw if pw else None
-    res = {"command": command, "copy_kernel_bytes": gib, "copy_fetch_raw": pf, "copy_write_raw": pw,
-           "fetch_factor": ff, "write_factor": fw, "kernels": {}}
-    for op, (stem, src) in KERNELS.items():
-        ids = sorted(d for d in fetch if stem in fnames[d])
-        if not ids or ff is None or fw is None:
+    path = os.path.join(PROFILES, "traffic.json")
+    res = json.load(open(path)) if os.path.exists(path) else {}
+    res.setdefault("parts", {})
+    res["calibration"] = {"copy_kernel_bytes": gib, "copy_fetch_raw": pf, "copy_write_raw": pw,
+                          "fetch_factor": ff, "write_factor": fw}
+    ent = {}
+    srcs = {stem: src for stem, src in KERNELS.get(part, {}).values()}
+    by_name = collections.defaultdict(list)
+    for d, n in fnames.items():
+        by_name[_kernel_stem(n)].append(d)
+    wby = collections.defaultdict(list)
+    for d, n in wnames.items():
+        wby[_kernel_stem(n)].append(write[d])
+    for stem, ids in by_name.items():
+        if stem not in srcs or ff is None or fw is None:
             continue
-        # the part of the benchmark where the kernel first runs is its own
-        # workload; later launches (the Gated DeltaProduct steps) are kept apart
-        part = fphase[ids[0]]
-        fv = [fetch[d] for d in ids if fphase[d] == part]
-        wv = [v for d, v in write.items() if stem in wnames[d] and wphase[d] == part]
-        fb = sum(fv) / len(fv) * ff
-        wb = (sum(wv) / len(wv) * fw) if wv else 0.0
-        res["kernels"][stem] = {"part": part, "fetch_bytes": fb, "write_bytes": wb,
-                                "bytes_per_launch": fb + wb, "launches": len(fv),
-                                "source_sha": source_hash(src)}
+        fb = sum(fetch[d] for d in ids) / len(ids) * ff
+        wv = wby.get(stem, [])
+        wb = sum(wv) / len(wv) * fw if wv else 0.0
+        ent[stem] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                     "launches": len(ids), "source_sha": source_hash(srcs[stem])}
+    res["parts"][part] = {"command": command, "kernels": ent}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+    with open(path, "w") as f:
         json.dump(res, f, indent=1)
     return res
 
 
-def summarize_mfma(csv_path, out_md, command, cus=256, simds=4, xcds=8):
-    """Per kernel and bench part: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
-    (active cycles x CUs x SIMDs), the active cycles being GRBM_GUI_ACTIVE per
-    XCD (the counter is summed over the XCDs); and MFMA instructions per launch."""
+def summarize_counters(csv_path, out_md, command, part, cus=256, simds=4, xcds=8):
+    """Per kernel: every counter of a --pmc run, summed over the XCDs and
+    averaged over its launches; with GRBM_GUI_ACTIVE, per-CU busy fractions
+    of the SQ/TA/TD/TCP busy counters (counter / (active cycles per XCD x CUs),
+    and / SIMDs for the per-SIMD MFMA busy counter)."""
     import collections
-    import csv
-    rows = list(csv.DictReader(open(csv_path)))
-    phase = _phases(rows, "Dispatch_Id", "Kernel_Name")
+    rows = _read_csv(csv_path)
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     names = {}
     for r in rows:
         d = int(r["Dispatch_Id"])
         per[d][r["Counter_Name"]] += float(r["Counter_Value"])
-        names[d] = (phase(r), r["Kernel_Name"])
+        names[d] = _kernel_stem(r["Kernel_Name"])
     groups = collections.OrderedDict()
     for d in sorted(per):
         groups.setdefault(names[d], []).append(per[d])
-    lines = ["# MFMA busy (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
-             f"busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs x {simds} SIMDs),",
-             "averaged over the launches of each kernel in each part of the bench.", "",
-             "| part | kernel | launches | MFMA busy | MFMA instructions / launch |",
-             "|---|---|---|---|---|"]
-    for (ph, name), cs in groups.items():
-        act = sum(c.get("GRBM_GUI_ACTIVE", 0) for c in cs) / xcds
-        busy = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for c in cs)
-        insts = sum(c.get("SQ_INSTS_MFMA", 0) for c in cs) / len(cs)
-        if insts == 0:
-            continue
-        frac = busy / (act * cus * simds) if act else 0.0
-        lines.append(f"| {ph} | `{_kernel_stem(name)}` | {len(cs)} | {frac:.3f} | {insts:.4g} |")
+    counters = sorted({c for d in per.values() for c in d})
+    w = PART_WORKLOAD.get(part, part)
+    lines = [f"# Counters, {w} workload ({part}) (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             "Values per launch (summed over the XCDs, averaged over launches). Busy fractions:",
+             f"counter / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs), and x {simds} SIMDs more for",
+             "SQ_VALU_MFMA_BUSY_CYCLES.", "",
+             "| kernel | launches | " + " | ".join(counters) + " | busy fractions |",
+             "|---|---|" + "---|" * len(counters) + "---|"]
+    for name, cs in groups.items():
+        avg = {c: sum(x.get(c, 0.0) for x in cs) / len(cs) for c in counters}
+        act = avg.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        fr = []
+        for c in counters:
+            if not act or not c.endswith(("BUSY", "BUSY_CYCLES", "_BUSY_CU")) and "BUSY" not in c:
+                continue
+            den = act * cus * (simds if c == "SQ_VALU_MFMA_BUSY_CYCLES" else 1)
+            fr.append(f"{c} {avg[c] / den:.3f}")
+        lines.append(f"| `{name}` | {len(cs)} | " + " | ".join(f"{avg[c]:.4g}" for c in counters)
+                     + f" | {'; '.join(fr)} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+# ------------------------------------------------------------------------ main
+
 def main():
     args = parse()
-    if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma[0], args.summarize_mfma[1], args.command)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.command,
+                           args.part)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command,
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command, args.part,
                         args.bench_log)
         return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
-                                           args.command), indent=1))
+                                           args.command, args.part), indent=1))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the kernels are "
@@ -667,6 +767,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    parts = [p for p in args.only.split(",") if p]
+    for p in parts:
+        if p not in PARTS:
+            raise SystemExit(f"unknown part {p} (one of {PARTS})")
 
     w = wl.WORKLOADS["prefill"]
     out = {"metric": "GDN chunk-fwd tokens/s (H=16,d=128,T=4096); decode req/s; % of roofline",
@@ -676,63 +780,45 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"prefill bf16 B={w.B} H={w.H} Hk={w.Hk} T={w.T} K=V={w.K} "
                                   "chunk=64, conv1d W=4 + SiLU over C=6144, fp32 state",
-                      "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"}}
+                      "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
+           "configs": {}}
 
-    if args.only != "decode":
-        w, op_ms, step_ms, step_stats = run_prefill(args, gdn, wl, torch, dev, stream)
-        acc = prefill_accounting(w.B, w.T, w.H, w.Hk, w.K, w.V)
-        tokens = w.B * w.T
-        out["value"] = tokens / (step_ms / 1e3)
-        out["ms_per_step"] = step_ms
-        out["ops_us"] = {op: ms * 1e3 for op, ms in op_ms.items()}
-        dom = max(op_ms, key=op_ms.get)
-        sec = op_ms[dom] / 1e3
-        ach = acc[dom]["bytes"] / sec / 1e9
-        out["roofline"] = {"kernel": KERNELS[dom][0], "bound": "hbm", "achieved": ach,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": load_traffic(dom),
-                           "algorithmic_bytes": acc[dom]["bytes"]}
-        if "flops" in acc[dom]:
-            out["roofline"]["mfma_frac"] = acc[dom]["flops"] / sec / (BF16_PEAK_TFLOPS * 1e12)
-        step_s = step_ms / 1e3
-        out["step"] = {"algorithmic_bytes": acc["prefill"]["bytes"],
-                       "hbm_frac": acc["prefill"]["bytes"] / step_s / (HBM_PEAK_GBS * 1e9),
-                       "iters": step_stats}
-        # the chunked forward: the prepare and scan phases (which here also form
-        # the gates and convolve the value rows)
-        out["chunk_fwd"] = chunk_fwd_report(acc, tokens, op_ms["prefill_prepare"] + op_ms["prefill_scan"])
-        out["kernels"] = {op: {"us": op_ms[op] * 1e3,
-                               "achieved_GBs": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9,
-                               "hbm_frac": acc[op]["bytes"] / (op_ms[op] / 1e3) / 1e9 / HBM_PEAK_GBS}
-                          for op in op_ms}
-    if not args.no_chain and args.only != "decode":
-        out["chain"] = run_chain(args, gdn, wl, torch, dev, stream)
-        ch = out["chain"]["ops_us"]
-        out["chain"]["chunk_fwd"] = chunk_fwd_report(acc, tokens, (ch["chunk_prepare"] + ch["chunk_scan"]) / 1e3)
-        for kind, st in out["chain"].pop("chunk_fwd_iters").items():
-            out["chain"]["chunk_fwd"][kind] = dict(
-                st, tokens_per_s_median=tokens / (st["median_us"] / 1e6),
-                mfma_frac_median=acc["chunk_fwd"]["flops"] / (st["median_us"] / 1e6) / (BF16_PEAK_TFLOPS * 1e12))
-    if args.only != "prefill" and not args.no_decode:
-        out["decode"] = run_decode(args, gdn, wl, torch, dev, stream)
-        out["gdp_steps"] = run_gdp_steps(gdn, wl, torch, dev, stream)
-    # the copy-kernel peak, the practical HBM ceiling the fractions are also read
-    # against (read + write bytes of a plain device copy)
-    cp = copy_peak(torch, dev, stream)
-    out["copy_peak_GBs"] = cp
-    for kk in out.get("kernels", {}).values():
-        kk["copy_frac"] = kk["achieved_GBs"] / cp
-    if "roofline" in out:
-        out["roofline"]["copy_frac"] = out["roofline"]["achieved"] / cp
-    if "decode" in out:
-        out["decode"]["roofline"]["copy_frac"] = out["decode"]["roofline"]["achieved"] / cp
+    for p in parts:
+        if p == "c5":
+            out["configs"]["c5"] = {"decode": run_decode(args, gdn, wl, torch, dev, stream),
+                                    "gdp_steps": run_gdp_steps(gdn, wl, torch, dev, stream)}
+            continue
+        res, acc = run_prefill_part(p, args, gdn, wl, torch, dev, stream, chain_ops=p in ("c1", "c2"))
+        out["configs"][p] = res
+        if p == "c2":
+            pf = res["prefill"]
+            out["value"] = pf["tokens_per_s"]
+            out["ms_per_step"] = pf["us"] / 1e3
+            if "flushed" in pf["iters"]:
+                fl = pf["iters"]["flushed"]
+                out["value_flushed"] = {
+                    "value": fl["tokens_per_s"], "median_us": fl["median_us"],
+                    "hbm_frac": fl["hbm_frac"],
+                    "protocol": "the same step timed per iteration with HIP events, a 512 MB "
+                                "write between iterations (outside the timed region) evicting the "
+                                "256 MB Infinity Cache and the L2s; median of the timed iterations"}
+            ops = {op: k for op, k in res["kernels"].items() if op.startswith("prefill_")}
+            dom = max(ops, key=lambda op: ops[op]["us"])
+            k = ops[dom]
+            out["roofline"] = {"kernel": k["kernel"], "bound": "hbm", "achieved": k["achieved_GBs"],
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": k["hbm_frac"],
+                               "traffic": k["traffic"], "traffic_ratio": k["traffic_ratio"],
+                               "share_bytes": k["share_bytes"], "us": k["us"]}
+    # the copy-kernel rate, a practical HBM reference point (read + write bytes
+    # of a plain device copy)
+    out["copy_peak_GBs"] = copy_peak(torch, dev, stream)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    if not args.no_cpu and args.only != "decode":
+    if not args.no_cpu and "c2" in parts:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_batch)
     print(json.dumps(out), flush=True)
 

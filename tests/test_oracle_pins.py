@@ -545,3 +545,11 @@ def test_softplus_golden_file_is_reproducible():
     script = os.path.join(GOLDEN, "make_softplus_threshold.py")
     r = subprocess.run([sys.executable, script, "--check"], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_no_decay_gates_are_exact():
+    # A_log = -inf gives g = -exp(-inf) * softplus(.) = -0 exactly: the
+    # no-decay cases of the long-sequence parity tests rely on it
+    g, beta = oracle.gate_prepare(np.array([[0.3, -5.0, 25.0]]), np.zeros((1, 3)),
+                                  np.full(3, -np.inf), np.zeros(3))
+    assert np.all(g == 0.0) and np.all(np.isfinite(g))
