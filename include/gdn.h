@@ -175,6 +175,39 @@ int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * hipMalloc, harnesses without an allocator): the same arguments minus the
+ * workspace, the same kernels and results, bit for bit. The workspace is a
+ * fixed device array inside the library, GDN_NOALLOC_SCRATCH_BYTES bytes
+ * (64 MiB) on every GPU the library runs on, held until the process ends.
+ *   - A call whose workspace (gdn_chunk_fwd_workspace_size) exceeds that
+ *     size returns GDN_EWORKSPACE before any HIP call; the prefill workload
+ *     (B=4, T=4096, H=16) fits, with room to spare.
+ *   - The call itself allocates nothing: no hipMalloc, no hipFree, no
+ *     allocating library routine. The first call on a device looks up the
+ *     array's address there (hipGetSymbolAddress) and keeps it.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero: each call writes
+ *     everything it reads). Calls that overlap on one GPU -- on different
+ *     streams, or from several host threads without ordering -- race on it;
+ *     the caller must order them (one stream, or events).
+ * gdn_chunk_fwd_noalloc_capacity returns the array's size in bytes.
+ * ---------------------------------------------------------------------- */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+size_t gdn_chunk_fwd_noalloc_capacity(void);
+
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, int64_t qk_stride_t,
+                          const void* v, int64_t v_stride_t,
+                          const float* g, const float* beta,
+                          const float* initial_state, float* final_state,
+                          void* o,
+                          const int32_t* cu_seqlens, int n_seqs,
+                          int B, int T, int H, int Hk, int K, int V,
+                          float scale, int qk_l2norm, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * gdn_chunk_prepare / gdn_chunk_scan -- the two phases of gdn_chunk_fwd,
  * exposed separately (same arguments, same workspace) so that each can be
  * launched and timed on its own; gdn_chunk_fwd(...) is exactly

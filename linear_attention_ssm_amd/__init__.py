@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "GdnError", "LIB_PATH", "gdn_status_string", "gdn_conv1d_causal", "gdn_gate_prepare",
     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prepare", "gdn_chunk_scan",
+    "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_noalloc_capacity",
     "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
     "gdn_tune_set", "gdn_tune_get", "GDN_TUNE_SCAN_TILES", "GDN_TUNE_CONV_RUN",
     "GDN_TUNE_CONV_THREADS",
@@ -53,6 +54,11 @@ _lib.gdn_chunk_fwd_workspace_size.restype = _sz
 _lib.gdn_chunk_fwd.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
                                + [_i32] * 6 + [_f32, _i32, _i32, _vp, _sz, _vp])
 _lib.gdn_chunk_fwd.restype = _i32
+_lib.gdn_chunk_fwd_noalloc.argtypes = ([_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32]
+                                       + [_i32] * 6 + [_f32, _i32, _i32, _vp])
+_lib.gdn_chunk_fwd_noalloc.restype = _i32
+_lib.gdn_chunk_fwd_noalloc_capacity.argtypes = []
+_lib.gdn_chunk_fwd_noalloc_capacity.restype = _sz
 _lib.gdn_tune_set.argtypes = [_i32, _i32]
 _lib.gdn_tune_set.restype = _i32
 _lib.gdn_tune_get.argtypes = [_i32]
@@ -307,6 +313,48 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                             _stream(q.device))
     _check(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc_capacity() -> int:
+    """Bytes of the library's own device workspace used by gdn_chunk_fwd_noalloc."""
+    return int(_lib.gdn_chunk_fwd_noalloc_capacity())
+
+
+def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, o: torch.Tensor,
+                          initial_state: torch.Tensor | None = None,
+                          final_state: torch.Tensor | None = None,
+                          cu_seqlens: torch.Tensor | None = None, scale: float = 1.0,
+                          qk_l2norm: bool = True):
+    """gdn_chunk_fwd with the library's own fixed device workspace: nothing is
+    allocated, so the caller passes the outputs (o [B, T, H, V]; final_state
+    [N, H, K, V] fp32 or None). Calls that overlap on one GPU race on the
+    workspace. Returns (o, final_state)."""
+    B, T, Hk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    st_qk = _token_rows(q, "q", Hk, K)
+    if _token_rows(k, "k", Hk, K) != st_qk or k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must share shape, strides and dtype")
+    st_v = _token_rows(v, "v", H, V)
+    if v.shape[:2] != (B, T) or v.dtype != q.dtype:
+        raise ValueError("v must agree with q in batch, length and dtype")
+    _need(g, "g", (B, T, H), torch.float32)
+    _need(beta, "beta", (B, T, H), torch.float32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = n_seqs if cu_seqlens is not None else B
+    _chunk_outputs(q, B, T, N, H, K, V, initial_state, final_state is not None, o, final_state)
+    _same_device(q, k, v, g, beta, o, initial_state, final_state, cu_seqlens)
+    rc = _lib.gdn_chunk_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), st_qk, _dev(v, "v"), st_v,
+                                    _dev(g, "g"), _dev(beta, "beta"),
+                                    _opt(initial_state, "initial_state"),
+                                    _opt(final_state, "final_state"), _dev(o, "o"),
+                                    _opt(cu_seqlens, "cu_seqlens"), n_seqs, B, T, H, Hk, K, V,
+                                    float(scale), int(bool(qk_l2norm)), _code(q.dtype),
+                                    _stream(q.device))
+    _check(rc, "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

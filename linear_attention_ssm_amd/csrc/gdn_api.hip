@@ -4,6 +4,7 @@
 // has no side effect and the checks can be exercised without a GPU.
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "gdn_common.hpp"
@@ -220,6 +221,69 @@ int gdn_chunk_scan(const void* q, const void* k, int64_t qk_stride_t, const void
     return status_from(gdn::launch_chunk_scan(q, k, qk_stride_t, v, v_stride_t, initial_state,
                                               final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
                                               dtype == GDN_BF16, workspace, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- no-alloc variant
+//
+// gdn_chunk_fwd_noalloc: gdn_chunk_fwd with the workspace taken from a
+// file-scope device array instead of a caller buffer. In host code the
+// array's name is only a stand-in for the symbol; its device address, one per
+// GPU, comes from hipGetSymbolAddress on the first call made with that device
+// current, and only that address is ever handed to a kernel.
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)GDN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (nullptr on failure).
+void* device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_chunk_fwd_noalloc_capacity(void) { return kScratchBytes; }
+
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, int64_t qk_stride_t, const void* v,
+                          int64_t v_stride_t, const float* g, const float* beta,
+                          const float* initial_state, float* final_state, void* o,
+                          const int32_t* cu_seqlens, int n_seqs, int B, int T, int H, int Hk,
+                          int K, int V, float scale, int qk_l2norm, int dtype, void* stream)
+{
+    // every check runs before the first HIP call, as for gdn_chunk_fwd; the
+    // array's size stands in for the workspace (its address is not needed yet:
+    // a placeholder with the array's alignment passes the workspace checks)
+    const int st = check_chunk(q, k, qk_stride_t, v, v_stride_t, true, g, beta, true, initial_state,
+                               final_state, o, true, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+                               qk_l2norm, dtype, reinterpret_cast<const void*>(uintptr_t(256)),
+                               kScratchBytes);
+    if (st != GDN_OK) return st;
+    void* ws = device_scratch();
+    if (!ws) return GDN_ELAUNCH;
+    hipError_t e = gdn::launch_chunk_prepare(q, k, qk_stride_t, g, beta, cu_seqlens, n_seqs, B, T, H,
+                                             Hk, K, scale, qk_l2norm, dtype == GDN_BF16, ws,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return GDN_ELAUNCH;
+    return status_from(gdn::launch_chunk_scan(q, k, qk_stride_t, v, v_stride_t, initial_state,
+                                              final_state, o, cu_seqlens, n_seqs, B, T, H, Hk, K, V,
+                                              dtype == GDN_BF16, ws, (hipStream_t)stream));
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, int64_t qk_stride_t, const void* v,

@@ -60,6 +60,10 @@ def lib():
     L.gdn_prefill_prepare.argtypes = ([vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, vp, i32] + [i32] * 6
                                       + [f32, i32, i32, vp, sz, vp])
     L.gdn_prefill_scan.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6 + [i32, vp, sz, vp]
+    L.gdn_chunk_fwd_noalloc.argtypes = ([vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i32] + [i32] * 6
+                                        + [f32, i32, i32, vp])
+    L.gdn_chunk_fwd_noalloc_capacity.argtypes = []
+    L.gdn_chunk_fwd_noalloc_capacity.restype = sz
     return L
 
 
@@ -525,3 +529,21 @@ def test_binding_checks_every_supplied_tensor():
     _raises(lambda: gdn.gdn_gdp_prefill_prepare(xg, bg, z(H, dtype=bf), AL, M, H, G, P, N), "A_log must be")
     # correct shapes on the CPU: the device check still refuses them
     _raises(lambda: gdn.gdn_chunk_fwd(q, q, v, g, g, o=ok_o), "GPU")
+
+
+def test_noalloc_validation(lib):
+    """gdn_chunk_fwd_noalloc: the checks of gdn_chunk_fwd, and a workspace
+    that would exceed the library's fixed array refused before any HIP call."""
+    cap = lib.gdn_chunk_fwd_noalloc_capacity()
+    assert cap == 64 << 20
+    call = lambda **kw: lib.gdn_chunk_fwd_noalloc(
+        kw.get("q", P), kw.get("k", P + 4096), kw.get("qks", 6144), kw.get("v", P + 8192), 6144,
+        kw.get("g", P2), kw.get("beta", P3), None, kw.get("Sf", P4), kw.get("o", P5), None, 0,
+        kw.get("B", 4), kw.get("T", 4096), 16, 16, 128, 128, 1.0, 1, kw.get("dtype", BF16), None)
+    assert call(q=None) == EINVAL and call(o=None) == EINVAL and call(o=P) == EINVAL
+    assert call(g=None) == EINVAL and call(Sf=P5) == EINVAL
+    assert call(dtype=3) == EUNSUP and call(q=P + 2) == EUNSUP
+    # the prefill workload fits; eight times its batch does not
+    assert lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16) <= cap
+    assert lib.gdn_chunk_fwd_workspace_size(32, 4096, 16, 16, 128, 128, 0, BF16) > cap
+    assert call(B=32) == EWS
