@@ -72,13 +72,20 @@ const char* gdn_status_string(int status);
  *                          32.
  *   GDN_TUNE_CONV_THREADS  threads per workgroup of gdn_conv1d_causal: 64,
  *                          128 or 256.
+ *   GDN_TUNE_SCAN_FORM     workgroup form of the bf16 state scan: 1 = one
+ *                          workgroup per group of 16 * GDN_TUNE_SCAN_TILES
+ *                          value columns of a (sequence, head) unit, waves
+ *                          split by role; 2 = one workgroup per unit over all
+ *                          its value columns, four waves each running the
+ *                          whole chunk step for a quarter of them.
  * gdn_tune_set returns GDN_EINVAL for an unknown knob or value (nothing
  * changes); gdn_tune_get returns the knob's value, or -1 for an unknown knob.
  * ---------------------------------------------------------------------- */
 enum {
     GDN_TUNE_SCAN_TILES = 0,
     GDN_TUNE_CONV_RUN = 1,
-    GDN_TUNE_CONV_THREADS = 2
+    GDN_TUNE_CONV_THREADS = 2,
+    GDN_TUNE_SCAN_FORM = 3
 };
 int gdn_tune_set(int knob, int value);
 int gdn_tune_get(int knob);

@@ -23,7 +23,7 @@ __all__ = [
     "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_noalloc_capacity",
     "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_prepare", "gdn_prefill_scan",
     "gdn_tune_set", "gdn_tune_get", "GDN_TUNE_SCAN_TILES", "GDN_TUNE_CONV_RUN",
-    "GDN_TUNE_CONV_THREADS",
+    "GDN_TUNE_CONV_THREADS", "GDN_TUNE_SCAN_FORM",
     "gdn_recurrent_decode", "gdn_decode_prepare", "gdn_conv1d_update", "gdn_gdp_prefill_prepare",
     "gdp_prefill", "prefill_chain", "split_qkv",
 ]
@@ -359,7 +359,7 @@ def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
 
 
 # launch-configuration knobs (C constants of the same names)
-GDN_TUNE_SCAN_TILES, GDN_TUNE_CONV_RUN, GDN_TUNE_CONV_THREADS = 0, 1, 2
+GDN_TUNE_SCAN_TILES, GDN_TUNE_CONV_RUN, GDN_TUNE_CONV_THREADS, GDN_TUNE_SCAN_FORM = 0, 1, 2, 3
 
 
 def gdn_tune_set(knob: int, value: int) -> None:

@@ -2100,6 +2100,458 @@ void chunk_scan_roles_kernel(
     }
 }
 
+// ------------------------------------------------------------ chunk_scan, wide workgroups (bf16)
+//
+// One workgroup per (sequence, value head) unit holding ALL of the unit's V
+// value columns, so a chunk's K and Q tiles and its record are staged into LDS
+// once per unit instead of once per column group. NT / TPW compute waves:
+// wave w owns the TPW column tiles TPW w .. TPW w + TPW - 1 (16 columns each,
+// V = 16 NT) and runs the whole chunk step for them, the dependent
+// chain X = K h, U = T (V - a o X), h' = gamma_L h + K^T (c o U) and the
+// output O^T = b o (h^T Q^T) + U^T P^T (as the role-split kernel's output
+// wave forms it, so each lane stores consecutive columns of one row), with no
+// hand-off between waves. With two compute waves per SIMD (one tile each),
+// one wave's VALU work and LDS waits overlap the other's matrix ops, and the
+// compute waves issue the copies of the next chunk themselves (a wave stalled
+// getting its share into the vector-memory pipe leaves its SIMD to the other);
+// with one compute wave per SIMD (two tiles each) a copy wave issues every
+// direct-to-LDS copy of the
+// next chunk at the start of a step (61 KiB at K = V = 128: 61 copies, which
+// fit its vector-memory counter) and waits for them at the end, so the
+// compute waves never stall on the vector-memory pipe: measured with cycle
+// stamps, a compute wave that issued a quarter of the copies itself spent
+// 2,200 - 3,500 cycles per chunk just getting them into the pipe. Two buffers:
+// chunk c + 1 lands while chunk c is computed; one barrier per chunk. Inside a
+// step each phase's LDS operands are requested during the phase before, so
+// their latency hides behind matrix ops.
+template <int KD, int NTILES>
+struct WideBuf {
+    static constexpr int RB = KD * 2;                       // bytes per K / Q row
+    static constexpr int SPR = RB / 16;                     // 16-byte segments per row
+    static constexpr int RPI = 1024 / RB;                   // rows per 1 KiB piece
+    static constexpr int tile_pieces = kChunk * RB / 1024;
+    static constexpr int rec_pieces = Rec<bf16>::bytes / 1024;
+    static constexpr int NT = NTILES;                       // column tiles of the unit
+    static constexpr int VRB = 32;                          // bytes per row of a tile slab
+    static constexpr int v_pieces = NT * kChunk * VRB / 1024;
+    static constexpr int copies = 2 * tile_pieces + v_pieces + rec_pieces;
+    static_assert(copies < 64, "a chunk's copies fit the vector-memory counter");
+    unsigned char k[kChunk * RB];
+    unsigned char q[kChunk * RB];
+    unsigned char rec[Rec<bf16>::bytes];
+    unsigned char v[NT][kChunk * VRB];
+};
+
+// The direct-to-LDS copies of one chunk, pieces p = wave, wave + NW, ... of
+// the list [K tile][Q tile][value slabs][record] (1 KiB each), issued by NW
+// waves: the copy wave alone (NW = 1), or every compute wave. Per piece this
+// lane's source offset and the piece's place in the buffer; the tensor of a
+// piece is wave-uniform.
+template <int KD, int NT, int NW>
+struct WideCopies {
+    typedef WideBuf<KD, NT> WB;
+    static constexpr int total = WB::copies;
+    static constexpr int per = (total + NW - 1) / NW;
+    uint32_t src[per];
+    uint32_t dst[per];
+    int tensor[per];          // 0 K, 1 Q, 2 values, 3 record, 4 none
+    __device__ __forceinline__ void init(int wave, int lane, uint32_t qk_row, uint32_t v_row) {
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            const int p = wave + NW * i;
+            int t = 4, j = 0;
+            if (p < WB::tile_pieces) { t = 0; j = p; }
+            else if (p < 2 * WB::tile_pieces) { t = 1; j = p - WB::tile_pieces; }
+            else if (p < 2 * WB::tile_pieces + WB::v_pieces) { t = 2; j = p - 2 * WB::tile_pieces; }
+            else if (p < total) { t = 3; j = p - 2 * WB::tile_pieces - WB::v_pieces; }
+            tensor[i] = t;
+            if (t <= 1) {
+                // rows RPI j .., each lane fetching the logical segment stored at its LDS position
+                const int row = j * WB::RPI + lane / WB::SPR;
+                const int sg = (lane % WB::SPR) ^ tile_mask<bf16, KD, 1>(row);
+                src[i] = (uint32_t)row * qk_row + (uint32_t)sg * 16;
+                dst[i] = (t == 0 ? offsetof(WB, k) : offsetof(WB, q)) + j * 1024;
+            } else if (t == 2) {
+                // rows 32 (j % 2) .. of slab j / 2
+                const int row = 32 * (j & 1) + lane / 2;
+                src[i] = (uint32_t)row * v_row + (uint32_t)(j >> 1) * 32 + (uint32_t)(lane & 1) * 16;
+                dst[i] = offsetof(WB, v) + (j >> 1) * (kChunk * WB::VRB) + (j & 1) * 1024;
+            } else {
+                src[i] = (uint32_t)j * 1024 + lane * 16;
+                dst[i] = offsetof(WB, rec) + j * 1024;
+            }
+        }
+    }
+    __device__ __forceinline__ void issue(unsigned char* buf, rsrc_t rk, rsrc_t rq, rsrc_t rv,
+                                          rsrc_t rr) const {
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            const int t = tensor[i];
+            if (t == 4) continue;
+            const rsrc_t r = t == 0 ? rk : t == 1 ? rq : t == 2 ? rv : rr;
+            dma16(r, buf + dst[i], src[i], 0);
+        }
+    }
+};
+
+// compute waves of a unit of NT column tiles with TPW tiles each; with
+// COPYW a copy wave comes after them
+template <int NT, int TPW>
+constexpr int wide_waves() { return NT / TPW; }
+template <int NT, int TPW, bool COPYW>
+constexpr int wide_block() { return (wide_waves<NT, TPW>() + (COPYW ? 1 : 0)) * kWave; }
+
+template <int KD, int NT, int TPW, bool COPYW>
+__global__ __launch_bounds__((wide_block<NT, TPW, COPYW>()))
+__attribute__((amdgpu_waves_per_eu((wide_block<NT, TPW, COPYW>() / kWave + 3) / 4,
+                                   (wide_block<NT, TPW, COPYW>() / kWave + 3) / 4)))
+void chunk_scan_wide_kernel(
+    const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
+    const bf16* __restrict__ vp, int64_t v_stride,
+    const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
+    const unsigned char* __restrict__ ws_rec, int T_len, int H, int Hk, int units)
+{
+    typedef WideBuf<KD, NT> WB;
+    constexpr int kWideWaves = wide_waves<NT, TPW>();
+    typedef Mma<bf16> MT;
+    typedef bf16x8 Frag;
+    typedef Rec<bf16> RC;
+    constexpr int V = 16 * WB::NT;
+    constexpr int KB = KD / 32;
+    constexpr int RT = KD / 16;
+    extern __shared__ __align__(1024) unsigned char smem_raw[];
+    WB* bufs = reinterpret_cast<WB*>(smem_raw);
+
+    // XCD-aware order: the value heads that share a q/k head run on one XCD
+    // (blockIdx % 8), one after another, so their K and Q rows come from its L2
+    const int bid = blockIdx.x;
+    const int u = (bid & 7) * ((units + 7) >> 3) + (bid >> 3);
+    if (u >= units) return;
+    const int seq = u / H;
+    const int h = u - seq * H;
+    const int hk = h / (H / Hk);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    int tok_begin, tok_end, tile0;
+    if (cu) {
+        tok_begin = cu[seq];
+        tok_end = cu[seq + 1];
+        tile0 = offsets[seq];
+    } else {
+        tok_begin = seq * T_len;
+        tok_end = tok_begin + T_len;
+        tile0 = seq * ((T_len + kChunk - 1) / kChunk);
+    }
+    const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
+
+    // A partial last chunk leaves the rows past the sequence unfetched: start
+    // them at zero so they hold finite values (their factors are zero).
+    if ((tok_end - tok_begin) % kChunk != 0) {
+        const f32x4 z = zero4();
+        for (int i = threadIdx.x * 16; i < 2 * (int)sizeof(WB); i += wide_block<NT, TPW, COPYW>() * 16)
+            *reinterpret_cast<f32x4*>(smem_raw + i) = z;
+        lds_barrier();
+    }
+
+    // ---- copies: chunk c + 1 into buffer (c + 1) % 2 during step c
+    const uint32_t qk_row = (uint32_t)(qk_stride * 2);
+    const uint32_t v_row = (uint32_t)(v_stride * 2);
+    const uint64_t k0 = (uint64_t)(kp + (int64_t)tok_begin * qk_stride + hk * KD);
+    const uint64_t q0 = (uint64_t)(qp + (int64_t)tok_begin * qk_stride + hk * KD);
+    const uint64_t v0 = (uint64_t)(vp + (int64_t)tok_begin * v_stride + h * V);
+    const uint64_t r0 = (uint64_t)(ws_rec + ((int64_t)tile0 * H + h) * RC::bytes);
+    const uint64_t rstep = (uint64_t)H * RC::bytes;
+    constexpr int NW = COPYW ? 1 : kWideWaves;
+    WideCopies<KD, NT, NW> cp;
+    if (!COPYW || wave == kWideWaves) cp.init(COPYW ? 0 : wave, lane, qk_row, v_row);
+    auto issue = [&](int c) {
+        const bool valid = c < nchunks;
+        const int cc = valid ? c : 0;
+        const uint32_t L = valid ? (uint32_t)min(kChunk, tok_end - (tok_begin + cc * kChunk)) : 0u;
+        cp.issue(reinterpret_cast<unsigned char*>(&bufs[c & 1]),
+                 make_rsrc((const void*)(k0 + (uint64_t)cc * kChunk * qk_row), L * qk_row),
+                 make_rsrc((const void*)(q0 + (uint64_t)cc * kChunk * qk_row), L * qk_row),
+                 make_rsrc((const void*)(v0 + (uint64_t)cc * kChunk * v_row), L * v_row),
+                 make_rsrc((const void*)(r0 + (uint64_t)cc * rstep), valid ? (uint32_t)RC::bytes : 0u));
+    };
+
+    if (COPYW && wave == kWideWaves) {
+        // ---------------- copy wave
+        issue(0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            issue(c + 1);
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---------------- compute wave
+    uint32_t rf[KB], tf[2][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        rf[kb] = (uint32_t)tile_off<bf16, KD, 1>(col, 32 * kb + 8 * grp);
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            tf[par][kb] = (uint32_t)tile_off<bf16, KD, 1>(4 * grp + (col >> 2), state_row(2 * kb + par, col & 3, 0));
+    }
+    const uint32_t vtr = (uint32_t)((4 * grp + (col >> 2)) * WB::VRB + (col & 3) * 8);
+
+    const int64_t sbase = ((int64_t)seq * H + h) * KD * V;
+    f32x4 hs[TPW][RT];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int vc = 16 * (TPW * wave + t) + col;
+        if (S0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hs[t][rt][e] = S0[sbase + (int64_t)state_row(rt, grp, e) * V + vc];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) hs[t][rt] = zero4();
+        }
+    }
+    Frag hf[TPW][KB];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag<bf16>(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
+
+    const int64_t HV = (int64_t)H * V;
+    const uint32_t o_row = (uint32_t)(HV * 2);
+    if constexpr (!COPYW) {
+        issue(0);
+        wait_vmcnt<0>();
+    }
+    lds_barrier();   // chunk 0 has landed
+
+    for (int c = 0; c < nchunks; ++c) {
+        if constexpr (!COPYW) issue(c + 1);
+        const WB* __restrict__ cur = &bufs[c & 1];
+        const unsigned char* kt = cur->k;
+        const unsigned char* qt = cur->q;
+        const unsigned char* rec = cur->rec;
+        auto row_frag = [&](const unsigned char* tile, int rt, int kb) -> Frag {
+            return ld<Frag>(tile + rf[kb] + 16 * rt * WB::RB);
+        };
+        auto fac4 = [&](int which, int rt) -> f32x4 {
+            return ld<f32x4>(rec + RC::fac + (which * kChunk + 16 * rt + 4 * grp) * 4);
+        };
+        auto kt_frag = [&](int rt, int half) -> Frag {
+            const unsigned char* p = kt + tf[rt & 1][rt >> 1] + 32 * half * WB::RB;
+            const s16x4 lo = lds_read_tr16(p);
+            const s16x4 hi = lds_read_tr16(p + 16 * WB::RB);
+            return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+
+        // ---- operands of X (row tiles 0, 1), the values and the factor a
+        Frag ka[2][KB], kb2[2][KB];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) ka[r][kb] = row_frag(kt, r, kb);
+        s16x4 vraw[TPW][4];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) vraw[t][rt] = lds_read_tr16(cur->v[TPW * wave + t] + vtr + rt * 16 * WB::VRB);
+        f32x4 fa[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) fa[rt] = fac4(0, rt);
+        SCAN_FENCE();
+
+        // ---- X = K h, row tiles 0, 1 (loads: K row tiles 2, 3 and T)
+        f32x4 X[TPW][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                X[t][r] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) X[t][r] = MT::mma(ka[r][kb], hf[t][kb], X[t][r]);
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) kb2[r][kb] = row_frag(kt, 2 + r, kb);
+        Frag tfr[kTriFrags];
+#pragma unroll
+        for (int f = 0; f < kTriFrags; ++f) tfr[f] = ld<Frag>(rec + RC::tfrag + (f * kWave + lane) * RC::frag_bytes);
+        SCAN_FENCE();
+
+        // ---- X, row tiles 2, 3 (loads: Q row tiles 0, 1)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                X[t][2 + r] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) X[t][2 + r] = MT::mma(kb2[r][kb], hf[t][kb], X[t][2 + r]);
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) ka[r][kb] = row_frag(qt, r, kb);
+        SCAN_FENCE();
+
+        // ---- U = T (V - a o X) (loads: Q row tiles 2, 3)
+        f32x4 U[TPW][4];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 vv = __builtin_convertvector(__builtin_bit_cast(bf16x4, vraw[t][rt]), f32x4);
+                X[t][rt] = vv - fa[rt] * X[t][rt];
+            }
+            const Frag vf0 = MT::acc_frag(X[t][0], X[t][1]);
+            const Frag vf1 = MT::acc_frag(X[t][2], X[t][3]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[t][rt] = MT::mma(tfr[tri_frag(rt, 0)], vf0, zero4());
+#pragma unroll
+            for (int rt = 2; rt < 4; ++rt) U[t][rt] = MT::mma(tfr[tri_frag(rt, 1)], vf1, U[t][rt]);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) kb2[r][kb] = row_frag(qt, 2 + r, kb);
+        SCAN_FENCE();
+
+        // ---- Y^T = h^T Q^T, row tiles 0, 1, then 2, 3 (loads: P, b, c, gamma_L)
+        f32x4 Y[TPW][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                Y[t][r] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) Y[t][r] = MT::mma(hf[t][kb], ka[r][kb], Y[t][r]);
+            }
+        Frag pfr[kTriFrags];
+#pragma unroll
+        for (int f = 0; f < kTriFrags; ++f) pfr[f] = ld<Frag>(rec + RC::pfrag + (f * kWave + lane) * RC::frag_bytes);
+        float fb[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) fb[rt] = ld<float>(rec + RC::fac + (1 * kChunk + 16 * rt + col) * 4);
+        SCAN_FENCE();
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                Y[t][2 + r] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) Y[t][2 + r] = MT::mma(hf[t][kb], kb2[r][kb], Y[t][2 + r]);
+            }
+        f32x4 fc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) fc[rt] = fac4(2, rt);
+        const float gL = ld<float>(rec + RC::fac + 3 * kChunk * 4);
+        SCAN_FENCE();
+
+        // ---- O^T = b o Y^T + U^T P^T; c o U (loads: K^T of state tiles 0, 1)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const Frag uf0 = MT::acc_frag(U[t][0], U[t][1]);
+            const Frag uf1 = MT::acc_frag(U[t][2], U[t][3]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Y[t][rt] = MT::mma(uf0, pfr[tri_frag(rt, 0)], Y[t][rt] * fb[rt]);
+                if (rt >= 2) Y[t][rt] = MT::mma(uf1, pfr[tri_frag(rt, 1)], Y[t][rt]);
+            }
+        }
+        Frag df[TPW][2];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) U[t][rt] *= fc[rt];
+            df[t][0] = MT::acc_frag(U[t][0], U[t][1]);
+            df[t][1] = MT::acc_frag(U[t][2], U[t][3]);
+        }
+        Frag ktf[2][2][2];   // [pair parity][tile of the pair][half]
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) ktf[0][i][half] = kt_frag(i, half);
+        SCAN_FENCE();
+
+        // ---- h' = gamma_L h + K^T (c o U), two state tiles at a time, the K^T
+        // operands of the next two requested before the current products
+#pragma unroll
+        for (int rp = 0; rp < RT / 2; ++rp) {
+            if (rp + 1 < RT / 2) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+                        ktf[(rp + 1) & 1][i][half] = kt_frag(2 * (rp + 1) + i, half);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const int rt = 2 * rp + i;
+                    f32x4 acc = hs[t][rt] * gL;
+                    acc = MT::mma(ktf[rp & 1][i][0], df[t][0], acc);
+                    hs[t][rt] = MT::mma(ktf[rp & 1][i][1], df[t][1], acc);
+                }
+            SCAN_FENCE();
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag<bf16>(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
+
+        // ---- the chunk's outputs
+        const int tok0 = tok_begin + c * kChunk;
+        const uint32_t L = (uint32_t)min(kChunk, tok_end - tok0);
+        const rsrc_t ro = make_rsrc(o + (int64_t)tok0 * HV + (int64_t)h * V + 16 * TPW * wave, L * o_row);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if constexpr (TPW == 2) {
+                // lane swaps give lane (g, c) the wave's columns 8 g .. + 7 of row c
+                const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[0][rt], bf16x4));
+                const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[1][rt], bf16x4));
+                u32x4 s;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(w32[0], w32[1], false, false);
+                    s[d] = w16[0];
+                    s[2 + d] = w16[1];
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(s, ro, (uint32_t)(16 * rt + col) * o_row + 16 * grp, 0, 0);
+            } else {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const bf16x4 ob = __builtin_convertvector(Y[t][rt], bf16x4);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
+                                                          (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
+                }
+            }
+        }
+        if constexpr (!COPYW) wait_vmcnt<0>();   // this wave's copies of chunk c + 1 (and its stores)
+        lds_barrier();   // every wave is done with this buffer; chunk c + 1 has landed
+    }
+
+    if (Sfin) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int vc = 16 * (TPW * wave + t) + col;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sfin[sbase + (int64_t)state_row(rt, grp, e) * V + vc] = hs[t][rt][e];
+        }
+    }
+}
+
 // ------------------------------------------------------------ launchers
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -2171,6 +2623,27 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
     return hipGetLastError();
 }
 
+template <int KD, int NT, int TPW, bool COPYW>
+static hipError_t launch_scan_wide(const void* q, const void* k, int64_t qks, const void* v,
+                                   int64_t vs, const float* S0, float* Sf, void* o,
+                                   const int32_t* cu, const int32_t* offsets,
+                                   const unsigned char* wsrec, int T_len, int H, int Hk, int N,
+                                   hipStream_t stream)
+{
+    const int units = N * H;
+    const int u8 = (units + 7) / 8;
+    typedef WideBuf<KD, NT> WB;
+    constexpr size_t smem = 2 * sizeof(WB);
+    static_assert(smem <= 160 * 1024, "wide scan staging fits in LDS");
+    auto kern = chunk_scan_wide_kernel<KD, NT, TPW, COPYW>;
+    hipError_t err = set_smem(kern, smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * u8)), dim3(wide_block<NT, TPW, COPYW>()), smem,
+                       stream, (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf,
+                       (bf16*)o, cu, offsets, wsrec, T_len, H, Hk, units);
+    return hipGetLastError();
+}
+
 struct ChunkWs {
     int32_t* offsets;
     unsigned char* rec;
@@ -2239,7 +2712,15 @@ static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const
     const int slabs = V / 16;
     const int tiles = scan_tiles(units, slabs, sizeof(T) == 2);
     if constexpr (sizeof(T) == 2) {
-        // bf16 operands: the split-role step
+        // bf16 operands: whole-unit workgroups when chosen, else the split-role step
+        if (tune_knob[kTuneScanForm] == 2) {
+            // (GDN_TUNE_SCAN_TILES = 2: two tiles per compute wave, else one)
+            if (V == 128 && tune_knob[kTuneScanTiles] == 2)
+                return launch_scan_wide<KD, 8, 2, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
+            if (V == 128)
+                return launch_scan_wide<KD, 8, 1, false>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
+            return launch_scan_wide<KD, 4, 1, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
+        }
         if (tiles == 2)
             return launch_scan_roles<KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);
         return launch_scan_roles<KD, 1>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);

@@ -54,7 +54,7 @@ hipError_t launch_gdp_prefill_prepare(const void* x, int64_t xs, const void* ba,
 }  // namespace gdn
 
 namespace gdn {
-int tune_knob[kTuneKnobs] = {0, 0, 0};
+int tune_knob[kTuneKnobs] = {0, 0, 0, 0};
 }  // namespace gdn
 
 namespace {
@@ -138,6 +138,9 @@ int gdn_tune_set(int knob, int value)
         break;
     case GDN_TUNE_CONV_THREADS:
         if (value != 0 && value != 64 && value != 128 && value != 256) return GDN_EINVAL;
+        break;
+    case GDN_TUNE_SCAN_FORM:
+        if (value < 0 || value > 2) return GDN_EINVAL;
         break;
     default:
         return GDN_EINVAL;

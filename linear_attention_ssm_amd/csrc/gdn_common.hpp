@@ -265,7 +265,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Launch-configuration knobs (gdn_tune_set): 0 = automatic. They change how
 // work is scheduled, never the arithmetic, so every setting gives the same
 // bits. Read by the launchers on the host.
-enum TuneKnob { kTuneScanTiles = 0, kTuneConvRun = 1, kTuneConvThreads = 2, kTuneKnobs = 3 };
+enum TuneKnob { kTuneScanTiles = 0, kTuneConvRun = 1, kTuneConvThreads = 2, kTuneScanForm = 3, kTuneKnobs = 4 };
 extern int tune_knob[kTuneKnobs];
 
 }  // namespace gdn

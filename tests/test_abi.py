@@ -257,19 +257,19 @@ def test_prefill_phase_validation(lib):
 
 
 def test_tune_knobs(lib):
-    SCAN, RUN, THREADS = 0, 1, 2
+    SCAN, RUN, THREADS, FORM = 0, 1, 2, 3
     try:
         for knob, good, bad in ((SCAN, (1, 2, 4, 0), (3, -1, 8)), (RUN, (8, 16, 32, 0), (4, 64)),
-                                (THREADS, (64, 128, 256, 0), (32, 512))):
+                                (THREADS, (64, 128, 256, 0), (32, 512)), (FORM, (1, 2, 0), (3, -1))):
             for v in good:
                 assert lib.gdn_tune_set(knob, v) == OK and lib.gdn_tune_get(knob) == v
             lib.gdn_tune_set(knob, good[0])
             for v in bad:   # rejected values change nothing
                 assert lib.gdn_tune_set(knob, v) == EINVAL and lib.gdn_tune_get(knob) == good[0]
-        assert lib.gdn_tune_set(3, 0) == EINVAL and lib.gdn_tune_get(3) == -1
+        assert lib.gdn_tune_set(4, 0) == EINVAL and lib.gdn_tune_get(4) == -1
         assert lib.gdn_tune_get(-1) == -1
     finally:
-        for knob in (SCAN, RUN, THREADS):
+        for knob in (SCAN, RUN, THREADS, FORM):
             lib.gdn_tune_set(knob, 0)
 
 

@@ -1,0 +1,103 @@
+"""The two workgroup forms of the bf16 state scan (GDN_TUNE_SCAN_FORM):
+column groups with role-split waves (1), and one workgroup per (sequence,
+head) unit over all its value columns (2). The form only reschedules the
+same arithmetic: both must give the same bits on every shape, and each is
+checked against the fp64 oracle directly on the small shapes (head dims,
+GQA, ragged and packed lengths, an initial state, scale, no normalisation)
+and at the workloads' full sizes on sampled units."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.helpers import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda")
+BF16 = torch.bfloat16
+FORMS = (1, 2)
+
+
+@pytest.fixture
+def form(gpu):
+    yield gpu
+    gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, 0)
+
+
+def _run(gdn, d, f, **kw):
+    gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, f)
+    t = {n: (None if d[n] is None else d[n].to(DEV)) for n in ("q", "k", "v", "g", "beta", "S0", "cu_seqlens")}
+    o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["S0"],
+                              cu_seqlens=t["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return o, sf
+
+
+def _oracle(d, **kw):
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
+    return oracle.gated_delta_rule(to_np(d["q"]), to_np(d["k"]), to_np(d["v"]), to_np(d["g"]),
+                                   to_np(d["beta"]), S0=None if d["S0"] is None else to_np(d["S0"]),
+                                   cu_seqlens=cu, **kw)
+
+
+SMALL = {
+    "k128v128": dict(B=2, T=321, H=4, Hk=4, K=128, V=128),
+    "k64v64": dict(B=2, T=200, H=2, Hk=2, K=64, V=64),
+    "k64v128": dict(B=1, T=130, H=2, Hk=1, K=64, V=128),
+    "k128v64": dict(B=1, T=257, H=4, Hk=2, K=128, V=64),
+    "gqa-s0": dict(B=1, T=700, H=4, Hk=2, K=128, V=128, s0_std=0.05, decay="weak"),
+    "one-token": dict(B=3, T=1, H=2, Hk=2, K=128, V=128, s0_std=0.1),
+    "packed": dict(B=1, T=1 + 64 + 65 + 200 + 3, H=2, Hk=2, K=128, V=128,
+                   lengths=[1, 64, 65, 200, 3], decay="weak"),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_forms_equal_and_match_oracle(form, case):
+    kw = dict(SMALL[case])
+    d = wl.chunk_inputs(dtype=BF16, seed=hash(case) % 1000, **kw)
+    print(f"scan forms: {case}", flush=True)
+    ref = _run(form, d, 1)
+    ro, rs = _oracle(d)
+    for f in FORMS:
+        o, sf = _run(form, d, f)
+        assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1]), (case, f)
+        assert_close(to_np(o), ro, BF16, f"{case} form={f} o")
+        assert_close(to_np(sf), rs, BF16, f"{case} form={f} state")
+
+
+def test_forms_scale_and_no_norm(form):
+    d = wl.chunk_inputs(B=1, T=150, H=2, Hk=2, K=128, V=128, dtype=BF16, seed=5)
+    # no normalisation: keys of unit norm so the recurrence stays bounded
+    for n in ("q", "k"):
+        x = d[n].float()
+        d[n] = (x / x.norm(dim=-1, keepdim=True)).to(BF16)
+    for kw in (dict(scale=128 ** -0.5), dict(qk_l2norm=False)):
+        ref = _run(form, d, 1, **kw)
+        ro, rs = _oracle(d, scale=kw.get("scale", 1.0), l2norm=kw.get("qk_l2norm", True))
+        o, sf = _run(form, d, 2, **kw)
+        assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1]), kw
+        assert_close(to_np(o), ro, BF16, f"form=2 {kw} o")
+
+
+@pytest.mark.parametrize("name", ["prefill", "gqa", "varlen"])
+def test_forms_equal_full_size(form, name):
+    # the workloads' full sizes through conv1d + gates + chunk_fwd: the forms
+    # agree bit for bit (the chain itself is checked against the oracle at
+    # these sizes in test_gpu_chunk.py)
+    w = wl.WORKLOADS[name]
+    d = wl.prefill_inputs(w)
+    print(f"scan forms full size: {name}", flush=True)
+    t = {n: d[n].to(DEV) for n in ("x", "w", "a", "b", "A_log", "dt_bias")}
+    S0 = None if d["S0"] is None else d["S0"].to(DEV)
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].to(DEV)
+    outs = []
+    for f in FORMS:
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f)
+        o, sf = form.prefill_chain(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                   Hk=w.Hk, K=w.K, H=w.H, V=w.V, initial_state=S0, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        outs.append((o, sf))
+    assert torch.equal(outs[0][0], outs[1][0]), f"{name}: o differs between forms"
+    assert torch.equal(outs[0][1], outs[1][1]), f"{name}: final state differs between forms"

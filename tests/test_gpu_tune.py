@@ -13,7 +13,8 @@ DEV = torch.device("cuda")
 @pytest.fixture
 def knobs(gpu):
     yield gpu
-    for k in (gpu.GDN_TUNE_SCAN_TILES, gpu.GDN_TUNE_CONV_RUN, gpu.GDN_TUNE_CONV_THREADS):
+    for k in (gpu.GDN_TUNE_SCAN_TILES, gpu.GDN_TUNE_CONV_RUN, gpu.GDN_TUNE_CONV_THREADS,
+              gpu.GDN_TUNE_SCAN_FORM):
         gpu.gdn_tune_set(k, 0)
 
 
