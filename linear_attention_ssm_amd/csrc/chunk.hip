@@ -73,12 +73,18 @@ template <typename T> struct Rec {
 
 // ------------------------------------------------------------ chunk plan
 
-// offsets[i] = sum_{j < i} ceil(len_j / 64) for packed sequences (one block).
+// offsets[i] = sum_{j < i} ceil(len_j / 64) for packed sequences (one block),
+// and order[r] = the sequence of rank r by length, longest first (ties by
+// index), so the whole-unit scan can start the longest sequences first;
+// beyond kPlanSortMax sequences the order is the identity.
+constexpr int kPlanSortMax = 1024;
 __global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t* __restrict__ cu, int n,
-                                                         int32_t* __restrict__ offsets)
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ order)
 {
     __shared__ int32_t buf[256];
     __shared__ int32_t carry_s;
+    __shared__ int32_t len_s[kPlanSortMax];
     if (threadIdx.x == 0) { carry_s = 0; offsets[0] = 0; }
     __syncthreads();
     for (int base = 0; base < n; base += 256) {
@@ -98,6 +104,22 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t* __restri
         __syncthreads();
         if (threadIdx.x == 255) carry_s = carry + buf[255];
         __syncthreads();
+    }
+    if (n > kPlanSortMax) {
+        for (int i = threadIdx.x; i < n; i += 256) order[i] = i;
+        return;
+    }
+    for (int i = threadIdx.x; i < n; i += 256) len_s[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    // rank of sequence i: the sequences longer than it, or as long with a smaller index
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int li = len_s[i];
+        int r = 0;
+        for (int j = 0; j < n; ++j) {
+            const int lj = len_s[j];
+            r += (lj > li) | ((lj == li) & (j < i));
+        }
+        order[r] = i;
     }
 }
 
@@ -695,6 +717,21 @@ __device__ __forceinline__ typename Mma<T>::Frag state_frag(const f32x4& t0, con
     return Mma<T>::acc_frag(lo, hi);
 }
 
+
+// The same B operand, built by converting each tile to bf16 first and then
+// swapping whole dwords in groups 2 and 3 (4 selects per operand instead of 8);
+// identical bits.
+__device__ __forceinline__ bf16x8 state_frag_bf16(const f32x4& t0, const f32x4& t1, int grp) {
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(t0, bf16x4));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(t1, bf16x4));
+    const bool sw = grp >= 2;
+    u32x4 r;
+    r[0] = sw ? b[0] : a[0];
+    r[1] = sw ? b[1] : a[1];
+    r[2] = sw ? a[0] : b[0];
+    r[3] = sw ? a[1] : b[1];
+    return __builtin_bit_cast(bf16x8, r);
+}
 
 // LDS staging of one chunk for the scan: raw K and Q tiles, the chunk's record
 // and each wave's 64 x 16 slab of values, all written by direct-to-LDS loads
@@ -2210,6 +2247,7 @@ void chunk_scan_wide_kernel(
     const bf16* __restrict__ vp, int64_t v_stride,
     const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ order,
     const unsigned char* __restrict__ ws_rec, int T_len, int H, int Hk, int units)
 {
     typedef WideBuf<KD, NT> WB;
@@ -2223,13 +2261,16 @@ void chunk_scan_wide_kernel(
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     WB* bufs = reinterpret_cast<WB*>(smem_raw);
 
-    // XCD-aware order: the value heads that share a q/k head run on one XCD
-    // (blockIdx % 8), one after another, so their K and Q rows come from its L2
+    // Dense batches: XCD-aware order, the value heads that share a q/k head run
+    // on one XCD (blockIdx % 8), one after another, so their K and Q rows come
+    // from its L2. Packed sequences: longest first (order from the plan), so
+    // the last workgroups to start are the shortest and the tail is short.
     const int bid = blockIdx.x;
-    const int u = (bid & 7) * ((units + 7) >> 3) + (bid >> 3);
+    const int u = cu ? bid : (bid & 7) * ((units + 7) >> 3) + (bid >> 3);
     if (u >= units) return;
-    const int seq = u / H;
-    const int h = u - seq * H;
+    const int rank = u / H;
+    const int h = u - rank * H;
+    const int seq = cu ? order[rank] : rank;
     const int hk = h / (H / Hk);
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -2323,7 +2364,7 @@ void chunk_scan_wide_kernel(
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag<bf16>(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
+        for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag_bf16(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
 
     const int64_t HV = (int64_t)H * V;
     const uint32_t o_row = (uint32_t)(HV * 2);
@@ -2506,7 +2547,7 @@ void chunk_scan_wide_kernel(
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag<bf16>(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
+            for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag_bf16(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
 
         // ---- the chunk's outputs
         const int tok0 = tok_begin + c * kChunk;
@@ -2561,10 +2602,14 @@ static inline int64_t tiles_upper_bound(int B, int T_len, int n_seqs, bool packe
     return ((int64_t)T_len + (int64_t)(kChunk - 1) * n_seqs) / kChunk;
 }
 
+// Workspace header: the packed sequences' chunk offsets (n_seqs + 1) and their
+// longest-first order (n_seqs), then the records.
+static inline size_t plan_bytes(int n_seqs) { return align256(sizeof(int32_t) * (size_t)(2 * n_seqs + 1)); }
+
 size_t chunk_workspace_bytes(int B, int T_len, int H, int n_seqs, bool packed, bool use_bf16) {
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
     const size_t rec = use_bf16 ? Rec<bf16>::bytes : Rec<float>::bytes;
-    return align256(sizeof(int32_t) * (size_t)(n_seqs + 1)) + rec * (size_t)tiles * H;
+    return plan_bytes(n_seqs) + rec * (size_t)tiles * H;
 }
 
 template <typename K>
@@ -2626,7 +2671,7 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
 template <int KD, int NT, int TPW, bool COPYW>
 static hipError_t launch_scan_wide(const void* q, const void* k, int64_t qks, const void* v,
                                    int64_t vs, const float* S0, float* Sf, void* o,
-                                   const int32_t* cu, const int32_t* offsets,
+                                   const int32_t* cu, const int32_t* offsets, const int32_t* order,
                                    const unsigned char* wsrec, int T_len, int H, int Hk, int N,
                                    hipStream_t stream)
 {
@@ -2640,19 +2685,21 @@ static hipError_t launch_scan_wide(const void* q, const void* k, int64_t qks, co
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * u8)), dim3(wide_block<NT, TPW, COPYW>()), smem,
                        stream, (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf,
-                       (bf16*)o, cu, offsets, wsrec, T_len, H, Hk, units);
+                       (bf16*)o, cu, offsets, order, wsrec, T_len, H, Hk, units);
     return hipGetLastError();
 }
 
 struct ChunkWs {
     int32_t* offsets;
+    int32_t* order;
     unsigned char* rec;
 };
 
 static inline ChunkWs carve(void* ws, int n_seqs) {
     ChunkWs w;
     w.offsets = (int32_t*)ws;
-    w.rec = (unsigned char*)ws + align256(sizeof(int32_t) * (size_t)(n_seqs + 1));
+    w.order = w.offsets + (n_seqs + 1);
+    w.rec = (unsigned char*)ws + plan_bytes(n_seqs);
     return w;
 }
 
@@ -2666,7 +2713,8 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
     const int64_t tiles = tiles_upper_bound(B, T_len, n_seqs, packed);
     const ChunkWs w = carve(ws, n_seqs);
     if (packed) {
-        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, w.offsets);
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, w.offsets,
+                           w.order);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -2690,6 +2738,17 @@ static hipError_t launch_prepare_t(const void* q, const void* k, int64_t qks, co
 // (shared staging) when there is parallelism to spare, else one (a 2-tile
 // instance does not get through the gfx950 backend). The tuning knob
 // overrides the choice with any value valid for the dtype.
+// Scan form for bf16 operands: whole-unit workgroups when the call has
+// enough (sequence, head) units to fill the chip twice over with one
+// workgroup each (their per-unit copies are a quarter of the column groups',
+// but a unit runs on one CU), else column groups. The knob overrides.
+constexpr int kWideMinUnits = 512;
+static inline bool scan_wide(int64_t units) {
+    const int f = tune_knob[kTuneScanForm];
+    if (f == 1 || f == 2) return f == 2;
+    return units >= kWideMinUnits;
+}
+
 static inline int scan_tiles(int64_t units, int slabs, bool bf16_ops) {
     const int k = tune_knob[kTuneScanTiles];
     if (bf16_ops) {
@@ -2713,13 +2772,15 @@ static hipError_t launch_scan_t(const void* q, const void* k, int64_t qks, const
     const int tiles = scan_tiles(units, slabs, sizeof(T) == 2);
     if constexpr (sizeof(T) == 2) {
         // bf16 operands: whole-unit workgroups when chosen, else the split-role step
-        if (tune_knob[kTuneScanForm] == 2) {
-            // (GDN_TUNE_SCAN_TILES = 2: two tiles per compute wave, else one)
-            if (V == 128 && tune_knob[kTuneScanTiles] == 2)
-                return launch_scan_wide<KD, 8, 2, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
+        if (scan_wide(units)) {
+            // V = 128: four compute waves of two tiles and a copy wave, or
+            // (GDN_TUNE_SCAN_TILES = 1) eight compute waves of one tile
+            // issuing the copies themselves; V = 64: four of one tile
+            if (V == 128 && tune_knob[kTuneScanTiles] == 1)
+                return launch_scan_wide<KD, 8, 1, false>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.order, w.rec, T_len, H, Hk, N, stream);
             if (V == 128)
-                return launch_scan_wide<KD, 8, 1, false>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
-            return launch_scan_wide<KD, 4, 1, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, N, stream);
+                return launch_scan_wide<KD, 8, 2, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.order, w.rec, T_len, H, Hk, N, stream);
+            return launch_scan_wide<KD, 4, 1, true>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.order, w.rec, T_len, H, Hk, N, stream);
         }
         if (tiles == 2)
             return launch_scan_roles<KD, 2>(q, k, qks, v, vs, S0, Sf, o, cu, w.offsets, w.rec, T_len, H, Hk, V, N, stream);

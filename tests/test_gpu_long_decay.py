@@ -23,8 +23,9 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda")
 BF16 = torch.bfloat16
 
-# scan schedules of the bf16 path (GDN_TUNE_SCAN_TILES): 0 = automatic
-SCHEDULES = [0, 1, 2]
+# scan schedules of the bf16 path (GDN_TUNE_SCAN_FORM, GDN_TUNE_SCAN_TILES):
+# automatic; column groups of one and two tiles; whole units (two tiles per wave)
+SCHEDULES = [(0, 0), (1, 1), (1, 2), (2, 0)]
 
 
 def _oracle(d):
@@ -59,7 +60,8 @@ def _run(gdn, d, entry):
 def _check_all(gdn, d, what):
     ro, rs = _oracle(d)
     for sched in SCHEDULES:
-        gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, sched)
+        gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, sched[0])
+        gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, sched[1])
         try:
             for entry in ("prefill", "chain"):
                 o, sf = _run(gdn, d, entry)
@@ -67,6 +69,7 @@ def _check_all(gdn, d, what):
                 assert_close(o, ro, BF16, f"{tag} o")
                 assert_close(sf, rs, BF16, f"{tag} state")
         finally:
+            gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, 0)
             gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, 0)
 
 

@@ -16,17 +16,21 @@ from tests.helpers import assert_close, to_np
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda")
 BF16 = torch.bfloat16
-FORMS = (1, 2)
+# (form, tiles): column groups; whole units with four compute waves of two
+# tiles and a copy wave; whole units with eight compute waves of one tile
+FORMS = ((1, 0), (2, 0), (2, 1))
 
 
 @pytest.fixture
 def form(gpu):
     yield gpu
     gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, 0)
+    gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, 0)
 
 
 def _run(gdn, d, f, **kw):
-    gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, f)
+    gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, f[0])
+    gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, f[1])
     t = {n: (None if d[n] is None else d[n].to(DEV)) for n in ("q", "k", "v", "g", "beta", "S0", "cu_seqlens")}
     o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["S0"],
                               cu_seqlens=t["cu_seqlens"], **kw)
@@ -58,7 +62,7 @@ def test_forms_equal_and_match_oracle(form, case):
     kw = dict(SMALL[case])
     d = wl.chunk_inputs(dtype=BF16, seed=hash(case) % 1000, **kw)
     print(f"scan forms: {case}", flush=True)
-    ref = _run(form, d, 1)
+    ref = _run(form, d, FORMS[0])
     ro, rs = _oracle(d)
     for f in FORMS:
         o, sf = _run(form, d, f)
@@ -74,11 +78,12 @@ def test_forms_scale_and_no_norm(form):
         x = d[n].float()
         d[n] = (x / x.norm(dim=-1, keepdim=True)).to(BF16)
     for kw in (dict(scale=128 ** -0.5), dict(qk_l2norm=False)):
-        ref = _run(form, d, 1, **kw)
+        ref = _run(form, d, FORMS[0], **kw)
         ro, rs = _oracle(d, scale=kw.get("scale", 1.0), l2norm=kw.get("qk_l2norm", True))
-        o, sf = _run(form, d, 2, **kw)
-        assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1]), kw
-        assert_close(to_np(o), ro, BF16, f"form=2 {kw} o")
+        for f in FORMS[1:]:
+            o, sf = _run(form, d, f, **kw)
+            assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1]), (kw, f)
+            assert_close(to_np(o), ro, BF16, f"form={f} {kw} o")
 
 
 @pytest.mark.parametrize("name", ["prefill", "gqa", "varlen"])
@@ -94,10 +99,12 @@ def test_forms_equal_full_size(form, name):
     cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].to(DEV)
     outs = []
     for f in FORMS:
-        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f)
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f[0])
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_TILES, f[1])
         o, sf = form.prefill_chain(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"],
                                    Hk=w.Hk, K=w.K, H=w.H, V=w.V, initial_state=S0, cu_seqlens=cu)
         torch.cuda.synchronize()
         outs.append((o, sf))
-    assert torch.equal(outs[0][0], outs[1][0]), f"{name}: o differs between forms"
-    assert torch.equal(outs[0][1], outs[1][1]), f"{name}: final state differs between forms"
+    for i in range(1, len(FORMS)):
+        assert torch.equal(outs[0][0], outs[i][0]), f"{name}: o differs, form {FORMS[i]}"
+        assert torch.equal(outs[0][1], outs[i][1]), f"{name}: final state differs, form {FORMS[i]}"
