@@ -2322,7 +2322,9 @@ void chunk_scan_wide_kernel(
     };
 
     if (COPYW && wave == kWideWaves) {
-        // ---------------- copy wave
+        // ---------------- copy wave: the copies of chunk c + 1 in step c (an L2
+        // prefetch of later chunks from this wave measured slower: its one-line
+        // loads congest the CU's vector-memory pipe)
         issue(0);
         wait_vmcnt<0>();
         lds_barrier();
@@ -2393,7 +2395,13 @@ void chunk_scan_wide_kernel(
             return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 
-        // ---- operands of X (row tiles 0, 1), the values and the factor a
+        // Each phase's LDS operands are requested in the phase before it, and
+        // each phase carries VALU work that does not depend on its own matrix
+        // ops, so the two overlap: the state decay and the value conversion
+        // beside X, U's operand packing beside Y, the outputs' packing and
+        // stores and the next step's state operands beside the h' products.
+
+        // ---- operands of X (row tiles 0, 1), the values, a and gamma_L
         Frag ka[2][KB], kb2[2][KB];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -2407,9 +2415,11 @@ void chunk_scan_wide_kernel(
         f32x4 fa[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) fa[rt] = fac4(0, rt);
+        const float gL = ld<float>(rec + RC::fac + 3 * kChunk * 4);
         SCAN_FENCE();
 
-        // ---- X = K h, row tiles 0, 1 (loads: K row tiles 2, 3 and T)
+        // ---- X = K h, row tiles 0, 1 (loads: K row tiles 2, 3 and T; VALU:
+        // the first half of the decayed state gamma_L h, the accumulator of h')
         f32x4 X[TPW][4];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -2426,9 +2436,14 @@ void chunk_scan_wide_kernel(
         Frag tfr[kTriFrags];
 #pragma unroll
         for (int f = 0; f < kTriFrags; ++f) tfr[f] = ld<Frag>(rec + RC::tfrag + (f * kWave + lane) * RC::frag_bytes);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int rt = 0; rt < RT / 2; ++rt) hs[t][rt] *= gL;
         SCAN_FENCE();
 
-        // ---- X, row tiles 2, 3 (loads: Q row tiles 0, 1)
+        // ---- X, row tiles 2, 3 (loads: Q row tiles 0, 1; VALU: the other
+        // half of gamma_L h, the values to fp32)
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -2441,6 +2456,10 @@ void chunk_scan_wide_kernel(
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) ka[r][kb] = row_frag(qt, r, kb);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int rt = RT / 2; rt < RT; ++rt) hs[t][rt] *= gL;
         SCAN_FENCE();
 
         // ---- U = T (V - a o X) (loads: Q row tiles 2, 3)
@@ -2465,7 +2484,7 @@ void chunk_scan_wide_kernel(
             for (int kb = 0; kb < KB; ++kb) kb2[r][kb] = row_frag(qt, 2 + r, kb);
         SCAN_FENCE();
 
-        // ---- Y^T = h^T Q^T, row tiles 0, 1, then 2, 3 (loads: P, b, c, gamma_L)
+        // ---- Y^T = h^T Q^T, row tiles 0, 1 (loads: b, c)
         f32x4 Y[TPW][4];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -2475,13 +2494,16 @@ void chunk_scan_wide_kernel(
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) Y[t][r] = MT::mma(hf[t][kb], ka[r][kb], Y[t][r]);
             }
-        Frag pfr[kTriFrags];
-#pragma unroll
-        for (int f = 0; f < kTriFrags; ++f) pfr[f] = ld<Frag>(rec + RC::pfrag + (f * kWave + lane) * RC::frag_bytes);
         float fb[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) fb[rt] = ld<float>(rec + RC::fac + (1 * kChunk + 16 * rt + col) * 4);
+        f32x4 fc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) fc[rt] = fac4(2, rt);
         SCAN_FENCE();
+
+        // ---- Y^T, row tiles 2, 3 (loads: P; VALU: the operands of U and of
+        // c o U, b o Y^T of row tiles 0, 1)
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -2490,40 +2512,69 @@ void chunk_scan_wide_kernel(
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) Y[t][2 + r] = MT::mma(hf[t][kb], kb2[r][kb], Y[t][2 + r]);
             }
-        f32x4 fc[4];
+        Frag pfr[kTriFrags];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) fc[rt] = fac4(2, rt);
-        const float gL = ld<float>(rec + RC::fac + 3 * kChunk * 4);
-        SCAN_FENCE();
-
-        // ---- O^T = b o Y^T + U^T P^T; c o U (loads: K^T of state tiles 0, 1)
+        for (int f = 0; f < kTriFrags; ++f) pfr[f] = ld<Frag>(rec + RC::pfrag + (f * kWave + lane) * RC::frag_bytes);
+        Frag uf[TPW][2], df[TPW][2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const Frag uf0 = MT::acc_frag(U[t][0], U[t][1]);
-            const Frag uf1 = MT::acc_frag(U[t][2], U[t][3]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                Y[t][rt] = MT::mma(uf0, pfr[tri_frag(rt, 0)], Y[t][rt] * fb[rt]);
-                if (rt >= 2) Y[t][rt] = MT::mma(uf1, pfr[tri_frag(rt, 1)], Y[t][rt]);
-            }
-        }
-        Frag df[TPW][2];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
+            uf[t][0] = MT::acc_frag(U[t][0], U[t][1]);
+            uf[t][1] = MT::acc_frag(U[t][2], U[t][3]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) U[t][rt] *= fc[rt];
             df[t][0] = MT::acc_frag(U[t][0], U[t][1]);
             df[t][1] = MT::acc_frag(U[t][2], U[t][3]);
+            Y[t][0] *= fb[0];
+            Y[t][1] *= fb[1];
         }
+        SCAN_FENCE();
+
+        // ---- O^T = b o Y^T + U^T P^T (loads: K^T of state tiles 0, 1)
         Frag ktf[2][2][2];   // [pair parity][tile of the pair][half]
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int half = 0; half < 2; ++half) ktf[0][i][half] = kt_frag(i, half);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Y[t][rt] = MT::mma(uf[t][0], pfr[tri_frag(rt, 0)], rt >= 2 ? Y[t][rt] * fb[rt] : Y[t][rt]);
+                if (rt >= 2) Y[t][rt] = MT::mma(uf[t][1], pfr[tri_frag(rt, 1)], Y[t][rt]);
+            }
+        }
         SCAN_FENCE();
 
         // ---- h' = gamma_L h + K^T (c o U), two state tiles at a time, the K^T
-        // operands of the next two requested before the current products
+        // operands of the next two requested before the current products; the
+        // outputs packed and stored, and the next step's state operands built,
+        // beside them
+        const int tok0 = tok_begin + c * kChunk;
+        const uint32_t L = (uint32_t)min(kChunk, tok_end - tok0);
+        const rsrc_t ro = make_rsrc(o + (int64_t)tok0 * HV + (int64_t)h * V + 16 * TPW * wave, L * o_row);
+        auto store_rows = [&](int rt) {
+            if constexpr (TPW == 2) {
+                // lane swaps give lane (g, c) the wave's columns 8 g .. + 7 of row c
+                const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[0][rt], bf16x4));
+                const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[1][rt], bf16x4));
+                u32x4 sv;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+                    const auto w16 = __builtin_amdgcn_permlane16_swap(w32[0], w32[1], false, false);
+                    sv[d] = w16[0];
+                    sv[2 + d] = w16[1];
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(sv, ro, (uint32_t)(16 * rt + col) * o_row + 16 * grp, 0, 0);
+            } else {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const bf16x4 ob = __builtin_convertvector(Y[t][rt], bf16x4);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
+                                                          (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
+                }
+            }
+        };
 #pragma unroll
         for (int rp = 0; rp < RT / 2; ++rp) {
             if (rp + 1 < RT / 2) {
@@ -2538,45 +2589,20 @@ void chunk_scan_wide_kernel(
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const int rt = 2 * rp + i;
-                    f32x4 acc = hs[t][rt] * gL;
-                    acc = MT::mma(ktf[rp & 1][i][0], df[t][0], acc);
+                    const f32x4 acc = MT::mma(ktf[rp & 1][i][0], df[t][0], hs[t][rt]);
                     hs[t][rt] = MT::mma(ktf[rp & 1][i][1], df[t][1], acc);
                 }
+            if (rp < 4) store_rows(rp);
+            if (rp >= 1) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) hf[t][rp - 1] = state_frag_bf16(hs[t][2 * rp - 2], hs[t][2 * rp - 1], grp);
+            }
             SCAN_FENCE();
         }
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int rt = RT / 2; rt < 4; ++rt) store_rows(rt);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) hf[t][kb] = state_frag_bf16(hs[t][2 * kb], hs[t][2 * kb + 1], grp);
-
-        // ---- the chunk's outputs
-        const int tok0 = tok_begin + c * kChunk;
-        const uint32_t L = (uint32_t)min(kChunk, tok_end - tok0);
-        const rsrc_t ro = make_rsrc(o + (int64_t)tok0 * HV + (int64_t)h * V + 16 * TPW * wave, L * o_row);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            if constexpr (TPW == 2) {
-                // lane swaps give lane (g, c) the wave's columns 8 g .. + 7 of row c
-                const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[0][rt], bf16x4));
-                const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(Y[1][rt], bf16x4));
-                u32x4 s;
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const auto w32 = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
-                    const auto w16 = __builtin_amdgcn_permlane16_swap(w32[0], w32[1], false, false);
-                    s[d] = w16[0];
-                    s[2 + d] = w16[1];
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(s, ro, (uint32_t)(16 * rt + col) * o_row + 16 * grp, 0, 0);
-            } else {
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const bf16x4 ob = __builtin_convertvector(Y[t][rt], bf16x4);
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
-                                                          (uint32_t)(16 * rt + col) * o_row + (16 * t + 4 * grp) * 2, 0, 0);
-                }
-            }
-        }
+        for (int t = 0; t < TPW; ++t) hf[t][KB - 1] = state_frag_bf16(hs[t][RT - 2], hs[t][RT - 1], grp);
         if constexpr (!COPYW) wait_vmcnt<0>();   // this wave's copies of chunk c + 1 (and its stores)
         lds_barrier();   // every wave is done with this buffer; chunk c + 1 has landed
     }
