@@ -2231,27 +2231,54 @@ struct WideCopies {
     }
 };
 
-// compute waves of a unit of NT column tiles with TPW tiles each; with
-// COPYW a copy wave comes after them
+// Whole-prefill form (CONV): the K and Q tiles and the record of a chunk in
+// two buffers, its value slabs in a ring of three (a slab is copied raw two
+// chunks ahead and convolved in place one chunk ahead).
+template <int KD>
+struct WideKQR {
+    unsigned char k[kChunk * KD * 2];
+    unsigned char q[kChunk * KD * 2];
+    unsigned char rec[Rec<bf16>::bytes];
+};
+template <int NT>
+struct WideVal {
+    unsigned char v[NT][kChunk * 32];
+};
+template <int KD, int NT, bool CONV>
+constexpr size_t wide_lds_bytes() {
+    return CONV ? 2 * sizeof(WideKQR<KD>) + 3 * sizeof(WideVal<NT>) : 2 * sizeof(WideBuf<KD, NT>);
+}
+
+// compute waves of a unit of NT column tiles with TPW tiles each; after them
+// a copy wave (COPYW), or (CONV) four auxiliary waves that issue the copies
+// and convolve the values, one per compute wave
 template <int NT, int TPW>
 constexpr int wide_waves() { return NT / TPW; }
-template <int NT, int TPW, bool COPYW>
-constexpr int wide_block() { return (wide_waves<NT, TPW>() + (COPYW ? 1 : 0)) * kWave; }
+template <int NT, int TPW, bool COPYW, bool CONV>
+constexpr int wide_block() { return (wide_waves<NT, TPW>() + (CONV ? 4 : COPYW ? 1 : 0)) * kWave; }
 
-template <int KD, int NT, int TPW, bool COPYW>
-__global__ __launch_bounds__((wide_block<NT, TPW, COPYW>()))
-__attribute__((amdgpu_waves_per_eu((wide_block<NT, TPW, COPYW>() / kWave + 3) / 4,
-                                   (wide_block<NT, TPW, COPYW>() / kWave + 3) / 4)))
+// CONV (whole-prefill form): qp points at the blocked convolved q / k rows
+// of the per-chunk solve ([q, k][32-column slice][64 rows][64 B] per (chunk,
+// key head)), vp at the raw value rows, wv / bv at the value channels' taps
+// and bias (bv may be null).
+template <int KD, int NT, int TPW, bool COPYW, bool CONV>
+__global__ __launch_bounds__((wide_block<NT, TPW, COPYW, CONV>()))
+__attribute__((amdgpu_waves_per_eu((wide_block<NT, TPW, COPYW, CONV>() / kWave + 3) / 4,
+                                   (wide_block<NT, TPW, COPYW, CONV>() / kWave + 3) / 4)))
 void chunk_scan_wide_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, int64_t qk_stride,
     const bf16* __restrict__ vp, int64_t v_stride,
     const float* __restrict__ S0, float* __restrict__ Sfin, bf16* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ order,
-    const unsigned char* __restrict__ ws_rec, int T_len, int H, int Hk, int units)
+    const unsigned char* __restrict__ ws_rec, int T_len, int H, int Hk, int units,
+    const bf16* __restrict__ wv, const bf16* __restrict__ bv)
 {
     typedef WideBuf<KD, NT> WB;
+    typedef WideKQR<KD> KQR;
+    typedef WideVal<NT> WV;
     constexpr int kWideWaves = wide_waves<NT, TPW>();
+    static_assert(!CONV || kWideWaves == 4, "one auxiliary wave per compute wave");
     typedef Mma<bf16> MT;
     typedef bf16x8 Frag;
     typedef Rec<bf16> RC;
@@ -2260,6 +2287,8 @@ void chunk_scan_wide_kernel(
     constexpr int RT = KD / 16;
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     WB* bufs = reinterpret_cast<WB*>(smem_raw);
+    KQR* kqrs = reinterpret_cast<KQR*>(smem_raw);
+    WV* vring = reinterpret_cast<WV*>(smem_raw + 2 * sizeof(KQR));
 
     // Dense batches: XCD-aware order, the value heads that share a q/k head run
     // on one XCD (blockIdx % 8), one after another, so their K and Q rows come
@@ -2294,7 +2323,7 @@ void chunk_scan_wide_kernel(
     // them at zero so they hold finite values (their factors are zero).
     if ((tok_end - tok_begin) % kChunk != 0) {
         const f32x4 z = zero4();
-        for (int i = threadIdx.x * 16; i < 2 * (int)sizeof(WB); i += wide_block<NT, TPW, COPYW>() * 16)
+        for (int i = threadIdx.x * 16; i < (int)wide_lds_bytes<KD, NT, CONV>(); i += wide_block<NT, TPW, COPYW, CONV>() * 16)
             *reinterpret_cast<f32x4*>(smem_raw + i) = z;
         lds_barrier();
     }
@@ -2309,7 +2338,7 @@ void chunk_scan_wide_kernel(
     const uint64_t rstep = (uint64_t)H * RC::bytes;
     constexpr int NW = COPYW ? 1 : kWideWaves;
     WideCopies<KD, NT, NW> cp;
-    if (!COPYW || wave == kWideWaves) cp.init(COPYW ? 0 : wave, lane, qk_row, v_row);
+    if (!CONV && (!COPYW || wave == kWideWaves)) cp.init(COPYW ? 0 : wave, lane, qk_row, v_row);
     auto issue = [&](int c) {
         const bool valid = c < nchunks;
         const int cc = valid ? c : 0;
@@ -2320,6 +2349,134 @@ void chunk_scan_wide_kernel(
                  make_rsrc((const void*)(v0 + (uint64_t)cc * kChunk * v_row), L * v_row),
                  make_rsrc((const void*)(r0 + (uint64_t)cc * rstep), valid ? (uint32_t)RC::bytes : 0u));
     };
+
+    if (CONV && wave >= kWideWaves) {
+        // ---------------- auxiliary wave a: a quarter of the copies (K, Q and
+        // record of chunk c + 1, raw values of chunk c + 2) and the
+        // convolution of compute wave a's value slabs of chunk c + 1, in step c
+        const int a = wave - kWideWaves;
+        constexpr uint32_t tb = qk_block_bytes<KD>();
+        constexpr int TPc = kChunk * KD * 2 / 1024;           // pieces of a K / Q tile
+        constexpr int RPc = Rec<bf16>::bytes / 1024;
+        constexpr int VPc = NT * 2;                            // value pieces (2 per slab)
+        constexpr int total = 2 * TPc + RPc + VPc;
+        constexpr int per = (total + 3) / 4;
+        constexpr int SPR = KD * 2 / 16, RPI = 1024 / (KD * 2);
+        const uint64_t qb0 = (uint64_t)qp + ((uint64_t)tile0 * Hk + hk) * 2 * tb;   // chunk 0's q block
+        const uint64_t kqstep = (uint64_t)Hk * 2 * tb;
+        uint32_t src[per], dst[per];
+        int ten[per];   // 0 K, 1 Q, 2 record, 3 values, 4 none
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            const int pc = a + 4 * i;
+            int t = 4, j = 0;
+            if (pc < TPc) { t = 0; j = pc; }
+            else if (pc < 2 * TPc) { t = 1; j = pc - TPc; }
+            else if (pc < 2 * TPc + RPc) { t = 2; j = pc - 2 * TPc; }
+            else if (pc < total) { t = 3; j = pc - 2 * TPc - RPc; }
+            ten[i] = t;
+            if (t <= 1) {
+                // (blocked: logical segment sg of a row is segment sg % 4 of slice sg / 4)
+                const int row = j * RPI + lane / SPR;
+                const int sg = (lane % SPR) ^ tile_mask<bf16, KD, 1>(row);
+                src[i] = (uint32_t)((sg >> 2) * (kChunk * 64) + row * 64 + (sg & 3) * 16);
+                dst[i] = (t == 0 ? offsetof(KQR, k) : offsetof(KQR, q)) + j * 1024;
+            } else if (t == 2) {
+                src[i] = (uint32_t)j * 1024 + lane * 16;
+                dst[i] = offsetof(KQR, rec) + j * 1024;
+            } else {
+                const int row = 32 * (j & 1) + lane / 2;
+                src[i] = (uint32_t)row * v_row + (uint32_t)(j >> 1) * 32 + (uint32_t)(lane & 1) * 16;
+                dst[i] = (uint32_t)(j >> 1) * (kChunk * 32) + (j & 1) * 1024;
+            }
+        }
+        auto chunk_rows = [&](int c) {
+            return c < nchunks ? (uint32_t)min(kChunk, tok_end - (tok_begin + c * kChunk)) : 0u;
+        };
+        // K, Q and record of chunk c into kqrs[c % 2], values of chunk cv into vring[cv % 3]
+        auto issue_aux = [&](int c, int cv, bool kqr, bool val) {
+            const bool valid = c < nchunks;
+            const int cc = valid ? c : 0;
+            const uint64_t qb = qb0 + (uint64_t)cc * kqstep;
+            const rsrc_t rq = make_rsrc((const void*)qb, valid ? tb : 0u);
+            const rsrc_t rk = make_rsrc((const void*)(qb + tb), valid ? tb : 0u);
+            const rsrc_t rr = make_rsrc((const void*)(r0 + (uint64_t)cc * rstep), valid ? (uint32_t)RC::bytes : 0u);
+            const int cvv = cv < nchunks ? cv : 0;
+            const rsrc_t rv = make_rsrc((const void*)(v0 + (uint64_t)cvv * kChunk * v_row), chunk_rows(cv) * v_row);
+            unsigned char* kb_ = reinterpret_cast<unsigned char*>(&kqrs[c & 1]);
+            unsigned char* vb_ = reinterpret_cast<unsigned char*>(&vring[cv % 3]);
+#pragma unroll
+            for (int i = 0; i < per; ++i) {
+                const int t = ten[i];
+                if (t <= 2 && kqr) dma16(t == 0 ? rk : t == 1 ? rq : rr, kb_ + dst[i], src[i], 0);
+                if (t == 3 && val) dma16(rv, vb_ + dst[i], src[i], 0);
+            }
+        };
+        // the taps and bias of this lane's column in each of compute wave a's tiles
+        ColTaps cv[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int64_t chn = (int64_t)h * V + 16 * (TPW * a + t) + col;
+            const u32x2 tw = *reinterpret_cast<const u32x2*>(wv + chn * 4);
+            cv[t].w01 = tw[0];
+            cv[t].w23 = tw[1];
+            cv[t].b = bv ? (float)bv[chn] : 0.f;
+        }
+        // raw rows 60 .. 63 of the previous chunk per tile (as lane group 3 holds
+        // them; zero before the sequence's first chunk)
+        u32x2 prev[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) prev[t] = u32x2{0u, 0u};
+        const uint32_t vtr_a = (uint32_t)((4 * grp + (col >> 2)) * 32 + (col & 3) * 8);
+        const int from = (48 + col) * 4;   // byte index of lane (3, col) for ds_bpermute
+        // the value slabs of chunk cc, in place: every row tile read (x: its 16
+        // rows; p: the 4 rows before them) before any is written
+        auto convert = [&](int cc) {
+            if (cc >= nchunks) return;
+            WV* __restrict__ vb = &vring[cc % 3];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                unsigned char* slab = vb->v[TPW * a + t];
+                u32x2 xs[4], ps[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned char* xa = slab + vtr_a + i * 16 * 32;
+                    xs[i] = __builtin_bit_cast(u32x2, lds_read_tr16(xa));
+                    ps[i] = __builtin_bit_cast(u32x2, lds_read_tr16(i == 0 && grp == 0 ? xa : xa - 4 * 32));
+                }
+                u32x2 halo;
+                halo[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)prev[t][0]);
+                halo[1] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)prev[t][1]);
+                if (grp == 0) ps[0] = halo;
+                prev[t] = xs[3];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 x = xs[i], pp = ps[i];
+                    const uint32_t p12 = pair_mid(pp[0], pp[1]), p3x0 = pair_mid(pp[1], x[0]);
+                    const uint32_t x12 = pair_mid(x[0], x[1]);
+                    f32x4 y;
+                    y[0] = conv_silu(conv_taps4_bf16(cv[t].w01, cv[t].w23, cv[t].b, p12, p3x0));
+                    y[1] = conv_silu(conv_taps4_bf16(cv[t].w01, cv[t].w23, cv[t].b, pp[1], x[0]));
+                    y[2] = conv_silu(conv_taps4_bf16(cv[t].w01, cv[t].w23, cv[t].b, p3x0, x12));
+                    y[3] = conv_silu(conv_taps4_bf16(cv[t].w01, cv[t].w23, cv[t].b, x[0], x[1]));
+                    *reinterpret_cast<bf16x4*>(conv_slot(slab, i, lane)) = __builtin_convertvector(y, bf16x4);
+                }
+            }
+        };
+        issue_aux(0, 0, true, true);
+        issue_aux(0, 1, false, true);
+        wait_vmcnt<0>();
+        lds_barrier();
+        convert(0);
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            issue_aux(c + 1, c + 2, true, true);
+            convert(c + 1);
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
+        return;
+    }
 
     if (COPYW && wave == kWideWaves) {
         // ---------------- copy wave: the copies of chunk c + 1 in step c (an L2
@@ -2370,18 +2527,36 @@ void chunk_scan_wide_kernel(
 
     const int64_t HV = (int64_t)H * V;
     const uint32_t o_row = (uint32_t)(HV * 2);
-    if constexpr (!COPYW) {
+    if constexpr (!COPYW && !CONV) {
         issue(0);
         wait_vmcnt<0>();
     }
     lds_barrier();   // chunk 0 has landed
+    if constexpr (CONV) lds_barrier();   // chunk 0's values are convolved
 
+    int vslot = 0;   // CONV: the value ring slot of chunk c
     for (int c = 0; c < nchunks; ++c) {
-        if constexpr (!COPYW) issue(c + 1);
-        const WB* __restrict__ cur = &bufs[c & 1];
-        const unsigned char* kt = cur->k;
-        const unsigned char* qt = cur->q;
-        const unsigned char* rec = cur->rec;
+        if constexpr (!COPYW && !CONV) issue(c + 1);
+        const unsigned char* kt;
+        const unsigned char* qt;
+        const unsigned char* rec;
+        const unsigned char* vsl[TPW];
+        if constexpr (CONV) {
+            const KQR* __restrict__ cur = &kqrs[c & 1];
+            kt = cur->k;
+            qt = cur->q;
+            rec = cur->rec;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) vsl[t] = vring[vslot].v[TPW * wave + t];
+            vslot = vslot == 2 ? 0 : vslot + 1;
+        } else {
+            const WB* __restrict__ cur = &bufs[c & 1];
+            kt = cur->k;
+            qt = cur->q;
+            rec = cur->rec;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) vsl[t] = cur->v[TPW * wave + t];
+        }
         auto row_frag = [&](const unsigned char* tile, int rt, int kb) -> Frag {
             return ld<Frag>(tile + rf[kb] + 16 * rt * WB::RB);
         };
@@ -2411,7 +2586,11 @@ void chunk_scan_wide_kernel(
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) vraw[t][rt] = lds_read_tr16(cur->v[TPW * wave + t] + vtr + rt * 16 * WB::VRB);
+            for (int rt = 0; rt < 4; ++rt) {
+                // (CONV: convolved in place in this lane's operand order)
+                if constexpr (CONV) vraw[t][rt] = ld<s16x4>(conv_slot(vsl[t], rt, lane));
+                else vraw[t][rt] = lds_read_tr16(vsl[t] + vtr + rt * 16 * WB::VRB);
+            }
         f32x4 fa[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) fa[rt] = fac4(0, rt);
@@ -2603,7 +2782,7 @@ void chunk_scan_wide_kernel(
         for (int rt = RT / 2; rt < 4; ++rt) store_rows(rt);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) hf[t][KB - 1] = state_frag_bf16(hs[t][RT - 2], hs[t][RT - 1], grp);
-        if constexpr (!COPYW) wait_vmcnt<0>();   // this wave's copies of chunk c + 1 (and its stores)
+        if constexpr (!COPYW && !CONV) wait_vmcnt<0>();   // this wave's copies of chunk c + 1 (and its stores)
         lds_barrier();   // every wave is done with this buffer; chunk c + 1 has landed
     }
 
@@ -2694,24 +2873,25 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
     return hipGetLastError();
 }
 
-template <int KD, int NT, int TPW, bool COPYW>
+template <int KD, int NT, int TPW, bool COPYW, bool CONV = false>
 static hipError_t launch_scan_wide(const void* q, const void* k, int64_t qks, const void* v,
                                    int64_t vs, const float* S0, float* Sf, void* o,
                                    const int32_t* cu, const int32_t* offsets, const int32_t* order,
                                    const unsigned char* wsrec, int T_len, int H, int Hk, int N,
-                                   hipStream_t stream)
+                                   hipStream_t stream, const void* wv = nullptr,
+                                   const void* bv = nullptr)
 {
     const int units = N * H;
     const int u8 = (units + 7) / 8;
-    typedef WideBuf<KD, NT> WB;
-    constexpr size_t smem = 2 * sizeof(WB);
+    constexpr size_t smem = wide_lds_bytes<KD, NT, CONV>();
     static_assert(smem <= 160 * 1024, "wide scan staging fits in LDS");
-    auto kern = chunk_scan_wide_kernel<KD, NT, TPW, COPYW>;
+    auto kern = chunk_scan_wide_kernel<KD, NT, TPW, COPYW, CONV>;
     hipError_t err = set_smem(kern, smem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * u8)), dim3(wide_block<NT, TPW, COPYW>()), smem,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * u8)), dim3(wide_block<NT, TPW, COPYW, CONV>()), smem,
                        stream, (const bf16*)q, (const bf16*)k, qks, (const bf16*)v, vs, S0, Sf,
-                       (bf16*)o, cu, offsets, order, wsrec, T_len, H, Hk, units);
+                       (bf16*)o, cu, offsets, order, wsrec, T_len, H, Hk, units, (const bf16*)wv,
+                       (const bf16*)bv);
     return hipGetLastError();
 }
 
@@ -2885,6 +3065,15 @@ static hipError_t launch_prefill_scan_t(const bf16* x, int64_t xs, const bf16* c
     const int slabs = V / 16;
     const bf16* wv = cw + 2 * qkc * 4;
     const bf16* bv = cb ? cb + 2 * qkc : nullptr;
+    if (scan_wide((int64_t)N * H)) {
+        if (V == 128)
+            return launch_scan_wide<KD, 8, 2, false, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu,
+                                                           w.offsets, w.order, w.rec, T_len, H, Hk, N,
+                                                           stream, wv, bv);
+        return launch_scan_wide<KD, 4, 1, false, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu,
+                                                       w.offsets, w.order, w.rec, T_len, H, Hk, N,
+                                                       stream, wv, bv);
+    }
     if (scan_tiles((int64_t)N * H, slabs, true) == 2)
         return launch_scan_roles<KD, 2, true>(qk, qk, 0, x + 2 * qkc, xs, S0, Sf, o, cu, w.offsets,
                                               w.rec, T_len, H, Hk, V, N, stream, wv, bv);

@@ -4,7 +4,9 @@ head) unit over all its value columns (2). The form only reschedules the
 same arithmetic: both must give the same bits on every shape, and each is
 checked against the fp64 oracle directly on the small shapes (head dims,
 GQA, ragged and packed lengths, an initial state, scale, no normalisation)
-and at the workloads' full sizes on sampled units."""
+and at the workloads' full sizes on sampled units. The whole prefill's scan
+(which also convolves the value rows) has both forms too: each must equal
+the conv1d -> gates -> chunk_fwd chain bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -108,3 +110,34 @@ def test_forms_equal_full_size(form, name):
     for i in range(1, len(FORMS)):
         assert torch.equal(outs[0][0], outs[i][0]), f"{name}: o differs, form {FORMS[i]}"
         assert torch.equal(outs[0][1], outs[i][1]), f"{name}: final state differs, form {FORMS[i]}"
+
+
+# whole prefill (gdn_prefill): the scan also convolves the value rows; both
+# forms must equal the conv1d -> gates -> chunk_fwd chain bit for bit
+@pytest.mark.parametrize("case", ["prefill-321", "gqa-700", "varlen-edges", "k64-v128",
+                                  "k128-v64", "k64-v64"])
+def test_forms_whole_prefill_equal_chain(form, case):
+    from tests.test_gpu_prefill import SMALL as PSMALL, _bias, _chain, _fused, _equal
+    w, kw = PSMALL[case]
+    d = wl.prefill_inputs(w, **kw)
+    print(f"scan forms, whole prefill: {case}", flush=True)
+    bias = _bias(d["C"])
+    ref = _chain(form, d)
+    refb = _chain(form, d, bias=bias, scale=0.125)
+    for f in FORMS[:2]:
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f[0])
+        _equal(_fused(form, d), ref, f"{case} form={f}")
+        _equal(_fused(form, d, bias=bias, scale=0.125), refb, f"{case} form={f} bias, scale")
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, 0)
+
+
+@pytest.mark.parametrize("name", ["prefill", "gqa", "varlen"])
+def test_forms_whole_prefill_full_size(form, name):
+    from tests.test_gpu_prefill import _chain, _fused, _equal
+    d = wl.prefill_inputs(wl.WORKLOADS[name])
+    print(f"scan forms, whole prefill full size: {name}", flush=True)
+    ref = _chain(form, d)
+    for f in FORMS[:2]:
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f[0])
+        _equal(_fused(form, d), ref, f"{name} form={f}")
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, 0)
