@@ -63,7 +63,7 @@ KERNELS = {
     "c1": {"conv1d": ("conv1d_causal_kernel<float, 16, 256>", CSRC + "conv1d.hip"),
            "gate_prepare": ("gate_prepare_kernel<float>", CSRC + "gate.hip"),
            "chunk_prepare": ("chunk_prep_kernel<float, 64, false, false>", _CHUNK),
-           "chunk_scan": ("chunk_scan_kernel<float, 64, 1, 3>", _CHUNK)},
+           "chunk_scan": ("chunk_scan_kernel<float, 64, 1, 2>", _CHUNK)},
     "c2": {"prefill_prepare": (_PREP, _CHUNK),
            "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
            "conv1d": ("conv1d_causal_kernel<bf16, 16, 256>", CSRC + "conv1d.hip"),
@@ -75,9 +75,9 @@ KERNELS = {
            "chunk_prepare": (_CPREP, _CHUNK),
            "chunk_scan": ("chunk_scan_roles_kernel<128, 1, 3, false>", _CHUNK)},
     "c4": {"prefill_prepare": (_PREP, _CHUNK),
-           "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
+           "prefill_scan": ("chunk_scan_wide_kernel<128, 8, 2, false, true>", _CHUNK),
            "chunk_prepare": (_CPREP, _CHUNK),
-           "chunk_scan": ("chunk_scan_roles_kernel<128, 2, 3, false>", _CHUNK)},
+           "chunk_scan": ("chunk_scan_wide_kernel<128, 8, 2, true, false>", _CHUNK)},
     "c5": {"decode": ("gdp_decode_kernel<bf16, 128, 128>", CSRC + "decode.hip"),
            "conv1d_update": ("conv1d_update_kernel<bf16>", CSRC + "gdp.hip"),
            "decode_prepare": ("gdp_decode_prepare_kernel<bf16>", CSRC + "gdp.hip")},
@@ -241,16 +241,15 @@ def iter_stats(fn, torch, stream, iters, flush=None):
 def timed_ops(torch, stream, calls, steps, warmup):
     """calls: list of (op, fn). `warmup` untimed passes, then `steps` timed
     passes with nothing else on the stream (wall time per pass, us, between
-    two synchronisations), then `steps` more with HIP events between the
-    calls (each op's duration; an event between two kernels leaves a gap of a
-    few microseconds, so these passes are not the ones the pass time comes from)."""
-    def run(evs=None):
-        for j, (_, fn) in enumerate(calls):
-            if evs:
-                evs[j].record(stream)
+    two synchronisations). Each op's launch duration is then timed on its own:
+    a spin kernel holds the stream while the host queues `steps` launches of
+    the op, and HIP events before and after them give the average per launch
+    (back to back, as in the passes; one event pair per op keeps the events'
+    own gaps out of the average). Every op may be repeated: each reads the
+    previous ops' outputs and rewrites its own."""
+    def run():
+        for _, fn in calls:
             fn()
-        if evs:
-            evs[-1].record(stream)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -259,15 +258,24 @@ def timed_ops(torch, stream, calls, steps, warmup):
         run()
     torch.cuda.synchronize()
     pass_us = (time.perf_counter() - t0) * 1e6 / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        run(evs[i])
-    torch.cuda.synchronize()
-    op_us = {op: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1e3
-             for j, (op, _) in enumerate(calls)}
+    op_us = {op: repeated_us(torch, stream, fn, steps) for op, fn in calls}
     return pass_us, op_us, run
+
+
+def repeated_us(torch, stream, fn, reps):
+    """Average duration (us) of `reps` back-to-back launches of fn, timed with
+    HIP events on the launch stream behind a spin kernel (so the host's call
+    overhead does not leave the GPU idle between the launches)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(reps * 300000))   # over 100 us of spinning per queued launch
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
 
 
 def copy_peak(torch, dev, stream):
@@ -626,17 +634,20 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
     lines = [f"# Kernel times, {w} workload ({part}) (rocprofv3 --kernel-trace --stats)", "",
              f"Command: `{command}`", "",
              "One line per kernel and launch shape (grid = work-items), from the kernel trace.", "",
-             "| kernel | grid | workgroup | calls | average (us) | min (us) | max (us) | share |",
-             "|---|---|---|---|---|---|---|---|"]
+             "| kernel | grid | workgroup | calls | average (us) | median (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for (name, grid, wg), d in items:
-        lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | "
+        med = sorted(d)[len(d) // 2]
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | {med:.2f} | "
                      f"{min(d):.2f} | {max(d):.2f} | {100 * sum(d) / total:.1f}% |")
+    lines += ["", "(`at::cuda::` rows are the spin kernels that hold the stream while the host",
+              "queues the repeated launches of one op; the calls include the warm-up passes.)"]
     if bench_log:
         js = [ln for ln in open(bench_log) if ln.startswith("{")]
         b = json.loads(js[-1])
         cfg = b.get("configs", {}).get(part, {})
-        lines += ["", "The same run's bench figures (HIP events on the launch stream, averaged",
-                  "over the timed passes), for comparison with the trace averages above:", ""]
+        lines += ["", "The same run's bench figures (HIP events on the launch stream around",
+                  "back-to-back repeated launches of each op), for comparison with the trace above:", ""]
         for op, k in cfg.get("kernels", {}).items():
             lines.append(f"- {op} (`{k['kernel']}`): {k['us']:.2f} us")
         if "decode" in cfg:
