@@ -9,7 +9,11 @@ automatic setting (a knob changes scheduling only), and they are timed with
 HIP events on the stream they run on.
 
 Knobs swept:
-  GDN_TUNE_SCAN_TILES    value-column tiles per scan workgroup (BV = 16 x tiles)
+  GDN_TUNE_SCAN_FORM     bf16 scan workgroup form: value-column groups with
+                         role-split waves (1) or one workgroup per (sequence,
+                         head) unit (2), swept together with
+  GDN_TUNE_SCAN_TILES    value-column tiles per scan workgroup (BV = 16 x tiles),
+                         per compute wave in the whole-unit form
   GDN_TUNE_CONV_RUN      tokens per thread of the prefill conv
   GDN_TUNE_CONV_THREADS  threads per workgroup of the prefill conv
 The decode kernel has no knob; its step is timed once for reference. The
@@ -37,7 +41,9 @@ import torch  # noqa: E402
 import linear_attention_ssm_amd as gdn  # noqa: E402
 import workloads as wl  # noqa: E402
 
-SCAN_VALUES = {torch.bfloat16: [0, 1, 2], torch.float32: [0, 1, 4]}
+# (scan form, scan tiles); (0, 0) is the automatic choice
+SCAN_VALUES = {torch.bfloat16: [(0, 0), (1, 1), (1, 2), (2, 2), (2, 1)],
+               torch.float32: [(0, 0), (0, 1), (0, 4)]}
 CONV_RUNS = [8, 16, 32]
 CONV_THREADS = [64, 128, 256]
 
@@ -94,7 +100,8 @@ def _cases():
 
 
 def _reset():
-    for k in (gdn.GDN_TUNE_SCAN_TILES, gdn.GDN_TUNE_CONV_RUN, gdn.GDN_TUNE_CONV_THREADS):
+    for k in (gdn.GDN_TUNE_SCAN_TILES, gdn.GDN_TUNE_CONV_RUN, gdn.GDN_TUNE_CONV_THREADS,
+              gdn.GDN_TUNE_SCAN_FORM):
         gdn.gdn_tune_set(k, 0)
 
 
@@ -134,12 +141,14 @@ def sweep_prefill(name, w, kw, reps, rounds, dev, stream, emit):
     equal = {v: True for v in values}
     for _ in range(rounds):
         for v in values:
-            gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, v)
+            gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, v[0])
+            gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_TILES, v[1])
             got = fwd()
             equal[v] &= all(torch.equal(g_, r_) for g_, r_ in zip(got, ref))
             best[v] = min(best[v], _time(fwd, reps, stream))
     for v in values:
-        emit(dict(workload=name, entry=entry, knob="scan_tiles", value=v, us=best[v],
+        emit(dict(workload=name, entry=entry, knob="scan_form,scan_tiles",
+                  value=0 if v == (0, 0) else f"{v[0]},{v[1]}", us=best[v],
                   tokens_per_s=tokens / (best[v] / 1e6), equal=equal[v]))
     _reset()
 
