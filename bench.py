@@ -177,18 +177,20 @@ def load_traffic(part, op):
     with open(path) as f:
         data = json.load(f)
     stem, src = KERNELS[part][op]
-    ent = data.get("parts", {}).get(part, {}).get(stem)
+    ent = data.get("parts", {}).get(part, {}).get("kernels", {}).get(stem)
     if not ent or ent.get("source_sha") != source_hash(src):
         return None
     return ent.get("bytes_per_launch")
 
 
-def kernel_report(part, op, us, share):
-    """One kernel's duration, its share of the single-pass bytes and the HBM
-    rate that share implies, beside the measured traffic."""
+def kernel_report(part, op, us, share, us_repeated=None):
+    """One kernel's duration (in the passes; back to back alone beside it), its
+    share of the single-pass bytes and the HBM rate that share implies, beside
+    the measured traffic."""
     gbs = share / (us * 1e-6) / 1e9
     tr = load_traffic(part, op)
-    return {"kernel": KERNELS.get(part, {}).get(op, (None,))[0], "us": us, "share_bytes": share,
+    return {"kernel": KERNELS.get(part, {}).get(op, (None,))[0], "us": us,
+            "us_repeated": us_repeated, "share_bytes": share,
             "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "traffic": tr,
             "traffic_ratio": None if tr is None else tr / share}
 
@@ -220,10 +222,10 @@ class Flush:
 
 
 def iter_stats(fn, torch, stream, iters, flush=None):
-    """Median, p10 and p90 (us) of `iters` single calls timed with HIP events on
-    `stream`, each preceded (outside its events) by `flush` when given."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
+    """Median, p10 and p90 (us) of `iters` single calls timed with HIP events
+    (TimingEvent) on `stream`, each preceded (outside its events) by `flush`
+    when given."""
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(iters)]
     for e0, e1 in evs:
         if flush is not None:
             flush()
@@ -238,15 +240,52 @@ def iter_stats(fn, torch, stream, iters, flush=None):
     return {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9), "iters": iters}
 
 
+class TimingEvent:
+    """A HIP event created with hipEventDisableSystemFence, for timing only:
+    recording it does not write back and invalidate the caches (a default
+    event's system-scope release does, which slows the kernel after it by
+    some microseconds and changes what it finds in the caches). Made through
+    the HIP runtime torch has loaded (found in the process's mappings)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln)
+            TimingEvent._hip = ctypes.CDLL(path)
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.h, self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        ms = self._c.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._c.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.h:
+            TimingEvent._hip.hipEventDestroy(self.h)
+
+
 def timed_ops(torch, stream, calls, steps, warmup):
     """calls: list of (op, fn). `warmup` untimed passes, then `steps` timed
     passes with nothing else on the stream (wall time per pass, us, between
-    two synchronisations). Each op's launch duration is then timed on its own:
-    a spin kernel holds the stream while the host queues `steps` launches of
-    the op, and HIP events before and after them give the average per launch
-    (back to back, as in the passes; one event pair per op keeps the events'
-    own gaps out of the average). Every op may be repeated: each reads the
-    previous ops' outputs and rewrites its own."""
+    two synchronisations). Each op's launch duration is then taken inside
+    `steps` more passes, HIP events (TimingEvent) recorded right before and
+    after that op only (one event pair per pass, so the op runs where it runs in the timed
+    passes, on the caches the ops before it leave), the passes queued behind
+    a spin kernel so the host's call overhead leaves no idle gaps; the average
+    over the passes. Also returned: the average of `steps` back-to-back
+    launches of the op alone (the same spin-and-queue timing), for reference."""
     def run():
         for _, fn in calls:
             fn()
@@ -258,16 +297,29 @@ def timed_ops(torch, stream, calls, steps, warmup):
         run()
     torch.cuda.synchronize()
     pass_us = (time.perf_counter() - t0) * 1e6 / steps
-    op_us = {op: repeated_us(torch, stream, fn, steps) for op, fn in calls}
-    return pass_us, op_us, run
+    op_us = {}
+    for j, (op, _) in enumerate(calls):
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(steps * len(calls) * 300000))   # over 100 us per queued launch
+        for e0, e1 in evs:
+            for i, (_, fn) in enumerate(calls):
+                if i == j:
+                    e0.record(stream)
+                fn()
+                if i == j:
+                    e1.record(stream)
+        torch.cuda.synchronize()
+        op_us[op] = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps * 1e3
+    rep_us = {op: repeated_us(torch, stream, fn, steps) for op, fn in calls}
+    return pass_us, op_us, rep_us, run
 
 
 def repeated_us(torch, stream, fn, reps):
     """Average duration (us) of `reps` back-to-back launches of fn, timed with
     HIP events on the launch stream behind a spin kernel (so the host's call
     overhead does not leave the GPU idle between the launches)."""
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
     torch.cuda._sleep(int(reps * 300000))   # over 100 us of spinning per queued launch
     e0.record(stream)
@@ -361,7 +413,7 @@ def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
                  ("prefill_scan",
                   lambda: gdn.gdn_prefill_scan(t["x"], t["w"], ws, initial_state=t["S0"],
                                                cu_seqlens=cu, o=o, final_state=fs, **dims))]
-        pass_us, op_us, run = timed_ops(torch, stream, calls, steps, warm)
+        pass_us, op_us, rep_us, run = timed_ops(torch, stream, calls, steps, warm)
         st = {"back_to_back": iter_stats(run, torch, stream, steps)}
         if flush:
             st["flushed"] = iter_stats(run, torch, stream, steps, flush)
@@ -373,7 +425,7 @@ def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
             s["hbm_frac"] = acc["prefill"]["bytes"] / (s["median_us"] * 1e-6) / (HBM_PEAK_GBS * 1e9)
         res["prefill"]["chunk_fwd"] = chunk_fwd_report(acc, tokens, sum(op_us.values()))
         for op, us in op_us.items():
-            kernels[op] = kernel_report(part, op, us, acc[op]["bytes"])
+            kernels[op] = kernel_report(part, op, us, acc[op]["bytes"], rep_us[op])
         del ws
 
     # the per-step path: conv1d + gates produce resident q, k, v, g, beta; the
@@ -393,7 +445,7 @@ def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
     conv[1]()
     gate[1]()
     calls = [conv, gate, prep, scan] if chain_ops else [prep, scan]
-    pass_us, op_us, run = timed_ops(torch, stream, calls, steps, warm)
+    pass_us, op_us, rep_us, run = timed_ops(torch, stream, calls, steps, warm)
     if chain_ops:
         res["chain"] = {"us": pass_us, "tokens_per_s": tokens / (pass_us * 1e-6)}
 
@@ -411,7 +463,7 @@ def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
             if kk in ("tokens_per_s", "mfma_frac", "hbm_frac")})
     res["chunk_fwd"]["iters"] = st
     for op, us in op_us.items():
-        kernels[op] = kernel_report(part, op, us, acc[op]["bytes"])
+        kernels[op] = kernel_report(part, op, us, acc[op]["bytes"], rep_us[op])
     res["kernels"] = kernels
     return res, acc
 
@@ -631,7 +683,9 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
     total = sum(sum(v) for v in groups.values())
     items = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     w = PART_WORKLOAD.get(part, part)
-    lines = [f"# Kernel times, {w} workload ({part}) (rocprofv3 --kernel-trace --stats)", "",
+    title = (f"{w} workload ({part})" if part in PART_WORKLOAD else
+             "the default bench run (every workload, cache-flushed iterations included)")
+    lines = [f"# Kernel times, {title} (rocprofv3 --kernel-trace --stats)", "",
              f"Command: `{command}`", "",
              "One line per kernel and launch shape (grid = work-items), from the kernel trace.", "",
              "| kernel | grid | workgroup | calls | average (us) | median (us) | min (us) | max (us) | share |",
@@ -645,13 +699,17 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
     if bench_log:
         js = [ln for ln in open(bench_log) if ln.startswith("{")]
         b = json.loads(js[-1])
-        cfg = b.get("configs", {}).get(part, {})
-        lines += ["", "The same run's bench figures (HIP events on the launch stream around",
-                  "back-to-back repeated launches of each op), for comparison with the trace above:", ""]
-        for op, k in cfg.get("kernels", {}).items():
-            lines.append(f"- {op} (`{k['kernel']}`): {k['us']:.2f} us")
-        if "decode" in cfg:
-            lines.append(f"- decode step (`{cfg['decode']['kernel']}`): {cfg['decode']['us_per_step']:.2f} us")
+        lines += ["", "The same run's bench figures (HIP events on the launch stream around the",
+                  "op inside the passes; in brackets, back-to-back launches of the op alone), for",
+                  "comparison with the trace above:", ""]
+        for p_ in ([part] if part in PART_WORKLOAD else list(b.get("configs", {}))):
+            cfg = b.get("configs", {}).get(p_, {})
+            for op, k in cfg.get("kernels", {}).items():
+                rep = f" ({k['us_repeated']:.2f} us)" if k.get("us_repeated") else ""
+                lines.append(f"- {p_} {op} (`{k['kernel']}`): {k['us']:.2f} us{rep}")
+            if "decode" in cfg:
+                lines.append(f"- {p_} decode step (`{cfg['decode']['kernel']}`): "
+                             f"{cfg['decode']['us_per_step']:.2f} us")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
