@@ -84,6 +84,23 @@ KERNELS = {
 }
 
 
+# the bf16 scan instances when the workgroup form is forced (--scan-form)
+_ROLES = {"prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
+          "chunk_scan": ("chunk_scan_roles_kernel<128, 2, 3, false>", _CHUNK)}
+_WIDE = {"prefill_scan": ("chunk_scan_wide_kernel<128, 8, 2, false, true>", _CHUNK),
+         "chunk_scan": ("chunk_scan_wide_kernel<128, 8, 2, true, false>", _CHUNK)}
+SCAN_FORM = 0
+
+
+def kernel_of(part, op):
+    """(kernel stem, source) that op runs in part under the scan form in force."""
+    if op in _ROLES and SCAN_FORM == 1 and part == "c4":
+        return _ROLES[op]     # (c2 and c3 run the column-group form by default)
+    if op in _ROLES and SCAN_FORM == 2 and part in ("c2", "c3"):
+        return _WIDE[op]      # (c4 runs the whole-unit form by default)
+    return KERNELS.get(part, {}).get(op)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -104,6 +121,9 @@ def parse():
                    help="skip the per-iteration timings with the caches flushed between "
                         "iterations (profiling runs: every traced launch then runs warm, as in "
                         "the timed steps)")
+    p.add_argument("--scan-form", type=int, default=0,
+                   help="GDN_TUNE_SCAN_FORM for the run (0 automatic, 1 column groups, 2 whole "
+                        "units): before/after comparisons of the bf16 scan schedules")
     p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_TRACE_CSV", "OUT_MD"),
                    help="turn a rocprofv3 --kernel-trace csv into a profiles/ summary")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -172,11 +192,11 @@ def load_traffic(part, op):
     of op's kernel in `part`, from profiles/traffic.json; None when absent or
     stale (the kernel's source has changed since the counters were taken)."""
     path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path) or op not in KERNELS.get(part, {}):
+    if not os.path.exists(path) or kernel_of(part, op) is None:
         return None
     with open(path) as f:
         data = json.load(f)
-    stem, src = KERNELS[part][op]
+    stem, src = kernel_of(part, op)
     ent = data.get("parts", {}).get(part, {}).get("kernels", {}).get(stem)
     if not ent or ent.get("source_sha") != source_hash(src):
         return None
@@ -189,7 +209,7 @@ def kernel_report(part, op, us, share, us_repeated=None):
     the measured traffic."""
     gbs = share / (us * 1e-6) / 1e9
     tr = load_traffic(part, op)
-    return {"kernel": KERNELS.get(part, {}).get(op, (None,))[0], "us": us,
+    return {"kernel": (kernel_of(part, op) or (None,))[0], "us": us,
             "us_repeated": us_repeated, "share_bytes": share,
             "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "traffic": tr,
             "traffic_ratio": None if tr is None else tr / share}
@@ -702,7 +722,8 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
         lines += ["", "The same run's bench figures (HIP events on the launch stream around the",
                   "op inside the passes; in brackets, back-to-back launches of the op alone), for",
                   "comparison with the trace above:", ""]
-        for p_ in ([part] if part in PART_WORKLOAD else list(b.get("configs", {}))):
+        parts_ = [part] if part in PART_WORKLOAD else list(b.get("configs", {}))
+        for p_ in parts_:
             cfg = b.get("configs", {}).get(p_, {})
             for op, k in cfg.get("kernels", {}).items():
                 rep = f" ({k['us_repeated']:.2f} us)" if k.get("us_repeated") else ""
@@ -710,6 +731,39 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
             if "decode" in cfg:
                 lines.append(f"- {p_} decode step (`{cfg['decode']['kernel']}`): "
                              f"{cfg['decode']['us_per_step']:.2f} us")
+        lines += ["", "The same run's pass figures (wall clock over the timed passes; per-iteration",
+                  "HIP-event medians back to back and with the caches flushed between iterations):",
+                  ""]
+        if b.get("value"):
+            lines.append(f"- headline: {b['value'] / 1e6:.2f} M tokens/s ({b['ms_per_step'] * 1e3:.1f} us "
+                         f"per step); flushed {b['value_flushed']['value'] / 1e6:.2f} M tokens/s "
+                         f"({b['value_flushed']['median_us']:.1f} us), HBM fraction "
+                         f"{b['value_flushed']['hbm_frac']:.3f}; roofline `{b['roofline']['kernel']}` "
+                         f"{b['roofline']['achieved']:.0f} GB/s = {b['roofline']['frac']:.3f} of "
+                         f"{b['roofline']['peak']:.0f}")
+        for p_ in parts_:
+            cfg = b.get("configs", {}).get(p_, {})
+            for key in ("prefill", "chunk_fwd"):
+                e = cfg.get(key) if key in cfg else None
+                if not e:
+                    continue
+                it = e.get("iters", {})
+                bb, fl = it.get("back_to_back", {}), it.get("flushed", {})
+                extra = (f", MFMA fraction {e['mfma_frac']:.3f} (dense count {e['mfma_frac_dense']:.3f})"
+                         if "mfma_frac" in e else "")
+                lines.append(f"- {p_} {key}: {e['us']:.1f} us, {e['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+                             f"HBM fraction {e['hbm_frac']:.3f}{extra}; medians {bb.get('median_us', 0):.1f} us "
+                             f"back to back, {fl.get('median_us', 0):.1f} us flushed")
+            if "chain" in cfg:
+                lines.append(f"- {p_} four per-step calls: {cfg['chain']['us']:.1f} us")
+            if "decode" in cfg:
+                dd = cfg["decode"]
+                lines.append(f"- {p_} decode: {dd['req_per_s'] / 1e6:.3f} M requests/s, "
+                             f"{dd['roofline']['achieved']:.0f} GB/s = {dd['roofline']['frac']:.3f} of HBM")
+        if "cpu_baseline" in b:
+            cb = b["cpu_baseline"]
+            lines.append(f"- oracle on the host: {cb['value']:.0f} {cb['unit']} on {cb['cores']} threads "
+                         f"({cb['sample']})")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -837,6 +891,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     parts = [p for p in args.only.split(",") if p]
+    global SCAN_FORM
+    SCAN_FORM = args.scan_form
+    gdn.gdn_tune_set(gdn.GDN_TUNE_SCAN_FORM, args.scan_form)
     for p in parts:
         if p not in PARTS:
             raise SystemExit(f"unknown part {p} (one of {PARTS})")

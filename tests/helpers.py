@@ -23,15 +23,22 @@ def rel_err(got, ref) -> float:
     return float(err / denom)
 
 
+# every parity figure measured in this process (the session summary prints them)
+PARITY = []
+
+
 def record_parity(what: str, err: float, tol: float) -> None:
-    """Append a measured parity figure to $GDN_PARITY_LOG (JSON lines), if set."""
+    """Keep a measured parity figure for the session summary, and append it to
+    $GDN_PARITY_LOG (JSON lines) when that is set."""
     import json
     import os
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    rec = {"test": test, "what": what, "err": float(err), "tol": tol}
+    PARITY.append(rec)
     path = os.environ.get("GDN_PARITY_LOG")
     if path:
-        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
         with open(path, "a") as f:
-            f.write(json.dumps({"test": test, "what": what, "err": err, "tol": tol}) + "\n")
+            f.write(json.dumps(rec) + "\n")
 
 
 def assert_close(got, ref, dtype, what=""):
