@@ -141,3 +141,40 @@ def test_forms_whole_prefill_full_size(form, name):
         form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f[0])
         _equal(_fused(form, d), ref, f"{name} form={f}")
         form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, 0)
+
+
+@pytest.mark.parametrize("n", [1000, 1100])
+def test_forms_many_packed_sequences(form, n):
+    # more (sequence, head) units than the whole-unit threshold; 1,000
+    # sequences are started longest first (the order is a rank sort on the
+    # device, ties by index), 1,100 in index order (past the sort's limit of
+    # 1,024). Lengths 0..130 (zero-length sequences pass S0 through); every
+    # unit is compared with the oracle, so an order that repeated or skipped a
+    # unit would show.
+    gen = np.random.default_rng(n)
+    lengths = [int(x) for x in gen.integers(0, 131, n)]
+    lengths[3] = 0
+    lengths[7] = 130
+    d = wl.chunk_inputs(B=1, T=sum(lengths), H=1, Hk=1, K=128, V=128, dtype=BF16,
+                        lengths=lengths, s0_std=0.05, seed=n)
+    print(f"scan forms: {n} packed sequences, {sum(lengths)} tokens", flush=True)
+    ref = _run(form, d, FORMS[0])
+    ro, rs = _oracle(d)
+    for f in FORMS[1:]:
+        o, sf = _run(form, d, f)
+        assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1]), (n, f)
+    assert_close(to_np(ref[0]), ro, BF16, f"{n} packed o")
+    assert_close(to_np(ref[1]), rs, BF16, f"{n} packed state")
+    # the automatic choice (whole units from 512 units) gives the same bits
+    o, sf = _run(form, d, (0, 0))
+    assert torch.equal(o, ref[0]) and torch.equal(sf, ref[1])
+
+
+def test_forms_without_final_state(form):
+    # no final state requested: the scan skips its store; o is unchanged
+    d = wl.chunk_inputs(B=2, T=200, H=4, Hk=2, K=128, V=128, dtype=BF16, s0_std=0.05, seed=11)
+    ref = _run(form, d, FORMS[0])
+    for f in FORMS:
+        o, sf = _run(form, d, f, output_final_state=False)
+        assert sf is None
+        assert torch.equal(o, ref[0]), f
