@@ -1,7 +1,7 @@
 """gdn_prefill on seeded random shapes: equal bit for bit to the four-step
-chain (conv1d + SiLU, gates, chunk_prepare, chunk_scan) under both column-tile
-settings of the scan, and within the bf16 bar of the fp64 oracle on the first
-few.
+chain (conv1d + SiLU, gates, chunk_prepare, chunk_scan) under every scan
+schedule (column groups of one and two tiles, whole units), and within the
+bf16 bar of the fp64 oracle on the first few.
 
 The shapes come from a fixed seed: head dims K and V in {64, 128}, 1, 2 or 4
 key heads with 1, 2 or 4 value heads each, either dense batches whose length
@@ -52,10 +52,12 @@ def test_random_shape_prefill_equals_chain(gpu, i):
     d, bias = _case(i)
     ref = _chain(gpu, d, bias=bias)
     try:
-        for tiles in (1, 2):
+        for form, tiles in ((1, 1), (1, 2), (2, 0)):
+            gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, form)
             gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, tiles)
-            _equal(_fused(gpu, d, bias=bias), ref, f"case {i}, {tiles} column tile(s)")
+            _equal(_fused(gpu, d, bias=bias), ref, f"case {i}, form {form}, {tiles} tile(s)")
     finally:
+        gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, 0)
         gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, 0)
 
 

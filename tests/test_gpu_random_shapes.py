@@ -6,7 +6,9 @@ heads with 1, 2 or 4 value heads each, dense batches (1 to 3 rows, lengths on
 or next to a chunk boundary or drawn up to 300) or up to six packed sequences
 of 0 to 200 tokens, with or without an initial state, each decay regime,
 scale 1 or 1/sqrt(K), with or without the L2 norm of q and k (without it,
-q and k are normalised beforehand: the recurrence needs |k| <= ~1).
+q and k are normalised beforehand: the recurrence needs |k| <= ~1); the bf16
+cases also run every scan schedule (forms and tiles) and must give the same
+bits.
 Decode: 1 to 9 requests, M = 1 to 4 Householder copies, G groups of 1, 2 or 4
 value heads, P and N in {64, 128}, three steps on one state.
 Conv1d: integer inputs (exact in both dtypes, so compared bit for bit), 1 to
@@ -66,6 +68,17 @@ def test_random_shape_chunk_fwd(gpu, i):
     ro, rs = _oracle_chunk(d, scale, l2norm)
     assert_close(to_np(o), ro, d["dtype"], f"case {i} o")
     assert_close(to_np(sf), rs, d["dtype"], f"case {i} final state")
+    if d["dtype"] == torch.bfloat16:
+        # the other bf16 scan schedules give the same bits
+        try:
+            for form, tiles in ((1, 1), (1, 2), (2, 0), (2, 1)):
+                gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, form)
+                gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, tiles)
+                o2, sf2 = _gpu_chunk(gpu, d, scale, l2norm)
+                assert torch.equal(o2, o) and torch.equal(sf2, sf), (i, form, tiles)
+        finally:
+            gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, 0)
+            gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, 0)
 
 
 @pytest.mark.parametrize("i", range(8))
