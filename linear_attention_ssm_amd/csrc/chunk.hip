@@ -2152,15 +2152,22 @@ void chunk_scan_roles_kernel(
 // compute waves issue the copies of the next chunk themselves (a wave stalled
 // getting its share into the vector-memory pipe leaves its SIMD to the other);
 // with one compute wave per SIMD (two tiles each) a copy wave issues every
-// direct-to-LDS copy of the
-// next chunk at the start of a step (61 KiB at K = V = 128: 61 copies, which
-// fit its vector-memory counter) and waits for them at the end, so the
-// compute waves never stall on the vector-memory pipe: measured with cycle
-// stamps, a compute wave that issued a quarter of the copies itself spent
-// 2,200 - 3,500 cycles per chunk just getting them into the pipe. Two buffers:
-// chunk c + 1 lands while chunk c is computed; one barrier per chunk. Inside a
-// step each phase's LDS operands are requested during the phase before, so
-// their latency hides behind matrix ops.
+// direct-to-LDS copy of the next chunk at the start of a step (61 KiB at
+// K = V = 128: 61 copies, which fit its vector-memory counter) and waits for
+// them at the end, so the compute waves never stall getting copies into the
+// vector-memory pipe (a compute wave that issues a quarter of them itself
+// spends a large part of its step there). Two buffers: chunk c + 1 lands while
+// chunk c is computed; one barrier per chunk. Inside a step each phase's LDS
+// operands are requested during the phase before, so their latency hides
+// behind matrix ops.
+//
+// Whole-prefill form (CONV): four compute waves of NT / 4 tiles and four
+// auxiliary waves, one per compute wave. Auxiliary wave a issues a quarter of
+// the copies (the K / Q blocks and record of chunk c + 1 into one of two
+// buffers, the raw value rows of chunk c + 2 into a ring of three) and, in
+// step c, convolves compute wave a's value slabs of chunk c + 1 in place, as
+// the column-group form's conv waves do; the compute waves read the convolved
+// values in their operand order.
 template <int KD, int NTILES>
 struct WideBuf {
     static constexpr int RB = KD * 2;                       // bytes per K / Q row
