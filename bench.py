@@ -141,17 +141,18 @@ def parse():
 
 # ------------------------------------------------------------------ accounting
 
-def accounting(tok, n_chunks, N, H, Hk, K, V, es=2):
+def accounting(tok, n_chunks, N, H, Hk, K, V, es=2, s0=False):
     """Algorithmic HBM bytes of the method's tensors (each read or written
     once) and MFMA flops, for a prefill of `tok` tokens in `n_chunks` chunks
-    per head and N sequences; es = bytes per activation element."""
+    per head and N sequences; es = bytes per activation element; s0: an
+    initial state is read."""
     C = 2 * Hk * K + H * V
     xqk = tok * 2 * Hk * K * es          # q|k channels (before or after the conv)
     xv = tok * H * V * es                # value channels
     o = tok * H * V * es
     ab = 2 * tok * H * es                # gate inputs a, b
     gb = 2 * tok * H * 4                 # g, beta (fp32)
-    state = N * H * K * V * 4
+    state = N * H * K * V * 4 * (2 if s0 else 1)   # final state written (+ initial read)
     taps = C * 4 * es
     d, Cc = K, 64
     flops = tok * H * (6 * d * d + 5 * Cc * d + (2 * Cc * Cc) / 3)
@@ -415,7 +416,7 @@ def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):
         lens = (cu[1:] - cu[:-1]).cpu()
         n_chunks = int(((lens + 63) // 64).sum())
     es = 2 if w.dtype == torch.bfloat16 else 4
-    acc = accounting(B * T, n_chunks, N, H, Hk, K, V, es)
+    acc = accounting(B * T, n_chunks, N, H, Hk, K, V, es, s0=t["S0"] is not None)
     tokens = B * T
     res = {"workload": _workload_name(w, B, T, N), "tokens": tokens}
     o = torch.empty((B, T, H, V), dtype=w.dtype, device=dev)
