@@ -1,5 +1,6 @@
-"""Whole-tensor parity at the prefill workload's full size, and long
-sequences with weak or no decay, against the fp64 oracle.
+"""Whole-tensor parity at the prefill, GQA and packed workloads' full sizes
+(every (sequence, head) unit), and long sequences with weak or no decay,
+against the fp64 oracle.
 
 The bf16 path rounds the state to a bf16 MFMA operand at every chunk (the
 products K h and Q h); the workload gates decay fast, which hides any drift
@@ -46,13 +47,14 @@ def _oracle(d):
 def _run(gdn, d, entry):
     t = {n: d[n].to(DEV) for n in ("x", "w", "a", "b", "A_log", "dt_bias")}
     S0 = None if d["S0"] is None else d["S0"].to(DEV)
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].to(DEV)
     dims = dict(Hk=d["Hk"], K=d["K"], H=d["H"], V=d["V"])
     if entry == "prefill":
         o, sf = gdn.gdn_prefill(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"],
-                                initial_state=S0, **dims)
+                                initial_state=S0, cu_seqlens=cu, **dims)
     else:
         o, sf = gdn.prefill_chain(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"],
-                                  initial_state=S0, **dims)
+                                  initial_state=S0, cu_seqlens=cu, **dims)
     torch.cuda.synchronize()
     return to_np(o), to_np(sf)
 
@@ -80,6 +82,20 @@ def test_prefill_full_all_heads(gpu):
     o, sf = _run(gpu, d, "prefill")
     assert_close(o, ro, BF16, "prefill full o")
     assert_close(sf, rs, BF16, "prefill full state")
+
+
+@pytest.mark.parametrize("name", ["gqa", "varlen"])
+def test_prefill_full_all_units(gpu, name):
+    # the long GQA and packed workloads, whole o and final state: every
+    # (sequence, head) unit against the oracle, on the whole-prefill entry
+    # and the per-step chain (the automatic scan schedule)
+    d = wl.prefill_inputs(wl.WORKLOADS[name])
+    print(f"full-size parity, every unit: {name}", flush=True)
+    ro, rs = _oracle(d)
+    for entry in ("prefill", "chain"):
+        o, sf = _run(gpu, d, entry)
+        assert_close(o, ro, BF16, f"{name} full {entry} o")
+        assert_close(sf, rs, BF16, f"{name} full {entry} state")
 
 
 @pytest.mark.parametrize("A_log", [-6.0, float("-inf")], ids=["weak", "none"])
