@@ -736,12 +736,16 @@ def summarize_stats(csv_path, out_md, command, part, bench_log=None):
                   "HIP-event medians back to back and with the caches flushed between iterations):",
                   ""]
         if b.get("value"):
-            lines.append(f"- headline: {b['value'] / 1e6:.2f} M tokens/s ({b['ms_per_step'] * 1e3:.1f} us "
-                         f"per step); flushed {b['value_flushed']['value'] / 1e6:.2f} M tokens/s "
-                         f"({b['value_flushed']['median_us']:.1f} us), HBM fraction "
-                         f"{b['value_flushed']['hbm_frac']:.3f}; roofline `{b['roofline']['kernel']}` "
-                         f"{b['roofline']['achieved']:.0f} GB/s = {b['roofline']['frac']:.3f} of "
-                         f"{b['roofline']['peak']:.0f}")
+            head = f"- headline: {b['value'] / 1e6:.2f} M tokens/s ({b['ms_per_step'] * 1e3:.1f} us per step)"
+            if "value_flushed" in b:
+                fl = b["value_flushed"]
+                head += (f"; flushed {fl['value'] / 1e6:.2f} M tokens/s ({fl['median_us']:.1f} us), "
+                         f"HBM fraction {fl['hbm_frac']:.3f}")
+            if "roofline" in b:
+                rf = b["roofline"]
+                head += (f"; roofline `{rf['kernel']}` {rf['achieved']:.0f} GB/s = {rf['frac']:.3f} "
+                         f"of {rf['peak']:.0f}")
+            lines.append(head)
         for p_ in parts_:
             cfg = b.get("configs", {}).get(p_, {})
             for key in ("prefill", "chunk_fwd"):
