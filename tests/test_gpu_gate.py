@@ -73,3 +73,27 @@ def test_gates_full_size(gpu, name):
     gr, br = oracle.gate_prepare(to_np(d["a"]), to_np(d["b"]), to_np(d["A_log"]), to_np(d["dt_bias"]))
     np.testing.assert_allclose(beta, br, rtol=2e-6, atol=1e-30)
     np.testing.assert_allclose(g, gr, rtol=4e-6, atol=1e-37)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gates_four_wide_and_one_wide_agree(gpu, dtype):
+    # contiguous rows with H % 4 == 0 take four heads per thread; the same
+    # values one element off a 4-element boundary take one per thread: the
+    # results must be the same bits
+    gen = torch.Generator().manual_seed(31)
+    R, H = 517, 16
+    wide_a = (torch.randn(R, H + 1, generator=gen) * 8).to(dtype)
+    wide_b = (torch.randn(R, H + 1, generator=gen) * 8).to(dtype)
+    A_log = torch.log(1 + 15 * torch.rand(H, generator=gen))
+    dt_bias = torch.randn(H, generator=gen) * 0.1
+    dev = torch.device("cuda")
+    wa, wb = wide_a.to(dev), wide_b.to(dev)
+    A, D = A_log.to(dev), dt_bias.to(dev)
+    g1, b1 = gpu.gdn_gate_prepare(wa[:, 1:], wb[:, 1:], A, D)               # misaligned rows
+    g4, b4 = gpu.gdn_gate_prepare(wa[:, 1:].contiguous(), wb[:, 1:].contiguous(), A, D)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g4) and torch.equal(b1, b4)
+    gr, br = oracle.gate_prepare(to_np(wide_a[:, 1:]), to_np(wide_b[:, 1:]), to_np(A_log),
+                                 to_np(dt_bias))
+    np.testing.assert_allclose(to_np(g4), gr, rtol=4e-6, atol=1e-37)
+    np.testing.assert_allclose(to_np(b4), br, rtol=2e-6, atol=1e-30)
