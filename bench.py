@@ -67,7 +67,7 @@ KERNELS = {
     "c2": {"prefill_prepare": (_PREP, _CHUNK),
            "prefill_scan": ("chunk_scan_roles_kernel<128, 2, 3, true>", _CHUNK),
            "conv1d": ("conv1d_causal_kernel<bf16, 16, 256>", CSRC + "conv1d.hip"),
-           "gate_prepare": ("gate_prepare_kernel<bf16>", CSRC + "gate.hip"),
+           "gate_prepare": ("gate_prepare4_kernel<bf16>", CSRC + "gate.hip"),
            "chunk_prepare": (_CPREP, _CHUNK),
            "chunk_scan": ("chunk_scan_roles_kernel<128, 2, 3, false>", _CHUNK)},
     "c3": {"prefill_prepare": (_PREP, _CHUNK),
