@@ -73,15 +73,18 @@ const char* gdn_status_string(int status);
  *   GDN_TUNE_CONV_THREADS  threads per workgroup of gdn_conv1d_causal: 64,
  *                          128 or 256.
  *   GDN_TUNE_SCAN_FORM     workgroup form of the bf16 state scan of
- *                          gdn_chunk_fwd / gdn_chunk_scan: 1 = one workgroup
- *                          per group of 16 * GDN_TUNE_SCAN_TILES value
- *                          columns of a (sequence, head) unit, waves split by
- *                          role; 2 = one workgroup per unit over all its value
- *                          columns, compute waves each running the whole chunk
- *                          step for 16 * GDN_TUNE_SCAN_TILES of them (2: four
- *                          waves and a copy wave, the default; 1: eight
- *                          waves), packed sequences longest first. Automatic:
- *                          2 from 512 units on, else 1.
+ *                          gdn_chunk_fwd, gdn_chunk_scan, gdn_prefill and
+ *                          gdn_prefill_scan: 1 = one workgroup per group of
+ *                          16 * GDN_TUNE_SCAN_TILES value columns of a
+ *                          (sequence, head) unit, waves split by role; 2 = one
+ *                          workgroup per unit over all its value columns,
+ *                          compute waves each running the whole chunk step for
+ *                          16 * GDN_TUNE_SCAN_TILES of them (2: four waves and
+ *                          a copy wave, the default; 1: eight waves; the
+ *                          whole-prefill scan always has four compute waves
+ *                          and four waves that copy and convolve), packed
+ *                          sequences longest first. Automatic: 2 from 512
+ *                          units on, else 1.
  * gdn_tune_set returns GDN_EINVAL for an unknown knob or value (nothing
  * changes); gdn_tune_get returns the knob's value, or -1 for an unknown knob.
  * ---------------------------------------------------------------------- */
