@@ -44,6 +44,8 @@
 //               tiles per workgroup take the role-split form below (chain,
 //               output and copy waves on separate SIMDs); the fp32 operand
 //               path and wide workgroups share one wave per column tile.
+#include <utility>
+
 #include "gdn_common.hpp"
 
 namespace gdn {
@@ -2256,6 +2258,44 @@ constexpr size_t wide_lds_bytes() {
     return CONV ? 2 * sizeof(WideKQR<KD>) + 3 * sizeof(WideVal<NT>) : 2 * sizeof(WideBuf<KD, NT>);
 }
 
+// The copies of a whole-prefill chunk step as pieces of 1 KiB, [K tile][Q
+// tile][record][value slabs], auxiliary wave a taking pieces a, a + 4, ...:
+// each piece's tensor, index in its tensor and LDS destination, at compile
+// time.
+template <int KD, int NT>
+struct WideAuxPieces {
+    typedef WideKQR<KD> KQR;
+    static constexpr int TPc = kChunk * KD * 2 / 1024;     // pieces of a K / Q tile
+    static constexpr int RPc = Rec<bf16>::bytes / 1024;
+    static constexpr int VPc = NT * 2;                      // value pieces (2 per slab)
+    static constexpr int total = 2 * TPc + RPc + VPc;
+    static constexpr int per = (total + 3) / 4;
+    // 0 K, 1 Q, 2 record, 3 values, 4 none
+    static constexpr int tensor(int pc) {
+        return pc < TPc ? 0 : pc < 2 * TPc ? 1 : pc < 2 * TPc + RPc ? 2 : pc < total ? 3 : 4;
+    }
+    static constexpr int index(int pc) {
+        return pc < TPc ? pc : pc < 2 * TPc ? pc - TPc : pc < 2 * TPc + RPc ? pc - 2 * TPc
+                                                                               : pc - 2 * TPc - RPc;
+    }
+    static constexpr uint32_t dst(int pc) {
+        return tensor(pc) == 0 ? (uint32_t)offsetof(KQR, k) + index(pc) * 1024
+             : tensor(pc) == 1 ? (uint32_t)offsetof(KQR, q) + index(pc) * 1024
+             : tensor(pc) == 2 ? (uint32_t)offsetof(KQR, rec) + index(pc) * 1024
+             : (uint32_t)(index(pc) >> 1) * (kChunk * 32) + (index(pc) & 1) * 1024;
+    }
+};
+
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1, unrolled
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // compute waves of a unit of NT column tiles with TPW tiles each; after them
 // a copy wave (COPYW), or (CONV) four auxiliary waves that issue the copies
 // and convolve the values, one per compute wave
@@ -2361,42 +2401,33 @@ void chunk_scan_wide_kernel(
         // ---------------- auxiliary wave a: a quarter of the copies (K, Q and
         // record of chunk c + 1, raw values of chunk c + 2) and the
         // convolution of compute wave a's value slabs of chunk c + 1, in step c
-        const int a = wave - kWideWaves;
+        // (one instance per a, so every piece's tensor and LDS destination are
+        // constants)
+      auto aux = [&](auto a_c) {
+        constexpr int a = decltype(a_c)::value;
+        typedef WideAuxPieces<KD, NT> AP;
         constexpr uint32_t tb = qk_block_bytes<KD>();
-        constexpr int TPc = kChunk * KD * 2 / 1024;           // pieces of a K / Q tile
-        constexpr int RPc = Rec<bf16>::bytes / 1024;
-        constexpr int VPc = NT * 2;                            // value pieces (2 per slab)
-        constexpr int total = 2 * TPc + RPc + VPc;
-        constexpr int per = (total + 3) / 4;
         constexpr int SPR = KD * 2 / 16, RPI = 1024 / (KD * 2);
         const uint64_t qb0 = (uint64_t)qp + ((uint64_t)tile0 * Hk + hk) * 2 * tb;   // chunk 0's q block
         const uint64_t kqstep = (uint64_t)Hk * 2 * tb;
-        uint32_t src[per], dst[per];
-        int ten[per];   // 0 K, 1 Q, 2 record, 3 values, 4 none
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-            const int pc = a + 4 * i;
-            int t = 4, j = 0;
-            if (pc < TPc) { t = 0; j = pc; }
-            else if (pc < 2 * TPc) { t = 1; j = pc - TPc; }
-            else if (pc < 2 * TPc + RPc) { t = 2; j = pc - 2 * TPc; }
-            else if (pc < total) { t = 3; j = pc - 2 * TPc - RPc; }
-            ten[i] = t;
-            if (t <= 1) {
+        uint32_t src[AP::per];   // this lane's source offset per piece
+        static_for<AP::per>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int pc = a + 4 * i, t = AP::tensor(pc), j = AP::index(pc);
+            if constexpr (t <= 1) {
                 // (blocked: logical segment sg of a row is segment sg % 4 of slice sg / 4)
                 const int row = j * RPI + lane / SPR;
                 const int sg = (lane % SPR) ^ tile_mask<bf16, KD, 1>(row);
                 src[i] = (uint32_t)((sg >> 2) * (kChunk * 64) + row * 64 + (sg & 3) * 16);
-                dst[i] = (t == 0 ? offsetof(KQR, k) : offsetof(KQR, q)) + j * 1024;
-            } else if (t == 2) {
+            } else if constexpr (t == 2) {
                 src[i] = (uint32_t)j * 1024 + lane * 16;
-                dst[i] = offsetof(KQR, rec) + j * 1024;
-            } else {
+            } else if constexpr (t == 3) {
                 const int row = 32 * (j & 1) + lane / 2;
                 src[i] = (uint32_t)row * v_row + (uint32_t)(j >> 1) * 32 + (uint32_t)(lane & 1) * 16;
-                dst[i] = (uint32_t)(j >> 1) * (kChunk * 32) + (j & 1) * 1024;
+            } else {
+                src[i] = 0u;
             }
-        }
+        });
         auto chunk_rows = [&](int c) {
             return c < nchunks ? (uint32_t)min(kChunk, tok_end - (tok_begin + c * kChunk)) : 0u;
         };
@@ -2412,12 +2443,16 @@ void chunk_scan_wide_kernel(
             const rsrc_t rv = make_rsrc((const void*)(v0 + (uint64_t)cvv * kChunk * v_row), chunk_rows(cv) * v_row);
             unsigned char* kb_ = reinterpret_cast<unsigned char*>(&kqrs[c & 1]);
             unsigned char* vb_ = reinterpret_cast<unsigned char*>(&vring[cv % 3]);
-#pragma unroll
-            for (int i = 0; i < per; ++i) {
-                const int t = ten[i];
-                if (t <= 2 && kqr) dma16(t == 0 ? rk : t == 1 ? rq : rr, kb_ + dst[i], src[i], 0);
-                if (t == 3 && val) dma16(rv, vb_ + dst[i], src[i], 0);
-            }
+            static_for<AP::per>([&](auto i_c) {
+                constexpr int i = decltype(i_c)::value;
+                constexpr int pc = a + 4 * i, t = AP::tensor(pc);
+                constexpr uint32_t d = AP::dst(pc);
+                if constexpr (t <= 2) {
+                    if (kqr) dma16(t == 0 ? rk : t == 1 ? rq : rr, kb_ + d, src[i], 0);
+                } else if constexpr (t == 3) {
+                    if (val) dma16(rv, vb_ + d, src[i], 0);
+                }
+            });
         };
         // the taps and bias of this lane's column in each of compute wave a's tiles
         ColTaps cv[TPW];
@@ -2481,6 +2516,13 @@ void chunk_scan_wide_kernel(
             convert(c + 1);
             wait_vmcnt<0>();
             lds_barrier();
+        }
+      };
+        switch (wave - kWideWaves) {
+        case 0: aux(std::integral_constant<int, 0>{}); break;
+        case 1: aux(std::integral_constant<int, 1>{}); break;
+        case 2: aux(std::integral_constant<int, 2>{}); break;
+        default: aux(std::integral_constant<int, 3>{}); break;
         }
         return;
     }
