@@ -1357,12 +1357,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     SB* bufs = reinterpret_cast<SB*>(smem_raw);
 
-    // XCD-aware block order: all column groups of one (seq, head) unit get the
-    // same blockIdx % 8, i.e. run on the same XCD and share its L2.
+    // XCD-aware block order: XCD x (blockIdx % 8) takes units x u8 .. x u8 +
+    // u8 - 1 (u8 = ceil(units / 8)) with all their column groups, so a unit's
+    // groups and the value heads that share a q/k head run on one XCD and
+    // read the K and Q rows and the records through its L2.
     const int bid = blockIdx.x;
     const int rest = bid >> 3;
     const int cgrp = rest % groups;
-    const int u = (rest / groups) * 8 + (bid & 7);
+    const int u = (bid & 7) * ((units + 7) >> 3) + rest / groups;
     if (u >= units) return;
     const int seq = u / H;
     const int h = u - seq * H;
@@ -1536,9 +1538,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 // In the whole-prefill form the values are staged raw and one conv wave per
 // column tile convolves its slab of each chunk in place during the step
 // before the chains read them, half before and half after the mid-step
-// barrier. Measured on MI355X (per-wave cycle stamps): this takes the
-// convolution off the chains' dependent path; a chunk's step went from
-// about 3,300 cycles (convolving in the chain waves) to 2,900.
+// barrier, which keeps the convolution off the chains' dependent path.
 template <int KD, int NT>
 struct RoleHand {
     bf16x8 h[KD / 32][NT][kWave];   // h of the step's chunk: B operand per contraction block and tile
@@ -1857,12 +1857,14 @@ void chunk_scan_roles_kernel(
     unsigned char* scratch = smem_raw + NBUF * sizeof(SB);
     HD* hand = reinterpret_cast<HD*>(smem_raw + NBUF * sizeof(SB) + 256);
 
-    // XCD-aware block order: all column groups of one (seq, head) unit get the
-    // same blockIdx % 8, i.e. run on the same XCD and share its L2.
+    // XCD-aware block order: XCD x (blockIdx % 8) takes units x u8 .. x u8 +
+    // u8 - 1 (u8 = ceil(units / 8)) with all their column groups, so a unit's
+    // groups and the value heads that share a q/k head run on one XCD and
+    // read the K and Q rows and the records through its L2.
     const int bid = blockIdx.x;
     const int rest = bid >> 3;
     const int cgrp = rest % groups;
-    const int u = (rest / groups) * 8 + (bid & 7);
+    const int u = (bid & 7) * ((units + 7) >> 3) + rest / groups;
     if (u >= units) return;
     const int seq = u / H;
     const int h = u - seq * H;

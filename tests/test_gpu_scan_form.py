@@ -178,3 +178,29 @@ def test_forms_without_final_state(form):
         o, sf = _run(form, d, f, output_final_state=False)
         assert sf is None
         assert torch.equal(o, ref[0]), f
+
+
+@pytest.mark.parametrize("n", [1000, 1100])
+def test_forms_whole_prefill_many_packed_sequences(form, n):
+    # the whole prefill over many short packed sequences (lengths 0..130, an
+    # initial state): past the whole-unit threshold the automatic choice runs
+    # the auxiliary-wave form, longest first for 1,000 sequences and in index
+    # order for 1,100. Both forms and the automatic choice equal the
+    # conv1d -> gates -> chunk_fwd chain bit for bit, and every unit matches
+    # the oracle.
+    from tests.test_gpu_prefill import _chain, _fused, _equal, _oracle as _poracle
+    gen = np.random.default_rng(n + 1)
+    lengths = [int(x) for x in gen.integers(0, 131, n)]
+    lengths[5] = 0
+    lengths[9] = 130
+    w = wl.Workload(f"packed{n}", 4, BF16, H=1, Hk=1, K=128, V=128, s0_std=0.05)
+    d = wl.prefill_inputs(w, lengths=lengths, seed=n)
+    print(f"scan forms, whole prefill: {n} packed sequences, {sum(lengths)} tokens", flush=True)
+    ref = _chain(form, d)
+    for f in ((1, 0), (2, 0), (0, 0)):
+        form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, f[0])
+        _equal(_fused(form, d), ref, f"{n} packed form={f}")
+    form.gdn_tune_set(form.GDN_TUNE_SCAN_FORM, 0)
+    ro, rs = _poracle(d)
+    assert_close(to_np(ref[0]), ro, BF16, f"{n} packed whole prefill o")
+    assert_close(to_np(ref[1]), rs, BF16, f"{n} packed whole prefill state")
