@@ -1357,15 +1357,20 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     SB* bufs = reinterpret_cast<SB*>(smem_raw);
 
-    // XCD-aware block order: XCD x (blockIdx % 8) takes units x u8 .. x u8 +
-    // u8 - 1 (u8 = ceil(units / 8)) with all their column groups, so a unit's
-    // groups and the value heads that share a q/k head run on one XCD and
-    // read the K and Q rows and the records through its L2.
+    // XCD-aware block order: the (sequence, q/k head) pairs go round the 8
+    // XCDs (blockIdx % 8), and on its XCD each pair runs all column groups of
+    // every value head that shares its q/k head, one after another. A unit's
+    // groups and its GQA siblings read the K and Q rows and the records
+    // through one L2, while consecutive pairs, of unequal packed lengths,
+    // spread over the XCDs.
     const int bid = blockIdx.x;
     const int rest = bid >> 3;
     const int cgrp = rest % groups;
-    const int u = (bid & 7) * ((units + 7) >> 3) + rest / groups;
-    if (u >= units) return;
+    const int per = H / Hk;                    // value heads per q/k head
+    const int sib = (rest / groups) % per;
+    const int kv = (rest / groups / per) * 8 + (bid & 7);   // (sequence, q/k head) pair
+    const int u = kv * per + sib;
+    if (kv >= units / per) return;
     const int seq = u / H;
     const int h = u - seq * H;
 
@@ -1857,15 +1862,20 @@ void chunk_scan_roles_kernel(
     unsigned char* scratch = smem_raw + NBUF * sizeof(SB);
     HD* hand = reinterpret_cast<HD*>(smem_raw + NBUF * sizeof(SB) + 256);
 
-    // XCD-aware block order: XCD x (blockIdx % 8) takes units x u8 .. x u8 +
-    // u8 - 1 (u8 = ceil(units / 8)) with all their column groups, so a unit's
-    // groups and the value heads that share a q/k head run on one XCD and
-    // read the K and Q rows and the records through its L2.
+    // XCD-aware block order: the (sequence, q/k head) pairs go round the 8
+    // XCDs (blockIdx % 8), and on its XCD each pair runs all column groups of
+    // every value head that shares its q/k head, one after another. A unit's
+    // groups and its GQA siblings read the K and Q rows and the records
+    // through one L2, while consecutive pairs, of unequal packed lengths,
+    // spread over the XCDs.
     const int bid = blockIdx.x;
     const int rest = bid >> 3;
     const int cgrp = rest % groups;
-    const int u = (bid & 7) * ((units + 7) >> 3) + rest / groups;
-    if (u >= units) return;
+    const int per = H / Hk;                    // value heads per q/k head
+    const int sib = (rest / groups) % per;
+    const int kv = (rest / groups / per) * 8 + (bid & 7);   // (sequence, q/k head) pair
+    const int u = kv * per + sib;
+    if (kv >= units / per) return;
     const int seq = u / H;
     const int h = u - seq * H;
 
@@ -2882,7 +2892,7 @@ static hipError_t launch_scan(const void* q, const void* k, int64_t qks, const v
 {
     const int units = N * H;
     const int groups = V / (16 * NW);
-    const int upad = (units + 7) / 8 * 8;
+    const int upad = (units / (H / Hk) + 7) / 8 * 8 * (H / Hk);   // 8 XCDs x whole (sequence, q/k head) pairs
     typedef ScanBuf<T, KD, NW> SB;
     // three buffers (two chunks in flight) where they fit in LDS and one
     // chunk's copies fit the 6-bit vector-memory counter
@@ -2909,7 +2919,7 @@ static hipError_t launch_scan_roles(const void* q, const void* k, int64_t qks, c
 {
     const int units = N * H;
     const int groups = V / (16 * NT);
-    const int upad = (units + 7) / 8 * 8;
+    const int upad = (units / (H / Hk) + 7) / 8 * 8 * (H / Hk);   // 8 XCDs x whole (sequence, q/k head) pairs
     typedef ScanBuf<bf16, KD, NT> SB;
     constexpr int NBUF = 3;
     constexpr size_t smem = NBUF * sizeof(SB) + 256 + sizeof(RoleHand<KD, NT>);
