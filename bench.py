@@ -367,36 +367,18 @@ def device_inputs(w, wl, torch, dev):
     """The prefill inputs of workload w on the device. The prefill workload
     and the tiny one use the seeded CPU draws of workloads.py; the GQA and
     varlen workloads (1 GB and more) are drawn on the GPU with a seeded
-    generator, in the same distributions (varlen: the lengths are the CPU
-    draw, made first as in workloads.py)."""
+    generator, in the same distributions (workloads.device_prefill_inputs;
+    varlen: the lengths are the CPU draw, made first as in workloads.py)."""
     if w.name in ("prefill", "tiny"):
         d = wl.prefill_inputs(w)
         t = {n: d[n].to(dev) for n in ("x", "w", "a", "b", "A_log", "dt_bias")}
         t["S0"] = None if d["S0"] is None else d["S0"].to(dev)
         t["cu"] = None if d["cu_seqlens"] is None else d["cu_seqlens"].to(dev)
         return t, d["B"], d["T"], d["N"]
-    gen_cpu = torch.Generator().manual_seed(w.seed)
-    cu = None
-    B, T, N = w.B, w.T, w.B
-    if w.n_seqs:
-        lengths = wl.varlen_lengths(gen_cpu, w.n_seqs, w.max_len)
-        cu_h = wl.cu_from_lengths(lengths)
-        B, T, N = 1, int(lengths.sum()), int(lengths.numel())
-        cu = cu_h.to(dev)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
-    C = 2 * w.Hk * w.K + w.H * w.V
-    bf = w.dtype
-    t = {"x": torch.randn((B, T, C), generator=gen, device=dev, dtype=bf),
-         "w": (torch.randn((C, 4), generator=gen, device=dev) * 0.5).to(bf),
-         "a": torch.randn((B, T, w.H), generator=gen, device=dev, dtype=bf),
-         "b": torch.randn((B, T, w.H), generator=gen, device=dev, dtype=bf),
-         "A_log": torch.log(1 + 15 * torch.rand(w.H, generator=gen, device=dev)),
-         "dt_bias": torch.randn(w.H, generator=gen, device=dev) * 0.1}
-    t["S0"] = (torch.randn((N, w.H, w.K, w.V), generator=gen, device=dev) * w.s0_std
-               if w.s0_std > 0 else None)
-    t["cu"] = cu
-    return t, B, T, N
+    d = wl.device_prefill_inputs(w, dev)
+    t = {n: d[n] for n in ("x", "w", "a", "b", "A_log", "dt_bias", "S0")}
+    t["cu"] = d["cu_seqlens"]
+    return t, d["B"], d["T"], d["N"]
 
 
 def run_prefill_part(part, args, gdn, wl, torch, dev, stream, chain_ops=False):

@@ -137,6 +137,43 @@ def prefill_inputs(w: Workload, *, T: int | None = None, B: int | None = None,
                 B=B_, T=T_, N=N, C=C, H=w.H, Hk=w.Hk, K=w.K, V=w.V, dtype=w.dtype)
 
 
+def device_prefill_inputs(w: Workload, dev, *, B: int | None = None, T: int | None = None,
+                          lengths=None, seed: int | None = None) -> dict:
+    """Inputs of the prefill chain drawn on the device, for sizes too large to
+    draw on the host: the distributions of prefill_inputs (the same shapes,
+    stds and draw order) from a seeded device generator, so the values are
+    the device RNG's, not the host draws'. Packed batches take `lengths` (or
+    the workload's length draw, made on the host first). Returns device
+    tensors x, w, a, b, A_log, dt_bias, S0 (or None), cu_seqlens (or None)
+    and the sizes B, T, N, C."""
+    seed_ = w.seed if seed is None else seed
+    cu = None
+    if lengths is None and w.n_seqs:
+        lengths = varlen_lengths(_gen(seed_), w.n_seqs, w.max_len)
+    if lengths is not None:
+        lengths = torch.as_tensor(lengths, dtype=torch.int64)
+        cu = cu_from_lengths(lengths).to(dev)
+        B_, T_, N = 1, int(lengths.sum()), int(lengths.numel())
+    else:
+        B_ = B or w.B
+        T_ = T or w.T
+        N = B_
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed_)
+    C = 2 * w.Hk * w.K + w.H * w.V
+    dt = w.dtype
+    d = {"x": torch.randn((B_, T_, C), generator=gen, device=dev, dtype=dt),
+         "w": (torch.randn((C, 4), generator=gen, device=dev) * 0.5).to(dt),
+         "a": torch.randn((B_, T_, w.H), generator=gen, device=dev, dtype=dt),
+         "b": torch.randn((B_, T_, w.H), generator=gen, device=dev, dtype=dt),
+         "A_log": torch.log(1 + 15 * torch.rand(w.H, generator=gen, device=dev)),
+         "dt_bias": torch.randn(w.H, generator=gen, device=dev) * 0.1}
+    d["S0"] = (torch.randn((N, w.H, w.K, w.V), generator=gen, device=dev) * w.s0_std
+               if w.s0_std > 0 else None)
+    d.update(cu_seqlens=cu, B=B_, T=T_, N=N, C=C)
+    return d
+
+
 # Log-decay regimes for stage-level tests of the chunked forward, where g and
 # beta are drawn directly: g = -U[0, gmax] (gmax = 0 means no decay), beta ~ U(0, 1).
 DECAY_GMAX = {"strong": 12.0, "weak": 0.05, "none": 0.0}
