@@ -164,3 +164,29 @@ def test_decay_underflow(gpu, dtype):
                         seed=25)
     d["g"] = -60 * torch.rand(d["g"].shape, generator=torch.Generator().manual_seed(4))
     _against_oracle(gpu, d, "decay underflow")
+
+
+def test_prefill_frozen_gates_keep_the_state(gpu):
+    # whole prefill with b = -inf (beta = sigmoid(b) = 0) and A_log = -inf (g = 0):
+    # the final state is S0 bit for bit and o = scale q^T S0 with q the
+    # convolved, normalised query rows, in both scan workgroup forms
+    w = wl.Workload("frozen", 3, BF16, H=4, Hk=2, K=128, V=128, s0_std=0.1)
+    d = wl.prefill_inputs(w, T=200, B=2)
+    d["b"] = torch.full_like(d["b"], float("-inf"))
+    d["A_log"] = torch.full_like(d["A_log"], float("-inf"))
+    y = oracle.conv1d_causal(to_np(d["x"]), to_np(d["w"]), silu=True)
+    q = y[:, :, :w.Hk * w.K].reshape(2, 200, w.Hk, w.K)
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6)
+    S0 = to_np(d["S0"])
+    ro = np.einsum("bthk,bhkv->bthv", np.repeat(qn, w.H // w.Hk, axis=2), S0) * 0.25
+    t = {n: d[n].to(DEV) for n in ("x", "w", "a", "b", "A_log", "dt_bias", "S0")}
+    for f in (1, 2):
+        gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, f)
+        try:
+            o, sf = gpu.gdn_prefill(t["x"], t["w"], t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                    Hk=w.Hk, K=w.K, H=w.H, V=w.V, initial_state=t["S0"], scale=0.25)
+            torch.cuda.synchronize()
+        finally:
+            gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_FORM, 0)
+        assert torch.equal(sf.cpu(), d["S0"]), f"form {f}: the state changed"
+        assert_close(to_np(o), ro, BF16, f"frozen gates, form {f} o")
