@@ -1534,7 +1534,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 //           prefetch, and waits for them.
 // With the work of a column group spread over SIMDs this way, each wave's
 // dependent chain is short and the copy engine is kept busy through the
-// whole step (the copies, not the matrix ops, bound the step at this size).
+// whole step. The step is then set by the group's shared staging and LDS
+// traffic and by the barriers between the roles, not by matrix throughput:
+// a chain wave given both tiles (half the K reads, twice the products) ran
+// slower, and one given half a tile's state updates ran no faster.
 // The chain waves hand h (at the end of a step) and U (mid-step) to the output
 // wave through LDS. A chain wave reads a chunk's operands one step ahead,
 // right after the mid-step barrier by which the copy wave has seen it land;
