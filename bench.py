@@ -38,6 +38,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -184,8 +185,14 @@ def decode_accounting(n, M, H, G, P, N):
 
 
 def source_hash(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source with its comments and spacing removed: an edit
+    to the comments alone leaves the kernels, and their counters, as they were."""
+    with open(os.path.join(ROOT, path), encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def load_traffic(part, op):
