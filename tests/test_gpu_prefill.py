@@ -187,3 +187,37 @@ def test_prefill_gqa_full_equals_chain(gpu):
 def test_prefill_varlen_full_equals_chain(gpu):
     d = wl.prefill_inputs(wl.WORKLOADS["varlen"])
     _equal(_fused(gpu, d), _chain(gpu, d), "varlen workload")
+
+
+def test_prefill_concurrent_streams(gpu):
+    # calls on separate streams, each with its own workspace and outputs, run
+    # concurrently (three streams, several rounds) and give the bits of the
+    # same calls made one after another
+    cases = [wl.prefill_inputs(wl.WORKLOADS["prefill"], T=700, B=2, seed=41),
+             wl.prefill_inputs(wl.WORKLOADS["varlen"], lengths=[5, 300, 64, 129], seed=42)]
+    dev = [_dev(d, None) for d in cases]
+
+    def call(d, t):
+        tt, cu, S0, _ = t
+        return gpu.gdn_prefill(tt["x"], tt["w"], tt["a"], tt["b"], tt["A_log"], tt["dt_bias"],
+                               Hk=d["Hk"], K=d["K"], H=d["H"], V=d["V"], initial_state=S0,
+                               cu_seqlens=cu)
+
+    ref = [call(d, t) for d, t in zip(cases, dev)]
+    dc = wl.chunk_inputs(B=2, T=300, H=4, Hk=2, K=128, V=128, dtype=BF16, s0_std=0.05, seed=43)
+    tc = {n: (None if dc[n] is None else dc[n].to(DEV)) for n in ("q", "k", "v", "g", "beta", "S0")}
+
+    def chunk():
+        return gpu.gdn_chunk_fwd(tc["q"], tc["k"], tc["v"], tc["g"], tc["beta"], initial_state=tc["S0"])
+
+    ref.append(chunk())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(3)]
+    for _ in range(4):
+        out = [None] * 3
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                out[i] = call(cases[i], dev[i]) if i < 2 else chunk()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(out[i][0], ref[i][0]) and torch.equal(out[i][1], ref[i][1]), f"stream {i}"
