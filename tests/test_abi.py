@@ -165,6 +165,8 @@ def test_chunk_validation(lib):
     assert chunk(lib, q=P + 2) == EUNSUP
     assert chunk(lib, ws=WS + 16) == EUNSUP             # workspace must be 256-byte aligned
     assert chunk(lib, qks=6148) == EUNSUP
+    assert chunk(lib, qks=1 << 24) == EUNSUP            # 64 rows overflow 32-bit offsets
+    assert chunk(lib, vs=1 << 24) == EUNSUP
     need = lib.gdn_chunk_fwd_workspace_size(4, 4096, 16, 16, 128, 128, 0, BF16)
     assert chunk(lib, wsb=need - 1) == EWS
 
