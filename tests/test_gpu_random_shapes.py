@@ -81,7 +81,7 @@ def test_random_shape_chunk_fwd(gpu, i):
             gpu.gdn_tune_set(gpu.GDN_TUNE_SCAN_TILES, 0)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(48))
 def test_random_shape_decode(gpu, i):
     r = random.Random(8192 + i)
     dtype = torch.float32 if i % 2 == 0 else torch.bfloat16
@@ -108,7 +108,7 @@ def test_random_shape_decode(gpu, i):
         assert_close(to_np(sg), sr, dtype, f"case {i} step {step} state")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(48))
 def test_random_shape_conv_bit_exact(gpu, i):
     r = random.Random(12288 + i)
     dtype = torch.float32 if i % 2 == 0 else torch.bfloat16
@@ -138,7 +138,7 @@ def test_random_shape_conv_bit_exact(gpu, i):
     np.testing.assert_array_equal(to_np(y), ref, err_msg=f"case {i}: C={C} run={run} threads={threads}")
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(24))
 def test_random_shape_gdp_prefill(gpu, i):
     r = random.Random(16384 + i)
     dtype = torch.float32 if i % 2 == 0 else torch.bfloat16
